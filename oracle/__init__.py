@@ -1,0 +1,155 @@
+"""ctypes front end of the fp64 CPU oracle (``oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are its only callers.  It shares no code with the GPU library
+and is never a fallback for it.
+"""
+from __future__ import annotations
+
+import ctypes as _ct
+import os as _os
+import subprocess as _sp
+
+import numpy as np
+
+_HERE = _os.path.dirname(_os.path.abspath(__file__))
+_SRC = _os.path.join(_HERE, "oracle.c")
+_LIB = _os.path.join(_HERE, "liboracle.so")
+# A different build of oracle.c (for instance one with a mistake planted on
+# purpose, to check that the pins in the test suite catch it) can be loaded
+# instead by naming it here.
+_LIB_OVERRIDE = _os.environ.get("SPEC_ORACLE_LIB")
+
+F32, BF16 = 0, 1
+_DT = {"f32": F32, "bf16": BF16}
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` with plain gcc (no fast-math)."""
+    if force or not _os.path.exists(_LIB) or _os.path.getmtime(_LIB) < _os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        _sp.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",
+                        "-fno-fast-math", "-o", tmp, _SRC, "-lm", "-lpthread"])
+        _os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None and _LIB_OVERRIDE:
+        _lib = _declare(_ct.CDLL(_LIB_OVERRIDE))
+    if _lib is None:
+        if not _os.path.exists(_LIB) or _os.path.getmtime(_LIB) < _os.path.getmtime(_SRC):
+            build(force=True)
+        _lib = _declare(_ct.CDLL(_LIB))
+    return _lib
+
+
+def _declare(lib):
+    P, I, D = _ct.c_void_p, _ct.c_int, _ct.c_double
+    lib.oracle_chain.argtypes = [P, P, I, P, P, I, I, I, D, P, P, P, P, P, P, I]
+    lib.oracle_chain_du.argtypes = [P, P, I, P, P, I, I, I, D, P, P, P, P, P, P, I]
+    lib.oracle_chain_alpha.argtypes = [P, P, I, I, I, I, D, P]
+    lib.oracle_tree_greedy.argtypes = [P, I, P, P, I, I, I, P, P, P, P, I]
+    for f in (lib.oracle_chain, lib.oracle_chain_du, lib.oracle_chain_alpha,
+              lib.oracle_tree_greedy):
+        f.restype = I
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(_ct.c_void_p)
+
+
+def _logits(a, dtype):
+    want = np.uint16 if dtype == "bf16" else np.float32
+    a = np.ascontiguousarray(a)
+    if a.dtype != want:
+        raise TypeError(f"{dtype} logits must be stored as {np.dtype(want).name}, got {a.dtype}")
+    return a
+
+
+def default_threads() -> int:
+    return max(1, min(16, _os.cpu_count() or 1))
+
+
+def chain(target, draft, draft_tokens, uniforms, T, dtype="f32", want_dist=False,
+          threads=None) -> dict:
+    """Chain verification (ratio test, first rejection, residual or bonus draw).
+
+    ``uniforms`` float32 [B, gamma+1] use the library's interface; float64
+    uniforms are taken as given (continuous-u enumeration in the tests).
+    Returns accept_len [B], out_tokens [B, gamma+1], margin [B] (distance of
+    the nearest decision on the path to its boundary, in u units), ratios
+    [B, gamma], fallback [B] and, if asked, final_dist [B, V] (the normalised
+    residual, or p at the bonus row).
+    """
+    lib = _load()
+    target = _logits(target, dtype)
+    draft = _logits(draft, dtype)
+    B, g1, V = target.shape
+    g = g1 - 1
+    if draft.shape != (B, g, V):
+        raise ValueError("draft must be [B, gamma, V]")
+    tok = np.ascontiguousarray(draft_tokens, dtype=np.int32).reshape(B, g)
+    u = np.ascontiguousarray(uniforms)
+    if u.shape != (B, g + 1):
+        raise ValueError("uniforms must be [B, gamma+1]")
+    acc = np.empty(B, np.int32)
+    out = np.empty((B, g + 1), np.int32)
+    margin = np.empty(B, np.float64)
+    ratios = np.empty((B, g), np.float64)
+    fb = np.empty(B, np.int32)
+    dist = np.empty((B, V), np.float64) if want_dist else None
+    nt = default_threads() if threads is None else threads
+    if u.dtype == np.float64:
+        rc = lib.oracle_chain_du(_ptr(target), _ptr(draft), _DT[dtype], _ptr(tok), _ptr(u), B,
+                                 g, V, float(T), _ptr(acc), _ptr(out), _ptr(dist),
+                                 _ptr(margin), _ptr(ratios), _ptr(fb), nt)
+    else:
+        u = np.ascontiguousarray(u, dtype=np.float32)
+        rc = lib.oracle_chain(_ptr(target), _ptr(draft), _DT[dtype], _ptr(tok), _ptr(u), B, g,
+                              V, float(T), _ptr(acc), _ptr(out), _ptr(dist), _ptr(margin),
+                              _ptr(ratios), _ptr(fb), nt)
+    if rc != 0:
+        raise ValueError(f"oracle_chain rejected its arguments (rc={rc})")
+    return dict(accept_len=acc, out_tokens=out, margin=margin, ratios=ratios, fallback=fb,
+                final_dist=dist)
+
+
+def chain_alpha(target, draft, T, dtype="f32") -> np.ndarray:
+    """alpha[b, i] = sum_v min(p_i(v), q_i(v)), the acceptance probability at
+    draft position i when the draft token is drawn from q_i."""
+    lib = _load()
+    target = _logits(target, dtype)
+    draft = _logits(draft, dtype)
+    B, g1, V = target.shape
+    out = np.empty((B, g1 - 1), np.float64)
+    rc = lib.oracle_chain_alpha(_ptr(target), _ptr(draft), _DT[dtype], B, g1 - 1, V, float(T),
+                                _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_chain_alpha rejected its arguments")
+    return out
+
+
+def tree_greedy(target, parents, tokens, dtype="bf16", threads=None) -> dict:
+    """Greedy tree verification: deepest root path whose tokens all equal the
+    target argmax after their parent, then the argmax after that path."""
+    lib = _load()
+    target = _logits(target, dtype)
+    B, n, V = target.shape
+    par = np.ascontiguousarray(parents, dtype=np.int32).reshape(B, n)
+    tok = np.ascontiguousarray(tokens, dtype=np.int32).reshape(B, n)
+    acc = np.empty(B, np.int32)
+    node = np.empty(B, np.int32)
+    out = np.empty((B, n), np.int32)
+    amax = np.empty((B, n), np.int32)
+    nt = default_threads() if threads is None else threads
+    rc = lib.oracle_tree_greedy(_ptr(target), _DT[dtype], _ptr(par), _ptr(tok), B, n, V,
+                                _ptr(acc), _ptr(node), _ptr(out), _ptr(amax), nt)
+    if rc != 0:
+        raise ValueError("oracle_tree_greedy rejected its arguments")
+    return dict(accept_len=acc, accept_node=node, out_tokens=out, amax=amax)

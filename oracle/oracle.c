@@ -1,0 +1,505 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU reference for speculative-decoding
+ * verification over the vocabulary.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load or call this library.  It shares no
+ * source, header or constant with the GPU library and must never serve as a
+ * fallback for it.
+ *
+ * Sources (page titles; sections/equations/figures on those pages):
+ *  [SD]  "Speculative decoding verifies draft tokens without changing the
+ *        target sampling distribution" -- sections "Acceptance depends on both
+ *        target and draft probabilities" (ratio test min(1, p(x)/q(x)), left
+ *        to right, stop at the first rejection), "Rejection uses a residual
+ *        distribution" (correction drawn from max(0, p - q) normalised), "A
+ *        fully accepted block yields more than one committed token" (bonus
+ *        token drawn from p after the last draft position), "Logit processing
+ *        must be consistent across verification" (one temperature for p and q;
+ *        masked tokens are impossible).
+ *  [J++] "JetSpec++: Foresight Parallel Drafting with Self Refinements" --
+ *        Appendix F.1 (worked example, Proposition 1: independent fresh draw
+ *        per test, rejection ends the block, bonus from p_{gamma+1}).
+ *  [JN]  "JetSpec reading notes" (page 3) -- Eq. 1 (acceptance probability),
+ *        Eq. 16-17 (per-branch Bernoulli tests, accepted prefix length),
+ *        section "Tree verification" with Fig. 5 and the greedy note (at T=0 a
+ *        node is accepted iff its token is the target argmax after its
+ *        parent's path), Algorithm 1 (parent pointers, node 0 is the root).
+ *
+ * Readings where the pages leave a step open (each also listed with the
+ * design notes of the repository):
+ *  - uniforms: u[b][i] drives the test at draft position i (i < gamma),
+ *    u[b][gamma] drives the final draw; accept iff u < r (u uniform on [0,1)
+ *    then accepts with probability exactly r);
+ *  - ratio r = min(1, p(x)/q(x)) evaluated as exp(log p(x) - log q(x)); by
+ *    convention r = 0 when p(x) = 0 and r = 1 when q(x) = 0 < p(x);
+ *  - the final draw maps u to a token by inverse CDF in ascending token id:
+ *    the smallest v with sum_{t<=v} w(t) > u * W; if rounding leaves no such
+ *    v, the last v with w(v) > 0;
+ *  - a residual with W = 0 (impossible in exact arithmetic after a
+ *    rejection) falls back to sampling from p at that position; the block is
+ *    flagged and its final margin is 0;
+ *  - argmax ties go to the lowest token id; among accepted tree nodes of
+ *    maximal depth the lowest node index wins;
+ *  - invalid input (a draft token outside [0, V), a NaN or +inf logit, a row
+ *    with no finite logit, a malformed parent array) makes that block
+ *    invalid: accept_len = -1 and all its output tokens -1.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_F32 0
+#define ORC_BF16 1
+
+/* Exact decoding: fp32 as stored; bf16 by placing its 16 bits on top of a
+ * 32-bit float.  Both then widen exactly to double. */
+static double logit_at(const void *base, int dtype, int64_t idx)
+{
+    if (dtype == ORC_F32)
+        return (double)((const float *)base)[idx];
+    uint32_t bits = ((uint32_t)((const uint16_t *)base)[idx]) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* Temperature softmax of one row, by definition: m = max z over the row,
+ * S = sum_v exp((z_v - m)/T), p(v) = exp((z_v - m)/T) / S.  Returns 0 and
+ * fills (m, S) for a valid row; -1 if the row holds NaN or +inf or no finite
+ * logit at all.  ([SD] "Logit processing must be consistent": p and q are
+ * both taken at the same temperature T.) */
+static int row_softmax_stats(const void *base, int dtype, int64_t off, int V, double T,
+                             double *m_out, double *S_out)
+{
+    double m = -INFINITY;
+    for (int v = 0; v < V; ++v) {
+        double z = logit_at(base, dtype, off + v);
+        if (isnan(z) || z == INFINITY)
+            return -1;
+        if (z > m)
+            m = z;
+    }
+    if (m == -INFINITY)
+        return -1;
+    double S = 0.0;
+    for (int v = 0; v < V; ++v) {
+        double z = logit_at(base, dtype, off + v);
+        S += exp((z - m) / T);
+    }
+    *m_out = m;
+    *S_out = S;
+    return 0;
+}
+
+static double prob_at(const void *base, int dtype, int64_t off, int v, double T, double m,
+                      double S)
+{
+    return exp((logit_at(base, dtype, off + v) - m) / T) / S;
+}
+
+static double logprob_at(const void *base, int dtype, int64_t off, int v, double T, double m,
+                         double S)
+{
+    double z = logit_at(base, dtype, off + v);
+    if (z == -INFINITY)
+        return -INFINITY;
+    return (z - m) / T - log(S);
+}
+
+typedef struct {
+    const void *target, *draft;
+    int dtype;
+    const int32_t *draft_tokens;
+    const double *uniforms; /* [B][gamma+1] as doubles */
+    int B, gamma, V;
+    double T;
+    int32_t *accept_len, *out_tokens;
+    double *final_dist; /* nullable [B][V] */
+    double *margin;     /* nullable [B]: smallest decision margin on the path */
+    double *ratios;     /* nullable [B][gamma]: r_i at every position */
+    int32_t *fallback;  /* nullable [B]: 1 if the W = 0 fallback was taken */
+    double *work;       /* [nthreads][V] scratch for w(v) */
+    int nthreads;
+} chain_job;
+
+/* One chain block, following [SD] and [J++] F.1 step by step. */
+static void chain_block(const chain_job *J, int b, double *w)
+{
+    const int g = J->gamma, V = J->V, dt = J->dtype;
+    const double T = J->T;
+    const double *u = J->uniforms + (int64_t)b * (g + 1);
+    int32_t *out = J->out_tokens + (int64_t)b * (g + 1);
+    const int32_t *d = J->draft_tokens + (int64_t)b * g;
+    const int64_t trow = (int64_t)V, tblk = (int64_t)(g + 1) * V, dblk = (int64_t)g * V;
+
+    for (int i = 0; i <= g; ++i)
+        out[i] = -1;
+    J->accept_len[b] = -1;
+    if (J->margin)
+        J->margin[b] = 0.0;
+    if (J->fallback)
+        J->fallback[b] = 0;
+    if (J->final_dist)
+        for (int v = 0; v < V; ++v)
+            J->final_dist[(int64_t)b * V + v] = 0.0;
+    if (J->ratios)
+        for (int i = 0; i < g; ++i)
+            J->ratios[(int64_t)b * g + i] = NAN;
+
+    /* Validate the whole block first: every draft token in range and every
+     * row a proper distribution. */
+    for (int i = 0; i < g; ++i)
+        if (d[i] < 0 || d[i] >= V)
+            return;
+    double *mp = malloc(sizeof(double) * (size_t)(g + 1));
+    double *Sp = malloc(sizeof(double) * (size_t)(g + 1));
+    double *mq = malloc(sizeof(double) * (size_t)g);
+    double *Sq = malloc(sizeof(double) * (size_t)g);
+    int bad = 0;
+    for (int j = 0; j <= g && !bad; ++j)
+        bad |= row_softmax_stats(J->target, dt, b * tblk + j * trow, V, T, &mp[j], &Sp[j]);
+    for (int j = 0; j < g && !bad; ++j)
+        bad |= row_softmax_stats(J->draft, dt, b * dblk + j * trow, V, T, &mq[j], &Sq[j]);
+    if (bad)
+        goto done;
+
+    /* Ratio r_i = min(1, p_i(x)/q_i(x)) at every draft position ([SD]
+     * "Acceptance depends on ..."; [JN] Eq. 1). */
+    double margin = INFINITY;
+    int k = g;
+    int decided = 0;
+    for (int i = 0; i < g; ++i) {
+        double lp = logprob_at(J->target, dt, b * tblk + i * trow, d[i], T, mp[i], Sp[i]);
+        double lq = logprob_at(J->draft, dt, b * dblk + i * trow, d[i], T, mq[i], Sq[i]);
+        double r;
+        if (lp == -INFINITY)
+            r = 0.0;
+        else if (lq == -INFINITY)
+            r = 1.0;
+        else
+            r = fmin(1.0, exp(lp - lq));
+        if (J->ratios)
+            J->ratios[(int64_t)b * g + i] = r;
+        if (!decided) {
+            /* Left to right; a fresh uniform per test; the first failure ends
+             * the block ([SD]; [J++] F.1; [JN] Eq. 17). */
+            margin = fmin(margin, fabs(u[i] - r));
+            if (!(u[i] < r)) {
+                k = i;
+                decided = 1;
+            }
+        }
+    }
+
+    /* Final draw: residual max(0, p_k - q_k) after a rejection, or p_gamma
+     * (the bonus row) after a fully accepted block ([SD] "Rejection uses a
+     * residual distribution", "A fully accepted block ..."; [J++] F.1). */
+    const int64_t prow = b * tblk + (int64_t)k * trow;
+    double W = 0.0;
+    if (k < g) {
+        const int64_t qrow = b * dblk + (int64_t)k * trow;
+        for (int v = 0; v < V; ++v) {
+            double pv = prob_at(J->target, dt, prow, v, T, mp[k], Sp[k]);
+            double qv = prob_at(J->draft, dt, qrow, v, T, mq[k], Sq[k]);
+            w[v] = fmax(0.0, pv - qv);
+            W += w[v];
+        }
+    }
+    int fell_back = 0;
+    if (k == g || !(W > 0.0)) {
+        fell_back = (k < g);
+        W = 0.0;
+        for (int v = 0; v < V; ++v) {
+            w[v] = prob_at(J->target, dt, prow, v, T, mp[k], Sp[k]);
+            W += w[v];
+        }
+    }
+    /* Inverse CDF in ascending token id. */
+    const double t = u[g] * W;
+    double C = 0.0, Cprev = 0.0;
+    int tok = -1;
+    for (int v = 0; v < V; ++v) {
+        Cprev = C;
+        C += w[v];
+        if (C > t) {
+            tok = v;
+            break;
+        }
+    }
+    double mf;
+    if (tok < 0) {
+        for (int v = V - 1; v >= 0; --v)
+            if (w[v] > 0.0) {
+                tok = v;
+                break;
+            }
+        mf = 0.0;
+    } else {
+        mf = fmin(t - Cprev, C - t) / W;
+    }
+    margin = fmin(margin, mf);
+    if (fell_back)
+        margin = 0.0;
+
+    J->accept_len[b] = k;
+    for (int i = 0; i < k; ++i)
+        out[i] = d[i];
+    out[k] = tok;
+    if (J->margin)
+        J->margin[b] = margin;
+    if (J->fallback)
+        J->fallback[b] = fell_back;
+    if (J->final_dist)
+        for (int v = 0; v < V; ++v)
+            J->final_dist[(int64_t)b * V + v] = w[v] / W;
+done:
+    free(mp);
+    free(Sp);
+    free(mq);
+    free(Sq);
+}
+
+typedef struct {
+    const chain_job *J;
+    int tid;
+} chain_arg;
+
+static void *chain_worker(void *p)
+{
+    const chain_arg *a = (const chain_arg *)p;
+    const chain_job *J = a->J;
+    double *w = J->work + (int64_t)a->tid * J->V;
+    for (int b = a->tid; b < J->B; b += J->nthreads)
+        chain_block(J, b, w);
+    return NULL;
+}
+
+static int run_chain(chain_job *J)
+{
+    int nt = J->nthreads < 1 ? 1 : J->nthreads;
+    if (nt > J->B)
+        nt = J->B;
+    J->nthreads = nt;
+    J->work = malloc(sizeof(double) * (size_t)nt * (size_t)J->V);
+    if (!J->work)
+        return -2;
+    if (nt == 1) {
+        chain_arg a = {J, 0};
+        chain_worker(&a);
+    } else {
+        pthread_t *th = malloc(sizeof(pthread_t) * (size_t)nt);
+        chain_arg *args = malloc(sizeof(chain_arg) * (size_t)nt);
+        for (int i = 0; i < nt; ++i) {
+            args[i].J = J;
+            args[i].tid = i;
+            pthread_create(&th[i], NULL, chain_worker, &args[i]);
+        }
+        for (int i = 0; i < nt; ++i)
+            pthread_join(th[i], NULL);
+        free(th);
+        free(args);
+    }
+    free(J->work);
+    return 0;
+}
+
+/* Chain verification with double-precision uniforms (the exact-enumeration
+ * tests drive the decision function with continuous u). */
+int oracle_chain_du(const void *target, const void *draft, int dtype,
+                    const int32_t *draft_tokens, const double *uniforms, int B, int gamma,
+                    int V, double T, int32_t *accept_len, int32_t *out_tokens,
+                    double *final_dist, double *margin, double *ratios, int32_t *fallback,
+                    int nthreads)
+{
+    if (!target || !draft || !draft_tokens || !uniforms || !accept_len || !out_tokens)
+        return -1;
+    if (B < 1 || gamma < 1 || V < 1 || !(T > 0.0) || !isfinite(T))
+        return -1;
+    if (dtype != ORC_F32 && dtype != ORC_BF16)
+        return -1;
+    chain_job J = {target, draft, dtype, draft_tokens, uniforms, B, gamma, V, T, accept_len,
+                   out_tokens, final_dist, margin, ratios, fallback, NULL, nthreads};
+    return run_chain(&J);
+}
+
+/* Chain verification with the float32 uniforms of the library interface;
+ * each uniform widens exactly to double. */
+int oracle_chain(const void *target, const void *draft, int dtype, const int32_t *draft_tokens,
+                 const float *uniforms, int B, int gamma, int V, double T,
+                 int32_t *accept_len, int32_t *out_tokens, double *final_dist, double *margin,
+                 double *ratios, int32_t *fallback, int nthreads)
+{
+    if (!uniforms || B < 1 || gamma < 1)
+        return -1;
+    size_t nu = (size_t)B * (size_t)(gamma + 1);
+    double *ud = malloc(sizeof(double) * nu);
+    if (!ud)
+        return -2;
+    for (size_t i = 0; i < nu; ++i)
+        ud[i] = (double)uniforms[i];
+    int rc = oracle_chain_du(target, draft, dtype, draft_tokens, ud, B, gamma, V, T, accept_len,
+                             out_tokens, final_dist, margin, ratios, fallback, nthreads);
+    free(ud);
+    return rc;
+}
+
+/* Per-position acceptance probability alpha_i = sum_v min(p_i(v), q_i(v)),
+ * the probability that the test at position i passes when x ~ q_i
+ * ([SD] "Rejection uses a residual distribution": accepted and residual
+ * parts recombine to p).  Invalid rows give NaN. */
+int oracle_chain_alpha(const void *target, const void *draft, int dtype, int B, int gamma, int V,
+                       double T, double *alpha)
+{
+    if (!target || !draft || !alpha || B < 1 || gamma < 1 || V < 1 || !(T > 0.0))
+        return -1;
+    for (int b = 0; b < B; ++b)
+        for (int i = 0; i < gamma; ++i) {
+            int64_t pr = (int64_t)b * (gamma + 1) * V + (int64_t)i * V;
+            int64_t qr = (int64_t)b * gamma * V + (int64_t)i * V;
+            double mp, Sp, mq, Sq, a = 0.0;
+            if (row_softmax_stats(target, dtype, pr, V, T, &mp, &Sp) ||
+                row_softmax_stats(draft, dtype, qr, V, T, &mq, &Sq)) {
+                alpha[(int64_t)b * gamma + i] = NAN;
+                continue;
+            }
+            for (int v = 0; v < V; ++v)
+                a += fmin(prob_at(target, dtype, pr, v, T, mp, Sp),
+                          prob_at(draft, dtype, qr, v, T, mq, Sq));
+            alpha[(int64_t)b * gamma + i] = a;
+        }
+    return 0;
+}
+
+/* ---------------------------------------------------------------- tree -- */
+
+typedef struct {
+    const void *target;
+    int dtype;
+    const int32_t *parents, *tokens;
+    int B, n, V;
+    int32_t *accept_len, *accept_node, *out_tokens, *amax_out;
+    int nthreads;
+} tree_job;
+
+/* Greedy tree verification of one request ([JN] "Tree verification",
+ * Fig. 5 and the greedy note; Eq. 17 for the accepted length). */
+static void tree_request(const tree_job *J, int b)
+{
+    const int n = J->n, V = J->V;
+    const int32_t *par = J->parents + (int64_t)b * n;
+    const int32_t *tok = J->tokens + (int64_t)b * n;
+    int32_t *out = J->out_tokens + (int64_t)b * n;
+    for (int j = 0; j < n; ++j)
+        out[j] = -1;
+    J->accept_len[b] = -1;
+    J->accept_node[b] = -1;
+    if (J->amax_out)
+        for (int j = 0; j < n; ++j)
+            J->amax_out[(int64_t)b * n + j] = -1;
+
+    /* Parent array: node 0 is the root; every other node's parent precedes
+     * it (Algorithm 1 adds a child only under an existing node). */
+    if (par[0] != -1)
+        return;
+    for (int j = 1; j < n; ++j)
+        if (par[j] < 0 || par[j] >= j || tok[j] < 0 || tok[j] >= V)
+            return;
+
+    /* Target argmax of every node row, lowest token id on ties. */
+    int32_t *amax = malloc(sizeof(int32_t) * (size_t)n);
+    int32_t *acc = malloc(sizeof(int32_t) * (size_t)n);
+    int32_t *depth = malloc(sizeof(int32_t) * (size_t)n);
+    for (int j = 0; j < n; ++j) {
+        int64_t off = ((int64_t)b * n + j) * V;
+        double best = -INFINITY;
+        int arg = -1;
+        for (int v = 0; v < V; ++v) {
+            double z = logit_at(J->target, J->dtype, off + v);
+            if (isnan(z) || z == INFINITY)
+                goto done;
+            if (z > best) {
+                best = z;
+                arg = v;
+            }
+        }
+        if (arg < 0)
+            goto done; /* no finite logit in this row */
+        amax[j] = arg;
+    }
+    if (J->amax_out)
+        for (int j = 0; j < n; ++j)
+            J->amax_out[(int64_t)b * n + j] = amax[j];
+
+    /* A node is accepted iff its parent is and its token equals the target
+     * argmax after the parent's path.  Parents precede children, so one
+     * pass in index order suffices. */
+    acc[0] = 1;
+    depth[0] = 0;
+    for (int j = 1; j < n; ++j) {
+        acc[j] = acc[par[j]] && tok[j] == amax[par[j]];
+        depth[j] = depth[par[j]] + 1;
+    }
+    int best = 0;
+    for (int j = 1; j < n; ++j)
+        if (acc[j] && depth[j] > depth[best])
+            best = j;
+    /* Emit the accepted path root->best (root excluded), then the target
+     * argmax after it (the bonus token). */
+    for (int j = best; j != 0; j = par[j])
+        out[depth[j] - 1] = tok[j];
+    out[depth[best]] = amax[best];
+    J->accept_len[b] = depth[best];
+    J->accept_node[b] = best;
+done:
+    free(amax);
+    free(acc);
+    free(depth);
+}
+
+typedef struct {
+    const tree_job *J;
+    int tid;
+} tree_arg;
+
+static void *tree_worker(void *p)
+{
+    const tree_arg *a = (const tree_arg *)p;
+    for (int b = a->tid; b < a->J->B; b += a->J->nthreads)
+        tree_request(a->J, b);
+    return NULL;
+}
+
+int oracle_tree_greedy(const void *target, int dtype, const int32_t *parents,
+                       const int32_t *tokens, int B, int n, int V, int32_t *accept_len,
+                       int32_t *accept_node, int32_t *out_tokens, int32_t *amax_out,
+                       int nthreads)
+{
+    if (!target || !parents || !tokens || !accept_len || !accept_node || !out_tokens)
+        return -1;
+    if (B < 1 || n < 1 || V < 1 || (dtype != ORC_F32 && dtype != ORC_BF16))
+        return -1;
+    tree_job J = {target, dtype, parents, tokens, B, n, V, accept_len, accept_node, out_tokens,
+                  amax_out, nthreads < 1 ? 1 : nthreads};
+    if (J.nthreads > B)
+        J.nthreads = B;
+    if (J.nthreads == 1) {
+        tree_arg a = {&J, 0};
+        tree_worker(&a);
+        return 0;
+    }
+    pthread_t *th = malloc(sizeof(pthread_t) * (size_t)J.nthreads);
+    tree_arg *args = malloc(sizeof(tree_arg) * (size_t)J.nthreads);
+    for (int i = 0; i < J.nthreads; ++i) {
+        args[i].J = &J;
+        args[i].tid = i;
+        pthread_create(&th[i], NULL, tree_worker, &args[i]);
+    }
+    for (int i = 0; i < J.nthreads; ++i)
+        pthread_join(th[i], NULL);
+    free(th);
+    free(args);
+    return 0;
+}
