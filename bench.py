@@ -1,0 +1,387 @@
+#!/usr/bin/env python3
+"""Throughput of speculative verification over the vocabulary on one MI355X.
+
+One step = one full verification call (all kernels of the path) over one
+batch of synthetic logits already resident in HBM.  The headline workload is
+chain verification with B=1, gamma=16, V=151936, fp32 logits; the greedy tree
+and the larger chain workloads are reported in the same JSON line under
+"per_config".
+
+Timing: the K timed steps are captured once in a HIP graph (rotating through
+enough input copies that the working set is at least 512 MiB, twice the
+Infinity Cache) and replayed between two events, with a device synchronise on
+both sides.  The dominant kernel's average duration comes from HIP events the
+library records around it on the same stream, over K eager steps.  The CPU
+baseline is the fp64 oracle on a bounded sample of the same workload.
+
+Prints exactly one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBPS = 8000.0  # MI355X HBM3E peak, GB/s
+METRIC = "logit bytes verified/s (HBM GB/s, % peak) + verify rounds/s at B×γ×V"
+CACHE_BYTES = 512 << 20
+HEADLINE_CFG = 2
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a),
+                                        ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.lib.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_draft_verification_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel_key)
+    if not rec or rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------- workloads --
+
+class Workload:
+    """Device-resident input copies plus a direct C-ABI call per step."""
+
+    def __init__(self, cfg, seed, torch, sv):
+        import numpy as np
+
+        import synth
+
+        self.cfg = cfg
+        self.spec = dict(synth.CONFIGS[cfg])
+        self.kind = self.spec["kind"]
+        self.bytes = synth.config_bytes(cfg)
+        t0 = time.time()
+        d = synth.config_inputs(cfg, seed=seed)
+        log(f"[bench] config {cfg}: inputs drawn in {time.time() - t0:.1f}s")
+        self.host = d
+        self.nsets = max(2, math.ceil(CACHE_BYTES / self.bytes))
+        dev = torch.device("cuda:0")
+        dt = self.spec["dtype"]
+
+        def logits(a):
+            if dt == "f32":
+                return torch.from_numpy(a).to(dev)
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+        self.lib = sv.load_library()
+        self.code = sv.SV_DTYPE_F32 if dt == "f32" else sv.SV_DTYPE_BF16
+        P = ctypes.c_void_p
+        if self.kind == "chain":
+            B, g, V = d["B"], d["gamma"], d["V"]
+            t0g, d0g = logits(d["target"]), logits(d["draft"])
+            tok = torch.from_numpy(d["draft_tokens"]).to(dev)
+            uni = torch.from_numpy(d["uniforms"]).to(dev)
+            self.sets = []
+            for i in range(self.nsets):
+                tg = t0g if i == 0 else t0g.clone()
+                dr = d0g if i == 0 else d0g.clone()
+                acc = torch.empty(B, dtype=torch.int32, device=dev)
+                out = torch.empty((B, g + 1), dtype=torch.int32, device=dev)
+                self.sets.append((tg, dr, tok, uni, acc, out))
+            nbytes = sv.spec_verify_chain_workspace_bytes(B, g, V, self.code)
+            self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+            self.args = [(P(tg.data_ptr()), P(dr.data_ptr()), self.code, P(tk.data_ptr()),
+                          P(un.data_ptr()), B, g, V, float(d["T"]), P(ac.data_ptr()),
+                          P(ou.data_ptr()), None, P(self.ws.data_ptr()), nbytes)
+                         for tg, dr, tk, un, ac, ou in self.sets]
+            self.n_events = 3
+            self.shape = dict(B=B, gamma=g, V=V)
+        else:
+            B, n, V = d["B"], d["n"], d["V"]
+            t0g = logits(d["target"])
+            par = torch.from_numpy(d["parents"]).to(dev)
+            tok = torch.from_numpy(d["tokens"]).to(dev)
+            self.sets = []
+            for i in range(self.nsets):
+                tg = t0g if i == 0 else t0g.clone()
+                acc = torch.empty(B, dtype=torch.int32, device=dev)
+                node = torch.empty(B, dtype=torch.int32, device=dev)
+                out = torch.empty((B, n), dtype=torch.int32, device=dev)
+                self.sets.append((tg, par, tok, acc, node, out))
+            nbytes = sv.spec_verify_tree_greedy_workspace_bytes(B, n, V, self.code)
+            self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+            self.args = [(P(tg.data_ptr()), self.code, P(pa.data_ptr()), P(tk.data_ptr()), B, n,
+                          V, P(ac.data_ptr()), P(no.data_ptr()), P(ou.data_ptr()),
+                          P(self.ws.data_ptr()), nbytes)
+                         for tg, pa, tk, ac, no, ou in self.sets]
+            self.n_events = 2
+            self.shape = dict(B=B, n=n, V=V)
+        torch.cuda.synchronize()
+
+    def step(self, i, stream_handle, events=None):
+        a = self.args[i % self.nsets]
+        ev = None
+        if events is not None:
+            arr = (ctypes.c_void_p * len(events))(*events)
+            ev = ctypes.cast(arr, ctypes.c_void_p)
+        if self.kind == "chain":
+            st = self.lib.spec_verify_chain(*a, stream_handle, ev)
+        else:
+            st = self.lib.spec_verify_tree_greedy(*a, stream_handle, ev)
+        if st != 0:
+            raise RuntimeError(f"library call failed with status {st}")
+
+    def outputs(self):
+        return [tuple(t.cpu().clone() for t in s[-2:]) for s in self.sets]
+
+    def describe(self):
+        s = self.spec
+        if self.kind == "chain":
+            tgt = f"{s['target'][0]}x{s['target'][1]}"
+            extra = f", +{s['boost'][1]:g} on {s['boost'][0]} ids/row" if s.get("boost") else ""
+            return (f"chain verify B={s['B']} gamma={s['gamma']} V={s['V']} {s['dtype']} "
+                    f"T={s['T']} (target {tgt}{extra}, draft = target + N(0,{s['noise']}^2), "
+                    f"draft tokens ~ q, seeded uniforms)")
+        return (f"greedy tree verify B={s['B']} n={s['n']} V={s['V']} {s['dtype']} "
+                f"(target N(0,{s['sigma']}^2), depth<={s['max_depth']}, "
+                f"branching<={s['max_children']}, tokens = parent argmax w.p. {s['p_match']})")
+
+
+def measure(w, steps, warmup, torch, hip):
+    """Graph-replayed throughput plus per-kernel event timing."""
+    cur = torch.cuda.current_stream()
+    h = ctypes.c_void_p(cur.cuda_stream)
+    for i in range(max(warmup, w.nsets)):
+        w.step(i, h)
+    torch.cuda.synchronize()
+    eager = w.outputs()
+
+    # capture the K timed steps once
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cap):
+        hc = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for i in range(steps):
+            w.step(i, hc)
+    g.replay()  # untimed warm replay
+    torch.cuda.synchronize()
+    for a, b in zip(eager, w.outputs()):
+        for x, y in zip(a, b):
+            if not torch.equal(x, y):
+                raise RuntimeError("graph replay disagrees with eager results")
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    for a, b in zip(eager, w.outputs()):
+        for x, y in zip(a, b):
+            if not torch.equal(x, y):
+                raise RuntimeError("timed replay disagrees with eager results")
+    del g
+
+    # dominant-kernel duration from events recorded around it by the library
+    n_ev = min(steps, 400)
+    evs = hip.create(w.n_events * n_ev)
+    torch.cuda.synchronize()
+    for i in range(n_ev):
+        w.step(i, h, evs[i * w.n_events:(i + 1) * w.n_events])
+    torch.cuda.synchronize()
+    k1 = [hip.elapsed_ms(evs[i * w.n_events], evs[i * w.n_events + 1]) for i in range(n_ev)]
+    k2 = ([hip.elapsed_ms(evs[i * 3 + 1], evs[i * 3 + 2]) for i in range(n_ev)]
+          if w.n_events == 3 else None)
+    hip.destroy(evs)
+    k1_ms = sum(k1) / len(k1)
+    res = dict(ms_per_step=ms / steps, gbps=w.bytes * steps / (ms * 1e-3) / 1e9,
+               rounds_per_s=steps / (ms * 1e-3), dominant_ms=k1_ms,
+               dominant_gbps=w.bytes / (k1_ms * 1e-3) / 1e9)
+    if k2 is not None:
+        res["final_kernel_ms"] = sum(k2) / len(k2)
+    return res
+
+
+def cpu_baseline(w, budget_s):
+    import oracle
+
+    d = w.host
+    threads = min(16, os.cpu_count() or 1)
+    rounds, t0 = 0, time.time()
+    while True:
+        if w.kind == "chain":
+            oracle.chain(d["target"], d["draft"], d["draft_tokens"], d["uniforms"], d["T"],
+                         dtype=d["dtype"], threads=threads)
+        else:
+            oracle.tree_greedy(d["target"], d["parents"], d["tokens"], dtype=d["dtype"],
+                               threads=threads)
+        rounds += 1
+        if time.time() - t0 >= budget_s:
+            break
+    dt = time.time() - t0
+    blocks = d["B"]
+    return {"value": round(w.bytes * rounds / dt / 1e9, 4), "unit": "GB/s",
+            "cores": min(threads, blocks), "kind": "oracle",
+            "rounds_per_s": round(rounds / dt, 3),
+            "sample": f"{rounds} full rounds of the headline workload in {dt:.1f}s "
+                      f"(fp64 oracle, threads over the {blocks} block(s))"}
+
+
+def copy_calibration(nbytes, reps, torch):
+    """A plain device copy of known size, for scaling rocprofv3 counters."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: about 0.2 s of GPU time)")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=HEADLINE_CFG,
+                    help="workload for the headline line (1-5)")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the other workloads in the per_config field")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the verification kernels run on a single "
+              "device and this build has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 5, torch)
+        return
+    import exact_draft_verification_amd as sv
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    hip = HipEvents()
+    default_steps = {1: 2000, 2: 2000, 3: 200, 4: 100, 5: 50}
+
+    def run(cfg, steps):
+        w = Workload(cfg, seed=1000 * cfg + 7, torch=torch, sv=sv)
+        k = steps or default_steps[cfg]
+        r = measure(w, k, args.warmup, torch, hip)
+        log(f"[bench] config {cfg}: {r['gbps']:.1f} GB/s over {k} steps, "
+            f"{r['ms_per_step'] * 1e3:.2f} us/step; dominant kernel {r['dominant_ms'] * 1e3:.2f} us")
+        return w, k, r
+
+    w, K, r = run(args.config, args.steps)
+    kernel = ("chain_stats_kernel" if w.kind == "chain" else "tree_kernel") + \
+        ("<F32>" if w.spec["dtype"] == "f32" else "<BF16>")
+    traffic = measured_traffic(f"{kernel} config{args.config}")
+    line = {
+        "metric": METRIC,
+        "value": round(r["gbps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.spec["dtype"],
+        "data": "synthetic",
+        "config": {"workload": w.describe(), **w.shape, "config_index": args.config,
+                   "bytes_per_step": w.bytes, "input_sets": w.nsets, "timing": "hip graph replay"},
+        "pct_peak": round(100.0 * r["gbps"] / PEAK_GBPS, 2),
+        "rounds_per_s": round(r["rounds_per_s"], 1),
+        "roofline": {"bound": "hbm", "kernel": kernel,
+                     "achieved": round(r["dominant_gbps"], 2), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(r["dominant_gbps"] / PEAK_GBPS, 4),
+                     "traffic": traffic, "avg_kernel_us": round(r["dominant_ms"] * 1e3, 3),
+                     "algorithmic_bytes_per_launch": w.bytes},
+    }
+    if "final_kernel_ms" in r:
+        line["roofline"]["final_kernel_us"] = round(r["final_kernel_ms"] * 1e3, 3)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    del w
+    torch.cuda.empty_cache()
+    if not args.no_per_config:
+        per = {}
+        for cfg in (3, 4, 5):
+            if cfg == args.config:
+                continue
+            try:
+                wc, kc, rc = run(cfg, None)
+                per[f"config{cfg}"] = {
+                    "workload": wc.describe(), "steps": kc,
+                    "gbps": round(rc["gbps"], 2), "pct_peak": round(100 * rc["gbps"] / PEAK_GBPS, 2),
+                    "rounds_per_s": round(rc["rounds_per_s"], 1),
+                    "us_per_step": round(rc["ms_per_step"] * 1e3, 3),
+                    "dominant_kernel_us": round(rc["dominant_ms"] * 1e3, 3),
+                    "dominant_kernel_gbps": round(rc["dominant_gbps"], 2)}
+                del wc
+                torch.cuda.empty_cache()
+            except Exception as e:  # keep the headline line even if one extra workload fails
+                per[f"config{cfg}"] = {"error": repr(e)}
+        line["per_config"] = per
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

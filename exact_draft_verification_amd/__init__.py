@@ -1,0 +1,253 @@
+"""Speculative-decoding verification over the vocabulary on MI355X (gfx950).
+
+Thin Python binding of ``libspecverify.so`` (declared in
+``include/spec_verify.h``).  It only marshals arguments: it checks dtypes,
+shapes, devices and contiguity, allocates outputs and a zero-filled workspace
+with torch when the caller passes none, and hands raw device pointers plus the
+current HIP stream to the C ABI.  Every step of the verification runs in the
+library's HIP kernels; there is no CPU path.
+
+Entry points (same names as the C ABI):
+  spec_verify_chain(target, draft, draft_tokens, uniforms, temperature, ...)
+  spec_verify_tree_greedy(target, parents, tokens, ...)
+"""
+from __future__ import annotations
+
+import ctypes as _ct
+import os as _os
+
+__all__ = [
+    "SV_DTYPE_F32", "SV_DTYPE_BF16", "SpecVerifyError", "library_path", "load_library",
+    "spec_verify_chain", "spec_verify_tree_greedy", "spec_verify_chain_workspace_bytes",
+    "spec_verify_tree_greedy_workspace_bytes", "spec_verify_workspace_zero",
+    "spec_verify_status_string",
+]
+
+SV_DTYPE_F32 = 0
+SV_DTYPE_BF16 = 1
+
+_HERE = _os.path.dirname(_os.path.abspath(__file__))
+_LIB_PATH = _os.path.join(_HERE, "libspecverify.so")
+_lib = None
+
+
+class SpecVerifyError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {spec_verify_status_string(status)} (status {status})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libspecverify.so (built by exact_draft_verification_amd.build).
+
+    Raises RuntimeError if it has not been built: there is no fallback."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing; build it with `python -m exact_draft_verification_amd.build`")
+    # torch ships its own HIP runtime under the same soname; importing torch
+    # first makes the library bind to that one, so streams and device
+    # pointers from torch are valid in it.
+    _torch()
+    lib = _ct.CDLL(_LIB_PATH)
+    P, I32, SZ, D = _ct.c_void_p, _ct.c_int32, _ct.c_size_t, _ct.c_double
+    lib.spec_verify_status_string.argtypes = [I32]
+    lib.spec_verify_status_string.restype = _ct.c_char_p
+    lib.spec_verify_chain_workspace_bytes.argtypes = [I32, I32, I32, I32]
+    lib.spec_verify_chain_workspace_bytes.restype = SZ
+    lib.spec_verify_tree_greedy_workspace_bytes.argtypes = [I32, I32, I32, I32]
+    lib.spec_verify_tree_greedy_workspace_bytes.restype = SZ
+    lib.spec_verify_chain.argtypes = [P, P, I32, P, P, I32, I32, I32, D, P, P, P, P, SZ, P, P]
+    lib.spec_verify_chain.restype = I32
+    lib.spec_verify_tree_greedy.argtypes = [P, I32, P, P, I32, I32, I32, P, P, P, P, SZ, P, P]
+    lib.spec_verify_tree_greedy.restype = I32
+    lib.spec_verify_workspace_zero.argtypes = [P, SZ, P]
+    lib.spec_verify_workspace_zero.restype = I32
+    _lib = lib
+    return lib
+
+
+def spec_verify_status_string(status: int) -> str:
+    return load_library().spec_verify_status_string(int(status)).decode()
+
+
+def spec_verify_chain_workspace_bytes(B: int, gamma: int, V: int, dtype: int) -> int:
+    return int(load_library().spec_verify_chain_workspace_bytes(B, gamma, V, dtype))
+
+
+def spec_verify_tree_greedy_workspace_bytes(B: int, n: int, V: int, dtype: int) -> int:
+    return int(load_library().spec_verify_tree_greedy_workspace_bytes(B, n, V, dtype))
+
+
+# ----------------------------------------------------------------- helpers --
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return SV_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return SV_DTYPE_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _check(t, name, shape, dtype=None, device=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _ptr(t):
+    return None if t is None else _ct.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return _ct.c_void_p(stream.cuda_stream)
+
+
+def _events(phase_events):
+    if phase_events is None:
+        return None
+    arr = (_ct.c_void_p * len(phase_events))(*[_ct.c_void_p(int(e)) for e in phase_events])
+    return _ct.cast(arr, _ct.c_void_p), arr
+
+
+_ws_cache: dict = {}
+
+
+def _workspace(nbytes: int, device, stream):
+    """A zero-filled workspace reused across calls on one device and stream
+    (each call leaves its workspace zero-filled again; calls on one stream
+    never overlap)."""
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    key = (str(device), int(stream.cuda_stream))
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+# ------------------------------------------------------------- entry points --
+
+def spec_verify_chain(target, draft, draft_tokens, uniforms, temperature, *, accept_len=None,
+                      out_tokens=None, final_dist=None, want_dist=False, workspace=None,
+                      stream=None, phase_events=None):
+    """Chain verification on the GPU.
+
+    target [B, gamma+1, V] and draft [B, gamma, V] (float32 or bfloat16, same
+    dtype), draft_tokens int32 [B, gamma], uniforms float32 [B, gamma+1],
+    temperature > 0.  Returns (accept_len [B], out_tokens [B, gamma+1],
+    final_dist [B, V] or None).  The call is asynchronous on `stream`
+    (default: the current stream)."""
+    torch = _torch()
+    lib = load_library()
+    if target.dim() != 3:
+        raise ValueError("target must be [B, gamma+1, V]")
+    B, g1, V = target.shape
+    g = g1 - 1
+    dev = target.device
+    code = _dtype_code(target)
+    _check(target, "target", (B, g1, V), device=dev)
+    _check(draft, "draft", (B, g, V), dtype=target.dtype, device=dev)
+    _check(draft_tokens, "draft_tokens", (B, g), dtype=torch.int32, device=dev)
+    _check(uniforms, "uniforms", (B, g1), dtype=torch.float32, device=dev)
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, g1), dtype=torch.int32, device=dev)
+    if final_dist is None and want_dist:
+        final_dist = torch.empty((B, V), dtype=torch.float32, device=dev)
+    _check(accept_len, "accept_len", (B,), dtype=torch.int32, device=dev)
+    _check(out_tokens, "out_tokens", (B, g1), dtype=torch.int32, device=dev)
+    if final_dist is not None:
+        _check(final_dist, "final_dist", (B, V), dtype=torch.float32, device=dev)
+    need = spec_verify_chain_workspace_bytes(B, g, V, code)
+    if need == 0:
+        raise SpecVerifyError(2, "spec_verify_chain")
+    if workspace is None:
+        workspace = _workspace(need, dev, stream)
+    ev = _events(phase_events)
+    st = lib.spec_verify_chain(_ptr(target), _ptr(draft), code, _ptr(draft_tokens),
+                               _ptr(uniforms), B, g, V, float(temperature), _ptr(accept_len),
+                               _ptr(out_tokens), _ptr(final_dist), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(),
+                               _stream_handle(stream, dev), None if ev is None else ev[0])
+    if st != 0:
+        raise SpecVerifyError(st, "spec_verify_chain")
+    return accept_len, out_tokens, final_dist
+
+
+def spec_verify_tree_greedy(target, parents, tokens, *, accept_len=None, accept_node=None,
+                            out_tokens=None, workspace=None, stream=None, phase_events=None):
+    """Greedy tree verification on the GPU.
+
+    target [B, n, V] (float32 or bfloat16), parents and tokens int32 [B, n].
+    Returns (accept_len [B], accept_node [B], out_tokens [B, n])."""
+    torch = _torch()
+    lib = load_library()
+    if target.dim() != 3:
+        raise ValueError("target must be [B, n, V]")
+    B, n, V = target.shape
+    dev = target.device
+    code = _dtype_code(target)
+    _check(target, "target", (B, n, V), device=dev)
+    _check(parents, "parents", (B, n), dtype=torch.int32, device=dev)
+    _check(tokens, "tokens", (B, n), dtype=torch.int32, device=dev)
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if accept_node is None:
+        accept_node = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, n), dtype=torch.int32, device=dev)
+    _check(accept_len, "accept_len", (B,), dtype=torch.int32, device=dev)
+    _check(accept_node, "accept_node", (B,), dtype=torch.int32, device=dev)
+    _check(out_tokens, "out_tokens", (B, n), dtype=torch.int32, device=dev)
+    need = spec_verify_tree_greedy_workspace_bytes(B, n, V, code)
+    if need == 0:
+        raise SpecVerifyError(2, "spec_verify_tree_greedy")
+    if workspace is None:
+        workspace = _workspace(need, dev, stream)
+    ev = _events(phase_events)
+    st = lib.spec_verify_tree_greedy(_ptr(target), code, _ptr(parents), _ptr(tokens), B, n, V,
+                                     _ptr(accept_len), _ptr(accept_node), _ptr(out_tokens),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream_handle(stream, dev), None if ev is None else ev[0])
+    if st != 0:
+        raise SpecVerifyError(st, "spec_verify_tree_greedy")
+    return accept_len, accept_node, out_tokens
+
+
+def spec_verify_workspace_zero(workspace, stream=None) -> None:
+    """Zero-fill a workspace tensor with the library's fill kernel."""
+    lib = load_library()
+    st = lib.spec_verify_workspace_zero(_ptr(workspace),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream_handle(stream, workspace.device))
+    if st != 0:
+        raise SpecVerifyError(st, "spec_verify_workspace_zero")

@@ -1,0 +1,268 @@
+// Host side of libspecverify.so: argument validation, workspace layout and
+// launch sequencing on the caller's stream.  See include/spec_verify.h for the
+// contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "spec_verify.h"
+#include "sv_kernels.hpp"
+
+namespace sv {
+namespace {
+
+constexpr int kThreadsHost = 256;
+constexpr int64_t kTargetUnits = 8192;  // statistics/argmax workgroups to aim for
+constexpr int64_t kTargetChunks = 1024; // final-draw workgroups to aim for
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int elem_bytes(int32_t dtype) { return dtype == SV_DTYPE_F32 ? 4 : 2; }
+bool dtype_ok(int32_t dtype) { return dtype == SV_DTYPE_F32 || dtype == SV_DTYPE_BF16; }
+
+// Segments of a row for the streaming kernels: enough workgroups to fill the
+// chip several times over, each with at least min_vec_per_thread 16-byte
+// vectors per thread; segment lengths are whole 16-byte vectors.
+void plan_segments(int64_t rows_total, int V, int epv, int64_t target, int min_vec_per_thread,
+                   int max_seg, int* nseg, int* seg_len) {
+    const int64_t nvec = ceil_div(V, epv);
+    int64_t cap = nvec / (static_cast<int64_t>(kThreadsHost) * min_vec_per_thread);
+    if (cap < 1) cap = 1;
+    if (cap > max_seg) cap = max_seg;
+    int64_t s = ceil_div(target, rows_total);
+    if (s < 1) s = 1;
+    if (s > cap) s = cap;
+    int64_t len = ceil_div(ceil_div(V, s), epv) * epv;
+    *seg_len = static_cast<int>(len);
+    *nseg = static_cast<int>(ceil_div(V, len));
+}
+
+struct ChainPlan {
+    int rows, nseg, seg_len, nchunk, chunk_len;
+    size_t off_part, off_dec, off_chunk, off_fin, off_cnt1, off_cnt2, bytes;
+};
+
+int32_t chain_plan(int32_t B, int32_t gamma, int32_t V, int32_t dtype, ChainPlan* p) {
+    if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
+    if (B < 1 || gamma < 1 || V < 1 || gamma > kMaxGamma) return SV_ERR_SHAPE;
+    const int E = elem_bytes(dtype), epv = 16 / E;
+    const int64_t rows = 2 * static_cast<int64_t>(gamma) + 1;
+    const int64_t rows_total = static_cast<int64_t>(B) * rows;
+    // every element index and byte offset must fit comfortably in int64, and
+    // grid sizes in int32
+    if (static_cast<double>(rows_total) * V * E > 9.0e18) return SV_ERR_SHAPE;
+    p->rows = static_cast<int>(rows);
+    plan_segments(rows_total, V, epv, kTargetUnits, 4, 1 << 16, &p->nseg, &p->seg_len);
+    if (rows_total * p->nseg > INT32_MAX) return SV_ERR_SHAPE;
+    plan_segments(B, V, epv, kTargetChunks, 2, kMaxChunks, &p->nchunk, &p->chunk_len);
+    if (static_cast<int64_t>(B) * p->nchunk > INT32_MAX) return SV_ERR_SHAPE;
+    size_t off = 0;
+    p->off_part = off;
+    off = align_up(off + sizeof(Stat) * static_cast<size_t>(rows_total) * p->nseg, 256);
+    p->off_dec = off;
+    off = align_up(off + sizeof(ChainDecision) * static_cast<size_t>(B), 256);
+    p->off_chunk = off;
+    off = align_up(off + sizeof(double) * static_cast<size_t>(B) * p->nchunk, 256);
+    p->off_fin = off;
+    off = align_up(off + sizeof(FinalState) * static_cast<size_t>(B), 256);
+    p->off_cnt1 = off;
+    off = align_up(off + sizeof(unsigned) * static_cast<size_t>(B), 256);
+    p->off_cnt2 = off;
+    off = align_up(off + sizeof(unsigned) * static_cast<size_t>(B), 256);
+    p->bytes = off;
+    return SV_OK;
+}
+
+struct TreePlan {
+    int nseg, seg_len;
+    size_t off_part, off_cnt, bytes;
+};
+
+int32_t tree_plan(int32_t B, int32_t n, int32_t V, int32_t dtype, TreePlan* p) {
+    if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
+    if (B < 1 || n < 1 || V < 1 || n > kMaxTreeNodes) return SV_ERR_SHAPE;
+    const int E = elem_bytes(dtype), epv = 16 / E;
+    const int64_t rows_total = static_cast<int64_t>(B) * n;
+    if (static_cast<double>(rows_total) * V * E > 9.0e18) return SV_ERR_SHAPE;
+    plan_segments(rows_total, V, epv, kTargetUnits, 4, 1 << 16, &p->nseg, &p->seg_len);
+    if (rows_total * p->nseg > INT32_MAX) return SV_ERR_SHAPE;
+    size_t off = 0;
+    p->off_part = off;
+    off = align_up(off + sizeof(ArgmaxPart) * static_cast<size_t>(rows_total) * p->nseg, 256);
+    p->off_cnt = off;
+    off = align_up(off + sizeof(unsigned) * static_cast<size_t>(B), 256);
+    p->bytes = off;
+    return SV_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int32_t record(void* const* ev, int i, hipStream_t s) {
+    if (!ev) return SV_OK;
+    return hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace sv
+
+using namespace sv;
+
+extern "C" const char* spec_verify_status_string(int32_t status) {
+    switch (status) {
+        case SV_OK: return "ok";
+        case SV_ERR_NULL: return "a required pointer is null";
+        case SV_ERR_SHAPE: return "a size is out of range";
+        case SV_ERR_TEMPERATURE: return "temperature must be finite and in [1e-6, 1e6]";
+        case SV_ERR_DTYPE: return "unknown logit dtype";
+        case SV_ERR_WORKSPACE: return "workspace too small or not 16-byte aligned";
+        case SV_ERR_HIP: return "HIP runtime error";
+        case SV_ERR_ALIGN: return "a pointer is not aligned to its element size";
+        default: return "unknown status";
+    }
+}
+
+extern "C" size_t spec_verify_chain_workspace_bytes(int32_t B, int32_t gamma, int32_t V,
+                                                    int32_t dtype) {
+    ChainPlan p;
+    return chain_plan(B, gamma, V, dtype, &p) == SV_OK ? p.bytes : 0;
+}
+
+extern "C" size_t spec_verify_tree_greedy_workspace_bytes(int32_t B, int32_t n, int32_t V,
+                                                          int32_t dtype) {
+    TreePlan p;
+    return tree_plan(B, n, V, dtype, &p) == SV_OK ? p.bytes : 0;
+}
+
+extern "C" int32_t spec_verify_chain(const void* target_logits, const void* draft_logits,
+                                     int32_t dtype, const int32_t* draft_tokens,
+                                     const float* uniforms, int32_t B, int32_t gamma, int32_t V,
+                                     double temperature, int32_t* accept_len,
+                                     int32_t* out_tokens, float* final_dist, void* workspace,
+                                     size_t workspace_bytes, void* stream,
+                                     void* const* phase_events) {
+    ChainPlan p;
+    int32_t st = chain_plan(B, gamma, V, dtype, &p);
+    if (st != SV_OK) return st;
+    if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !accept_len ||
+        !out_tokens || !workspace)
+        return SV_ERR_NULL;
+    if (!std::isfinite(temperature) || temperature < 1e-6 || temperature > 1e6)
+        return SV_ERR_TEMPERATURE;
+    const size_t E = static_cast<size_t>(elem_bytes(dtype));
+    if (!aligned(target_logits, E) || !aligned(draft_logits, E) || !aligned(draft_tokens, 4) ||
+        !aligned(uniforms, 4) || !aligned(accept_len, 4) || !aligned(out_tokens, 4) ||
+        (final_dist && !aligned(final_dist, 4)))
+        return SV_ERR_ALIGN;
+    if (!aligned(workspace, 16) || workspace_bytes < p.bytes) return SV_ERR_WORKSPACE;
+
+    ChainArgs a;
+    a.target = target_logits;
+    a.draft = draft_logits;
+    a.tokens = draft_tokens;
+    a.uniforms = uniforms;
+    a.B = B;
+    a.gamma = gamma;
+    a.V = V;
+    const double c = 1.4426950408889634074 / temperature;  // log2(e) / T
+    a.c_hi = static_cast<float>(c);
+    a.c_lo = static_cast<float>(c - static_cast<double>(a.c_hi));
+    a.c_d = static_cast<double>(a.c_hi) + static_cast<double>(a.c_lo);
+    a.T = temperature;
+    a.nseg = p.nseg;
+    a.seg_len = p.seg_len;
+    a.nchunk = p.nchunk;
+    a.chunk_len = p.chunk_len;
+    char* ws = static_cast<char*>(workspace);
+    a.part = reinterpret_cast<Stat*>(ws + p.off_part);
+    a.dec = reinterpret_cast<ChainDecision*>(ws + p.off_dec);
+    a.chunk_sum = reinterpret_cast<double*>(ws + p.off_chunk);
+    a.fin = reinterpret_cast<FinalState*>(ws + p.off_fin);
+    a.cnt_stats = reinterpret_cast<unsigned*>(ws + p.off_cnt1);
+    a.cnt_final = reinterpret_cast<unsigned*>(ws + p.off_cnt2);
+    a.accept_len = accept_len;
+    a.out_tokens = out_tokens;
+    a.final_dist = final_dist;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (record(phase_events, 0, s) != SV_OK) return SV_ERR_HIP;
+    if (launch_chain_stats(a, dtype, s) != hipSuccess) return SV_ERR_HIP;
+    if (record(phase_events, 1, s) != SV_OK) return SV_ERR_HIP;
+    if (launch_chain_final(a, dtype, s) != hipSuccess) return SV_ERR_HIP;
+    if (record(phase_events, 2, s) != SV_OK) return SV_ERR_HIP;
+    if (final_dist && launch_chain_dist(a, dtype, s) != hipSuccess) return SV_ERR_HIP;
+    return SV_OK;
+}
+
+extern "C" int32_t spec_verify_tree_greedy(const void* target_logits, int32_t dtype,
+                                           const int32_t* parents, const int32_t* tokens,
+                                           int32_t B, int32_t n, int32_t V, int32_t* accept_len,
+                                           int32_t* accept_node, int32_t* out_tokens,
+                                           void* workspace, size_t workspace_bytes, void* stream,
+                                           void* const* phase_events) {
+    TreePlan p;
+    int32_t st = tree_plan(B, n, V, dtype, &p);
+    if (st != SV_OK) return st;
+    if (!target_logits || !parents || !tokens || !accept_len || !accept_node || !out_tokens ||
+        !workspace)
+        return SV_ERR_NULL;
+    const size_t E = static_cast<size_t>(elem_bytes(dtype));
+    if (!aligned(target_logits, E) || !aligned(parents, 4) || !aligned(tokens, 4) ||
+        !aligned(accept_len, 4) || !aligned(accept_node, 4) || !aligned(out_tokens, 4))
+        return SV_ERR_ALIGN;
+    if (!aligned(workspace, 16) || workspace_bytes < p.bytes) return SV_ERR_WORKSPACE;
+    TreeArgs a;
+    a.target = target_logits;
+    a.parents = parents;
+    a.tokens = tokens;
+    a.B = B;
+    a.n = n;
+    a.V = V;
+    a.nseg = p.nseg;
+    a.seg_len = p.seg_len;
+    char* ws = static_cast<char*>(workspace);
+    a.part = reinterpret_cast<ArgmaxPart*>(ws + p.off_part);
+    a.cnt = reinterpret_cast<unsigned*>(ws + p.off_cnt);
+    a.accept_len = accept_len;
+    a.accept_node = accept_node;
+    a.out_tokens = out_tokens;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (record(phase_events, 0, s) != SV_OK) return SV_ERR_HIP;
+    if (launch_tree(a, dtype, s) != hipSuccess) return SV_ERR_HIP;
+    if (record(phase_events, 1, s) != SV_OK) return SV_ERR_HIP;
+    return SV_OK;
+}
+
+namespace sv {
+namespace {
+__global__ void zero_kernel(uint4* p, size_t nvec, unsigned char* tail, size_t ntail) {
+    const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+    for (size_t v = i; v < nvec; v += stride) p[v] = make_uint4(0u, 0u, 0u, 0u);
+    if (i < ntail) tail[i] = 0;
+}
+}  // namespace
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+    const size_t nvec = bytes / 16, ntail = bytes % 16;
+    size_t blocks = (nvec + kThreadsHost - 1) / kThreadsHost;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreadsHost), 0, s,
+                       static_cast<uint4*>(p), nvec,
+                       static_cast<unsigned char*>(p) + nvec * 16, ntail);
+    return hipGetLastError();
+}
+}  // namespace sv
+
+extern "C" int32_t spec_verify_workspace_zero(void* workspace, size_t workspace_bytes,
+                                              void* stream) {
+    if (!workspace) return SV_ERR_NULL;
+    if (!aligned(workspace, 16)) return SV_ERR_WORKSPACE;
+    if (workspace_bytes == 0) return SV_OK;
+    return launch_zero(workspace, workspace_bytes, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? SV_OK
+               : SV_ERR_HIP;
+}

@@ -1,0 +1,220 @@
+// Device-side building blocks shared by the verification kernels (gfx950).
+//
+// Layout conventions: a logit row is V contiguous elements (float32, or
+// bfloat16 bit patterns).  A workgroup of kThreads threads streams an element
+// range of one row with 16-byte vector loads (4 fp32 or 8 bf16 elements per
+// load; consecutive threads read consecutive 16-byte vectors, so every wave
+// load instruction moves one contiguous KiB).  Elements before the first
+// 16-byte boundary and after the last one are read one at a time.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cfloat>
+#include <cmath>
+
+#include "sv_kernels.hpp"
+
+namespace sv {
+
+constexpr int kThreads = 256;          // threads per workgroup (4 wave64s)
+constexpr int kWaves = kThreads / 64;  // waves per workgroup
+
+// Element traits: storage type and unpacking of one 16-byte vector.
+struct F32 {
+    using storage = float;
+    static constexpr int kPerVec = 4;
+    __device__ static inline float one(const storage* p) { return *p; }
+    __device__ static inline void unpack(const uint4& v, float* x) {
+        x[0] = __uint_as_float(v.x);
+        x[1] = __uint_as_float(v.y);
+        x[2] = __uint_as_float(v.z);
+        x[3] = __uint_as_float(v.w);
+    }
+};
+
+struct BF16 {
+    using storage = uint16_t;
+    static constexpr int kPerVec = 8;
+    __device__ static inline float one(const storage* p) {
+        return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+    }
+    // A bf16 value is the top half of a float32; the lower address holds the
+    // lower 16 bits of each 32-bit word (little endian).
+    __device__ static inline void unpack(const uint4& v, float* x) {
+        x[0] = __uint_as_float(v.x << 16);
+        x[1] = __uint_as_float(v.x & 0xffff0000u);
+        x[2] = __uint_as_float(v.y << 16);
+        x[3] = __uint_as_float(v.y & 0xffff0000u);
+        x[4] = __uint_as_float(v.z << 16);
+        x[5] = __uint_as_float(v.z & 0xffff0000u);
+        x[6] = __uint_as_float(v.w << 16);
+        x[7] = __uint_as_float(v.w & 0xffff0000u);
+    }
+};
+
+// Split of an element range [e0, e1) of a row into a scalar head, a body of
+// whole 16-byte vectors and a scalar tail, from the actual addresses.
+template <class E>
+struct RangeSplit {
+    int head_begin, head_end;  // scalar elements [head_begin, head_end)
+    int body_begin;            // first element of the vector body
+    int nvec;                  // number of 16-byte vectors in the body
+    int tail_begin, tail_end;  // scalar elements [tail_begin, tail_end)
+};
+
+template <class E>
+__device__ inline RangeSplit<E> split_range(const typename E::storage* row, int e0, int e1) {
+    using S = typename E::storage;
+    RangeSplit<E> r;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(row + e0);
+    int head = static_cast<int>(((16u - (a & 15u)) & 15u) / sizeof(S));
+    const int len = e1 - e0;
+    if (head > len) head = len;
+    r.head_begin = e0;
+    r.head_end = e0 + head;
+    r.body_begin = e0 + head;
+    r.nvec = (len - head) / E::kPerVec;
+    r.tail_begin = r.body_begin + r.nvec * E::kPerVec;
+    r.tail_end = e1;
+    return r;
+}
+
+// Plain 16-byte load that the compiler may schedule freely.
+__device__ inline uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// ---------------------------------------------------------------------------
+// Row statistics of a temperature softmax, kept as (m, R, S):
+//   m  the largest logit seen (for the domain check),
+//   R  an integer-valued float with R >= (approximately) max z*c,
+//   S  sum over the seen elements of 2^(z*c - R), in fp64,
+// where c = log2(e)/T is carried as c_hi + c_lo (two floats, so z*c is
+// effectively exact).  Because R is an integer, moving S to a larger R' is an
+// exact multiplication by 2^(R - R'), so partial sums from different lanes,
+// waves and workgroups merge without rounding in the rescale.  The row's
+// log2-sum-exp is then R + log2(S) in units of log2, i.e.
+//   log2 p(v) = z_v*c - (R + log2 S).
+__device__ inline Stat stat_empty() { return Stat{-INFINITY, -FLT_MAX, 0.0}; }
+
+__device__ inline int rescale_exponent(float from, float to) {
+    // from <= to; clamp so that the conversion is defined even when "from" is
+    // the -FLT_MAX start value (the scaled sum is then 0 anyway).
+    float d = fmaxf(from - to, -2000.0f);
+    return static_cast<int>(d);
+}
+
+__device__ inline Stat stat_merge(const Stat& a, const Stat& b) {
+    Stat r;
+    r.m = fmaxf(a.m, b.m);
+    r.R = fmaxf(a.R, b.R);
+    r.S = ldexp(a.S, rescale_exponent(a.R, r.R)) + ldexp(b.S, rescale_exponent(b.R, r.R));
+    return r;
+}
+
+// Pairwise sum of N floats (N a power of two) to keep the fp32 rounding of
+// one batch at log2(N) steps.
+template <int N>
+__device__ inline float pairwise_sum(float* v) {
+#pragma unroll
+    for (int w = N / 2; w >= 1; w /= 2) {
+#pragma unroll
+        for (int i = 0; i < w; ++i) v[i] = v[i] + v[i + w];
+    }
+    return v[0];
+}
+
+// Fold a batch of N logits into the running statistics.  One max per
+// element, one integer-aligned reference update per batch, then for each
+// element t = z*c_hi - R + z*c_lo (two fused multiply-adds, the subtraction
+// of R exact inside the first) and 2^t on the hardware exp2 unit; the batch
+// sum is pairwise in fp32 and accumulated in fp64.
+template <int N>
+__device__ inline void stat_fold(Stat& s, const float* x, float c_hi, float c_lo) {
+    float lm = x[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) lm = fmaxf(lm, x[i]);
+    const float Rn = fmaxf(s.R, ceilf(lm * c_hi));
+    s.S = ldexp(s.S, rescale_exponent(s.R, Rn));
+    s.R = Rn;
+    s.m = fmaxf(s.m, lm);
+    float e[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        float t = fmaf(x[i], c_hi, -Rn);
+        t = fmaf(x[i], c_lo, t);
+        e[i] = __builtin_amdgcn_exp2f(t);
+    }
+    s.S += static_cast<double>(pairwise_sum<N>(e));
+}
+
+// ---------------------------------------------------------------------------
+// Wave64 and workgroup reductions.
+
+template <class T>
+__device__ inline T wave_xor(T v, int mask) {
+    return __shfl_xor(v, mask, 64);
+}
+
+__device__ inline Stat wave_reduce_stat(Stat s) {
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) {
+        Stat o;
+        o.m = wave_xor(s.m, mask);
+        o.R = wave_xor(s.R, mask);
+        o.S = wave_xor(s.S, mask);
+        s = stat_merge(s, o);
+    }
+    return s;
+}
+
+__device__ inline double wave_sum(double v) {
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) v += wave_xor(v, mask);
+    return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (Hillis-Steele).
+__device__ inline double wave_inclusive_scan(double v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        double o = __shfl_up(v, d, 64);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+// Workgroup-wide exclusive prefix sum of one double per thread, in thread
+// order; also returns the total.  Uses kWaves doubles of LDS.
+__device__ inline double block_exclusive_scan(double v, double* lds_waves, double* total) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    double incl = wave_inclusive_scan(v);
+    if (lane == 63) lds_waves[wave] = incl;
+    __syncthreads();
+    double base = 0.0, all = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        double t = lds_waves[w];
+        if (w < wave) base += t;
+        all += t;
+    }
+    __syncthreads();
+    *total = all;
+    return base + incl - v;
+}
+
+__device__ inline double block_sum(double v, double* lds_waves) {
+    double t;
+    block_exclusive_scan(v, lds_waves, &t);
+    return t;
+}
+
+// Device-scope release/acquire around the "last workgroup to arrive" counters.
+__device__ inline unsigned arrive(unsigned* counter) {
+    __threadfence();
+    return atomicAdd(counter, 1u);
+}
+
+}  // namespace sv

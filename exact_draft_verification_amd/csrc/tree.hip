@@ -1,0 +1,296 @@
+// Greedy tree verification kernel for gfx950.
+//
+// The rule ("JetSpec reading notes", section "Tree verification", Fig. 5 and
+// the greedy note; parent pointers as built by Algorithm 1): node j of a draft
+// tree is accepted iff its parent is accepted and its token equals the target
+// argmax after the parent's path; the deepest accepted node v* is kept (the
+// lowest node index among equally deep ones), its path is committed and the
+// target argmax after v* is emitted as the extra token.
+//
+// One launch.  Each workgroup takes one segment of one node row and finds the
+// largest logit and the lowest index holding it (plus a NaN flag); the last
+// workgroup to finish a request (arrival counter) merges the row results,
+// validates the parent array and resolves every node's acceptance and depth
+// by pointer jumping in LDS (ceil(log2 n) rounds), then writes the path.
+#include "sv_device.hpp"
+
+namespace sv {
+
+namespace {
+
+struct Best {
+    float v;
+    int idx;
+};
+
+// Keep the larger value; on equal values the lower index.
+__device__ inline Best best_merge(Best a, Best b) {
+    if (b.v > a.v || (b.v == a.v && b.idx < a.idx)) return b;
+    return a;
+}
+
+// Fold a batch of N elements whose token ids are idx_of(i), increasing in i.
+template <int N, class IdxFn>
+__device__ inline void argmax_fold(Best& best, const float* x, IdxFn idx_of) {
+    float bm = x[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) bm = fmaxf(bm, x[i]);
+    if (bm > best.v) {
+        int first = N - 1;
+#pragma unroll
+        for (int i = N - 1; i >= 0; --i)
+            if (x[i] == bm) first = i;
+        best.v = bm;
+        best.idx = idx_of(first);
+    }
+}
+
+// NaN flag for one 16-byte vector, from the raw bits.
+__device__ inline uint32_t nan_bits(const uint4& v, F32) {
+    // (|x| bits) + 0x007fffff has bit 31 set iff |x| > +inf, i.e. NaN
+    return ((v.x & 0x7fffffffu) + 0x007fffffu) | ((v.y & 0x7fffffffu) + 0x007fffffu) |
+           ((v.z & 0x7fffffffu) + 0x007fffffu) | ((v.w & 0x7fffffffu) + 0x007fffffu);
+}
+__device__ inline uint32_t nan_bits(const uint4& v, BF16) {
+    // per 16-bit half: (|x| bits) + 0x007f sets the half's top bit iff NaN
+    constexpr uint32_t M = 0x7fff7fffu, A = 0x007f007fu;
+    return ((v.x & M) + A) | ((v.y & M) + A) | ((v.z & M) + A) | ((v.w & M) + A);
+}
+__device__ inline uint32_t nan_mask(F32) { return 0x80000000u; }
+__device__ inline uint32_t nan_mask(BF16) { return 0x80008000u; }
+
+template <class E>
+__device__ inline void range_argmax(const typename E::storage* row, int e0, int e1, Best& best,
+                                    uint32_t& nanacc, bool& nan_scalar) {
+    constexpr int U = 4;
+    constexpr int NB = U * E::kPerVec;
+    constexpr int kBatchVec = kThreads * U;
+    const int tid = threadIdx.x;
+    if (e0 >= e1) return;
+    const RangeSplit<E> sp = split_range<E>(row, e0, e1);
+    for (int e = sp.head_begin + tid; e < sp.head_end; e += kThreads) {
+        const float x = E::one(row + e);
+        nan_scalar |= isnan(x);
+        argmax_fold<1>(best, &x, [&](int) { return e; });
+    }
+    const char* body = reinterpret_cast<const char*>(row + sp.body_begin);
+    const int nfull = sp.nvec / kBatchVec;
+    auto fold_batch = [&](const uint4* V4, int vbase) {
+        float x[NB];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            E::unpack(V4[u], x + u * E::kPerVec);
+            nanacc |= nan_bits(V4[u], E{});
+        }
+        argmax_fold<NB>(best, x, [&](int i) {
+            const int u = i / E::kPerVec, w = i % E::kPerVec;
+            return sp.body_begin + (vbase + u * kThreads + tid) * E::kPerVec + w;
+        });
+    };
+    if (nfull > 0) {
+        uint4 A[U], Bv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) A[u] = load16(body + static_cast<size_t>(u * kThreads + tid) * 16);
+        for (int t = 0; t < nfull; t += 2) {
+            const bool has1 = t + 1 < nfull;
+            if (has1) {
+                const char* nb = body + static_cast<size_t>(t + 1) * kBatchVec * 16;
+#pragma unroll
+                for (int u = 0; u < U; ++u) Bv[u] = load16(nb + static_cast<size_t>(u * kThreads + tid) * 16);
+            }
+            {
+                uint4 cur[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) cur[u] = A[u];
+                if (t + 2 < nfull) {
+                    const char* nb = body + static_cast<size_t>(t + 2) * kBatchVec * 16;
+#pragma unroll
+                    for (int u = 0; u < U; ++u) A[u] = load16(nb + static_cast<size_t>(u * kThreads + tid) * 16);
+                }
+                fold_batch(cur, t * kBatchVec);
+            }
+            if (has1) fold_batch(Bv, (t + 1) * kBatchVec);
+        }
+    }
+    for (int v = nfull * kBatchVec + tid; v < sp.nvec; v += kThreads) {
+        const uint4 raw = load16(body + static_cast<size_t>(v) * 16);
+        float x[E::kPerVec];
+        E::unpack(raw, x);
+        nanacc |= nan_bits(raw, E{});
+        argmax_fold<E::kPerVec>(best, x, [&](int i) { return sp.body_begin + v * E::kPerVec + i; });
+    }
+    for (int e = sp.tail_begin + tid; e < sp.tail_end; e += kThreads) {
+        const float x = E::one(row + e);
+        nan_scalar |= isnan(x);
+        argmax_fold<1>(best, &x, [&](int) { return e; });
+    }
+}
+
+// Path resolution for request b: runs in the last workgroup of the request.
+__device__ void tree_resolve(const TreeArgs& a, int b) {
+    __shared__ int s_par[kMaxTreeNodes];
+    __shared__ int s_anc[kMaxTreeNodes];
+    __shared__ int s_dep[kMaxTreeNodes];
+    __shared__ int s_amax[kMaxTreeNodes];
+    __shared__ unsigned char s_ok[kMaxTreeNodes];
+    __shared__ int s_bad, s_key;
+    constexpr int kPer = kMaxTreeNodes / kThreads;
+    const int n = a.n, tid = threadIdx.x;
+    const int32_t* par = a.parents + static_cast<int64_t>(b) * n;
+    const int32_t* tok = a.tokens + static_cast<int64_t>(b) * n;
+    int32_t* out = a.out_tokens + static_cast<int64_t>(b) * n;
+    if (tid == 0) {
+        s_bad = 0;
+        s_key = -1;
+    }
+    __syncthreads();
+    for (int j = tid; j < n; j += kThreads) {
+        const ArgmaxPart* p = a.part + (static_cast<int64_t>(b) * n + j) * a.nseg;
+        Best best{p[0].best, p[0].idx};
+        uint32_t bad = p[0].bad;
+        for (int s = 1; s < a.nseg; ++s) {
+            best = best_merge(best, Best{p[s].best, p[s].idx});
+            bad |= p[s].bad;
+        }
+        // a valid row has no NaN, no +inf and at least one finite logit
+        if (bad || !(best.v > -INFINITY) || best.v == INFINITY) s_bad = 1;
+        s_amax[j] = best.idx;
+        const int pj = par[j];
+        if (j == 0) {
+            if (pj != -1) s_bad = 1;
+        } else if (pj < 0 || pj >= j || tok[j] < 0 || tok[j] >= a.V) {
+            s_bad = 1;
+        }
+        s_par[j] = pj;
+    }
+    __syncthreads();
+    if (s_bad) {
+        for (int j = tid; j < n; j += kThreads) out[j] = -1;
+        if (tid == 0) {
+            a.accept_len[b] = -1;
+            a.accept_node[b] = -1;
+            a.cnt[b] = 0u;
+        }
+        return;
+    }
+    // acceptance of the edge into each node, then pointer jumping: after each
+    // round s_anc[j] is 2^r levels up (or the root), s_dep[j] the distance to
+    // it and s_ok[j] whether every edge in between matched.
+    for (int j = tid; j < n; j += kThreads) {
+        if (j == 0) {
+            s_anc[0] = 0;
+            s_dep[0] = 0;
+            s_ok[0] = 1;
+        } else {
+            s_anc[j] = s_par[j];
+            s_dep[j] = 1;
+            s_ok[j] = tok[j] == s_amax[s_par[j]];
+        }
+    }
+    __syncthreads();
+    for (int span = 1; span < n; span <<= 1) {
+        int nanc[kPer], ndep[kPer];
+        unsigned char nok[kPer];
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int j = tid + m * kThreads;
+            if (j < n) {
+                const int up = s_anc[j];
+                nok[m] = s_ok[j] & s_ok[up];
+                ndep[m] = s_dep[j] + s_dep[up];
+                nanc[m] = s_anc[up];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int j = tid + m * kThreads;
+            if (j < n) {
+                s_ok[j] = nok[m];
+                s_dep[j] = ndep[m];
+                s_anc[j] = nanc[m];
+            }
+        }
+        __syncthreads();
+    }
+    // deepest accepted node, lowest index on ties: maximise (depth, -index)
+    for (int j = tid; j < n; j += kThreads)
+        if (s_ok[j]) atomicMax(&s_key, (s_dep[j] << 11) | (2047 - j));
+    __syncthreads();
+    const int key = s_key;
+    const int depth = key >> 11;
+    const int vstar = 2047 - (key & 2047);
+    for (int j = depth + 1 + tid; j < n; j += kThreads) out[j] = -1;
+    if (tid == 0) {
+        int v = vstar;
+        for (int d = depth; d >= 1; --d) {
+            out[d - 1] = tok[v];
+            v = s_par[v];
+        }
+        out[depth] = s_amax[vstar];
+        a.accept_len[b] = depth;
+        a.accept_node[b] = vstar;
+        a.cnt[b] = 0u;
+    }
+}
+
+template <class E>
+__global__ __launch_bounds__(kThreads) void tree_kernel(TreeArgs a) {
+    const int unit = blockIdx.x;
+    const int seg = unit % a.nseg;
+    const int rr = unit / a.nseg;  // = b * n + j
+    const int b = rr / a.n;
+    using S = typename E::storage;
+    const S* row = static_cast<const S*>(a.target) + static_cast<int64_t>(rr) * a.V;
+    const int e0 = seg * a.seg_len;
+    const int e1 = min(a.V, e0 + a.seg_len);
+    Best best{-INFINITY, INT32_MAX};
+    uint32_t nanacc = 0;
+    bool nan_scalar = false;
+    range_argmax<E>(row, e0, e1, best, nanacc, nan_scalar);
+    uint32_t bad = ((nanacc & nan_mask(E{})) != 0u || nan_scalar) ? 1u : 0u;
+    // wave then workgroup reduction
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) {
+        Best o{__shfl_xor(best.v, mask, 64), __shfl_xor(best.idx, mask, 64)};
+        best = best_merge(best, o);
+        bad |= __shfl_xor(bad, mask, 64);
+    }
+    __shared__ Best s_b[kWaves];
+    __shared__ uint32_t s_bad[kWaves];
+    __shared__ int s_last;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+        s_b[wave] = best;
+        s_bad[wave] = bad;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        Best r = s_b[0];
+        uint32_t rb = s_bad[0];
+        for (int w = 1; w < kWaves; ++w) {
+            r = best_merge(r, s_b[w]);
+            rb |= s_bad[w];
+        }
+        a.part[unit] = ArgmaxPart{r.v, r.idx, rb, 0u};
+        const unsigned prev = arrive(&a.cnt[b]);
+        s_last = (prev == static_cast<unsigned>(a.n * a.nseg - 1));
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    tree_resolve(a, b);
+}
+
+}  // namespace
+
+hipError_t launch_tree(const TreeArgs& a, int dtype, hipStream_t s) {
+    const int grid = a.B * a.n * a.nseg;
+    if (dtype == 0)
+        hipLaunchKernelGGL(tree_kernel<F32>, dim3(grid), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(tree_kernel<BF16>, dim3(grid), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace sv

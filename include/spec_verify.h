@@ -1,0 +1,167 @@
+/*
+ * spec_verify.h -- C ABI of the MI355X (gfx950) speculative-verification
+ * library libspecverify.so.
+ *
+ * Two operations, both over the vocabulary, both stated on the pages:
+ *
+ *  spec_verify_chain: speculative sampling of one drafted block per batch
+ *    entry.  For draft position i the target distribution p_i and the draft
+ *    distribution q_i are the temperature softmaxes of the given logits,
+ *    taken identically for both ("Speculative decoding verifies draft tokens
+ *    without changing the target sampling distribution", section "Logit
+ *    processing must be consistent across verification").  Draft token x_i is
+ *    accepted with probability min(1, p_i(x_i)/q_i(x_i)), left to right, and
+ *    the first rejection ends the block (same page, section "Acceptance
+ *    depends on both target and draft probabilities"; "JetSpec reading
+ *    notes", Eq. 1 and Eq. 17).  After a rejection at position k the extra
+ *    token is drawn from max(0, p_k - q_k) normalised (section "Rejection
+ *    uses a residual distribution"); after a fully accepted block it is drawn
+ *    from the target's bonus row p_gamma (section "A fully accepted block
+ *    yields more than one committed token"; "JetSpec++", Appendix F.1).
+ *
+ *  spec_verify_tree_greedy: greedy (T = 0) verification of a draft tree given
+ *    as a parent array: a node is accepted iff its parent is accepted and its
+ *    token equals the target argmax after the parent's path; the deepest
+ *    accepted node is kept and the target argmax after it is emitted as the
+ *    extra token ("JetSpec reading notes", section "Tree verification",
+ *    Fig. 5 and the greedy note; Algorithm 1 for the parent array).
+ *
+ * Every random draw is an explicit input: the caller passes one uniform per
+ * test and one for the final draw, so results are a pure function of the
+ * arguments.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers to logits, tokens, uniforms, parents, outputs and workspace are
+ *    DEVICE pointers owned by the caller; the library allocates no device
+ *    memory, keeps no global state and never synchronises the stream.  All
+ *    work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    results are valid once that stream reaches this point.
+ *  - Arrays are dense, row-major, with the shapes given below.  Logits are
+ *    float32 (SV_DTYPE_F32) or bfloat16 bit patterns (SV_DTYPE_BF16); each
+ *    pointer must be aligned to its element size.
+ *  - Host-detectable errors (a null required pointer, a size out of range, an
+ *    unknown dtype, a bad temperature, a workspace that is too small or not
+ *    16-byte aligned, a misaligned pointer) return a non-zero status BEFORE
+ *    anything is enqueued, and nothing is written.
+ *  - Data-dependent errors are reported per block (per request for trees)
+ *    without any host synchronisation: accept_len[b] = -1 and every output
+ *    token of that block = -1, while the other blocks are unaffected.  They
+ *    are: a draft token outside [0, V); a NaN or +inf logit in any row of the
+ *    block; a row without any finite logit; for chains, a row whose largest
+ *    finite logit m has |m| / T > 2^28 (outside the supported domain); for
+ *    trees, a malformed parent array or a node token outside [0, V).
+ *  - -inf logits are legal and mean "masked": that token has probability 0.
+ *  - The workspace must be zero-filled before its first use (for example with
+ *    spec_verify_workspace_zero); every call leaves it zero-filled again.  Two
+ *    calls in flight at the same time need distinct workspaces.
+ *  - A failure of the HIP runtime to launch returns SV_ERR_HIP.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of the logits. */
+#define SV_DTYPE_F32 0
+#define SV_DTYPE_BF16 1
+
+/* Status codes. */
+#define SV_OK 0
+#define SV_ERR_NULL 1        /* a required pointer is NULL                        */
+#define SV_ERR_SHAPE 2       /* B, gamma, n or V out of range, or sizes overflow   */
+#define SV_ERR_TEMPERATURE 3 /* temperature not finite or outside [1e-6, 1e6]     */
+#define SV_ERR_DTYPE 4       /* dtype is neither SV_DTYPE_F32 nor SV_DTYPE_BF16    */
+#define SV_ERR_WORKSPACE 5   /* workspace too small or not 16-byte aligned         */
+#define SV_ERR_HIP 6         /* the HIP runtime reported an error                  */
+#define SV_ERR_ALIGN 7       /* a pointer is not aligned to its element size       */
+
+/* Limits checked on the host. */
+#define SV_MAX_GAMMA 255   /* draft positions per chain block                     */
+#define SV_MAX_TREE_NODES 1024 /* nodes per tree, root included                   */
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *spec_verify_status_string(int32_t status);
+
+/* Bytes of workspace spec_verify_chain needs for these sizes; 0 if the sizes
+ * or dtype are invalid. */
+size_t spec_verify_chain_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t dtype);
+
+/* Chain verification (see the top of this file).
+ *
+ *  target_logits  [B][gamma+1][V] dtype: row i < gamma is the target's logits
+ *                 at draft position i, row gamma the bonus row.
+ *  draft_logits   [B][gamma][V] dtype: row i is the draft's logits at draft
+ *                 position i (the distribution x_i was drawn from).
+ *  draft_tokens   [B][gamma] int32: x_0 .. x_{gamma-1}.
+ *  uniforms       [B][gamma+1] float32: entry i < gamma drives the test at
+ *                 position i (accept iff u < min(1, p/q)); entry gamma drives
+ *                 the final draw: the smallest token v with
+ *                 sum_{t <= v} w(t) > u * sum_t w(t), w being the residual or
+ *                 the bonus-row distribution (inverse CDF in ascending token
+ *                 id).  Uniforms are expected in [0, 1).
+ *  temperature    T, the same for every target and draft row; finite and in
+ *                 [1e-6, 1e6].
+ *  accept_len     out [B] int32: k in [0, gamma], or -1 for an invalid block.
+ *  out_tokens     out [B][gamma+1] int32: x_0 .. x_{k-1}, then the
+ *                 correction (k < gamma) or bonus (k = gamma) token, then -1.
+ *  final_dist     out, NULLABLE [B][V] float32: the normalised distribution
+ *                 the extra token was drawn from (zeros for invalid blocks).
+ *                 When NULL it is neither computed nor written.
+ *  workspace      device scratch of at least
+ *                 spec_verify_chain_workspace_bytes(B, gamma, V, dtype)
+ *                 bytes, 16-byte aligned, zero-filled before first use.
+ *  stream         hipStream_t to enqueue on (NULL = null stream).
+ *  phase_events   NULLABLE: if not NULL, points to 3 hipEvent_t handles that
+ *                 are recorded on `stream` before the row-statistics kernel,
+ *                 after it, and after the final-draw kernel (instrumentation
+ *                 for timing; the optional final_dist pass comes later).
+ */
+int32_t spec_verify_chain(const void *target_logits, const void *draft_logits, int32_t dtype,
+                          const int32_t *draft_tokens, const float *uniforms, int32_t B,
+                          int32_t gamma, int32_t V, double temperature, int32_t *accept_len,
+                          int32_t *out_tokens, float *final_dist, void *workspace,
+                          size_t workspace_bytes, void *stream, void *const *phase_events);
+
+/* Bytes of workspace spec_verify_tree_greedy needs; 0 if the sizes or dtype
+ * are invalid. */
+size_t spec_verify_tree_greedy_workspace_bytes(int32_t B, int32_t n, int32_t V, int32_t dtype);
+
+/* Greedy tree verification (see the top of this file).
+ *
+ *  target_logits  [B][n][V] dtype: row j = the target's logits after the
+ *                 root -> j path (row 0: after the verified context).
+ *  parents        [B][n] int32: parents[0] = -1; 0 <= parents[j] < j.
+ *  tokens         [B][n] int32: token of node j (tokens[0], the anchor, is
+ *                 not checked).
+ *  accept_len     out [B] int32: depth of the deepest accepted node (0 = no
+ *                 draft token accepted), -1 for an invalid request.
+ *  accept_node    out [B] int32: that node's index (0 = root; the lowest
+ *                 index wins among accepted nodes of equal depth), -1 if
+ *                 invalid.
+ *  out_tokens     out [B][n] int32: the accepted path's tokens root -> leaf
+ *                 (root excluded), then the target argmax after it (lowest
+ *                 token id on ties), then -1.
+ *  workspace      as for spec_verify_chain, sized by
+ *                 spec_verify_tree_greedy_workspace_bytes.
+ *  phase_events   NULLABLE: 2 hipEvent_t recorded before and after the
+ *                 verification kernel.
+ */
+int32_t spec_verify_tree_greedy(const void *target_logits, int32_t dtype,
+                                const int32_t *parents, const int32_t *tokens, int32_t B,
+                                int32_t n, int32_t V, int32_t *accept_len, int32_t *accept_node,
+                                int32_t *out_tokens, void *workspace, size_t workspace_bytes,
+                                void *stream, void *const *phase_events);
+
+/* Zero-fill a workspace on `stream` (a plain fill kernel, no memset node). */
+int32_t spec_verify_workspace_zero(void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -43,7 +43,10 @@
  *    maximal depth the lowest node index wins;
  *  - invalid input (a draft token outside [0, V), a NaN or +inf logit, a row
  *    with no finite logit, a malformed parent array) makes that block
- *    invalid: accept_len = -1 and all its output tokens -1.
+ *    invalid: accept_len = -1 and all its output tokens -1;
+ *  - the library interface supports chain rows whose largest finite logit m
+ *    satisfies |m| / T <= 2^28; a row outside that domain makes its block
+ *    invalid here too.
  */
 #include <math.h>
 #include <pthread.h>
@@ -83,6 +86,10 @@ static int row_softmax_stats(const void *base, int dtype, int64_t off, int V, do
             m = z;
     }
     if (m == -INFINITY)
+        return -1;
+    /* Interface domain: the library accepts rows whose largest finite logit
+     * satisfies |m| / T <= 2^28; larger magnitudes make the block invalid. */
+    if (fabs(m / T) > 268435456.0)
         return -1;
     double S = 0.0;
     for (int v = 0; v < V; ++v) {

@@ -1,0 +1,187 @@
+"""GPU parity of spec_verify_chain against the fp64 oracle (needs an MI355X).
+
+Every case draws seeded inputs, runs the HIP library through its C ABI and
+the oracle on the same inputs, and compares with the rule in gpu_util: exact
+accept lengths and tokens outside the 1e-6 boundary band, final_dist to 1e-5.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import compare_chain, gpu_chain, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(d, label, want_dist=True):
+    print(f"[case] {label} B={d['B']} gamma={d['gamma']} V={d['V']} {d['dtype']} T={d['T']}",
+          flush=True)
+    g = gpu_chain(d, want_dist=want_dist)
+    o = oracle.chain(d["target"], d["draft"], d["draft_tokens"], d["uniforms"], d["T"],
+                     dtype=d["dtype"], want_dist=want_dist)
+    n, near = compare_chain(g, o, label)
+    print(f"[case] {label}: compared {n} blocks, {near} inside the boundary band", flush=True)
+    return g, o
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+SHAPES = [(3, 1, 1), (5, 2, 7), (4, 31, 1000), (2, 3, 5003), (1, 16, 151937), (7, 4, 4096),
+          (2, 255, 64)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"B{b}g{g}V{v}" for b, g, v in SHAPES])
+def test_shapes_and_ragged_tails(shape, dtype):
+    B, g, V = shape
+    for seed in range(3):
+        d = synth.chain_inputs(B, g, V, dtype, T=0.9, target=("normal", 2.0), noise=0.6,
+                               seed=1000 + seed)
+        run_case(d, f"shape{shape}-{dtype}-s{seed}")
+
+
+@pytest.mark.parametrize("cfg,seeds", [(1, range(40)), (2, range(6)), (3, range(2)), (5, range(1))])
+def test_configs_full_size(cfg, seeds):
+    for s in seeds:
+        d = synth.config_inputs(cfg, seed=1000 * cfg + s)
+        run_case(d, f"config{cfg}-s{s}", want_dist=(cfg != 5))
+
+
+def test_config3_more_uniforms():
+    """Same logits, fresh uniforms: many more decisions at full size."""
+    d = synth.config_inputs(3, seed=3001)
+    rng = np.random.default_rng(5)
+    for r in range(4):
+        d["uniforms"] = rng.random(d["uniforms"].shape, dtype=np.float32)
+        run_case(d, f"config3-u{r}", want_dist=False)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_all_accept_bonus_path(dtype):
+    d = synth.chain_inputs(16, 5, 3000, dtype, T=0.8, seed=7)
+    d["draft"] = d["target"][:, :5].copy()
+    g, o = run_case(d, f"all-accept-{dtype}")
+    assert (g["accept_len"] == 5).all()
+
+
+def test_point_mass_drafts():
+    """One-hot draft logits (-inf elsewhere): q = delta_d, the exact-match rule
+    of JetSpec++ Appendix F.3 expressed through the ratio test."""
+    d = synth.chain_inputs(32, 4, 2000, "f32", T=1.0, seed=8)
+    drf = np.full_like(d["draft"], -np.inf)
+    for b in range(32):
+        for i in range(4):
+            drf[b, i, d["draft_tokens"][b, i]] = 0.0
+    d["draft"] = drf
+    run_case(d, "point-mass")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_masked_tokens(dtype):
+    d = synth.chain_inputs(24, 6, 4099, dtype, T=1.1, seed=9)
+    rng = np.random.default_rng(9)
+    ninf = np.float32(-np.inf) if dtype == "f32" else np.uint16(0xFF80)
+    for key in ("target", "draft"):
+        arr = d[key]
+        mask = rng.random(arr.shape) < 0.3
+        arr[mask] = ninf
+    # keep every draft token possible under q so the inputs stay meaningful
+    for b in range(24):
+        for i in range(6):
+            x = d["draft_tokens"][b, i]
+            d["draft"][b, i, x] = 0 if dtype == "bf16" else np.float32(0.0)
+    run_case(d, f"masked-{dtype}")
+
+
+@pytest.mark.parametrize("T", [0.05, 5.0])
+def test_temperature_extremes(T):
+    d = synth.chain_inputs(16, 8, 10000, "bf16", T=T, target=("normal", 2.0), noise=0.3, seed=10)
+    run_case(d, f"T{T}")
+
+
+def test_large_logits():
+    d = synth.chain_inputs(8, 4, 3000, "f32", T=1.0, seed=11)
+    rng = np.random.default_rng(11)
+    d["target"] = np.where(rng.random(d["target"].shape) < 0.5, 1e4, -1e4).astype(np.float32)
+    d["draft"] = d["target"][:, :4] + rng.normal(0, 0.5, d["draft"].shape).astype(np.float32)
+    run_case(d, "pm1e4")
+
+
+@pytest.mark.parametrize("kind", ["nan", "posinf", "allneginf", "token_hi", "token_neg", "domain"])
+def test_invalid_blocks(kind):
+    d = synth.chain_inputs(4, 3, 1030, "f32", T=1.0, seed=12)
+    if kind == "nan":
+        d["draft"][1, 2, 5] = np.nan
+    elif kind == "posinf":
+        d["target"][1, 3, 0] = np.inf
+    elif kind == "allneginf":
+        d["target"][1, 0, :] = -np.inf
+    elif kind == "token_hi":
+        d["draft_tokens"][1, 2] = 1030
+    elif kind == "token_neg":
+        d["draft_tokens"][1, 0] = -1
+    else:
+        d["draft"][1, 1, 3] = 3.0e8
+    g, o = run_case(d, f"invalid-{kind}")
+    assert g["accept_len"][1] == -1 and (g["out_tokens"][1] == -1).all()
+    assert (g["accept_len"][[0, 2, 3]] >= 0).all()
+
+
+def test_uniform_extremes():
+    d = synth.chain_inputs(20, 3, 2500, "bf16", T=1.0, seed=13)
+    d["uniforms"] = np.zeros_like(d["uniforms"])
+    g, _ = run_case(d, "u0")
+    assert (g["accept_len"] == 3).all()
+    d["uniforms"] = np.full_like(d["uniforms"], np.nextafter(np.float32(1), np.float32(0)))
+    run_case(d, "u-top")
+
+
+def test_repeated_calls_share_workspace():
+    """Counters are left at zero: repeated calls on one workspace agree."""
+    torch, sv = require_gpu()
+    d = synth.chain_inputs(9, 7, 20000, "bf16", T=0.7, seed=14)
+    ws = torch.zeros(sv.spec_verify_chain_workspace_bytes(9, 7, 20000, sv.SV_DTYPE_BF16),
+                     dtype=torch.uint8, device="cuda")
+    first = gpu_chain(d, workspace=ws)
+    for _ in range(3):
+        again = gpu_chain(d, workspace=ws)
+        assert np.array_equal(first["accept_len"], again["accept_len"])
+        assert np.array_equal(first["out_tokens"], again["out_tokens"])
+    assert (ws.cpu().numpy()[-64:] == 0).all()
+
+
+def test_acceptance_frequency_matches_sum_min():
+    """Per-position pass rate against sum_v min(p, q) (z-test over blocks)."""
+    d = synth.chain_inputs(2000, 4, 600, "f32", T=0.8, target=("normal", 1.5), noise=0.6, seed=15)
+    g = gpu_chain(d)
+    alpha = oracle.chain_alpha(d["target"], d["draft"], d["T"])
+    k = g["accept_len"]
+    for i in range(4):
+        reached = k >= i
+        a = alpha[reached, i]
+        sd = np.sqrt((a * (1 - a)).sum())
+        assert abs((k[reached] > i).sum() - a.sum()) < 4.5 * sd, i
+
+
+def test_first_token_chi_square():
+    """gamma = 1: the first committed token must follow p_0 (chi-square)."""
+    from scipy.special import softmax
+    from scipy.stats import chisquare
+
+    rng = np.random.default_rng(16)
+    V, B = 32, 100_000
+    zp = rng.normal(0, 1.0, (2, V)).astype(np.float32)
+    zq = (zp[0] + rng.normal(0, 0.8, V)).astype(np.float32)
+    q = softmax(zq.astype(np.float64))
+    d = dict(target=np.broadcast_to(zp, (B, 2, V)).copy(),
+             draft=np.broadcast_to(zq[None], (B, 1, V)).copy(),
+             draft_tokens=rng.choice(V, size=(B, 1), p=q).astype(np.int32),
+             uniforms=rng.random((B, 2), dtype=np.float32), B=B, gamma=1, V=V, dtype="f32", T=1.0)
+    g = gpu_chain(d)
+    obs = np.bincount(g["out_tokens"][:, 0], minlength=V)
+    p = softmax(zp[0].astype(np.float64))
+    assert chisquare(obs, B * p).pvalue > 1e-4

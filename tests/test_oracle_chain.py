@@ -357,7 +357,8 @@ def test_residual_excludes_overweighted_tokens():
         assert np.allclose(r["final_dist"][b], w / w.sum(), atol=1e-13)
 
 
-@pytest.mark.parametrize("kind", ["nan", "posinf", "allneginf", "token_hi", "token_neg"])
+@pytest.mark.parametrize("kind", ["nan", "posinf", "allneginf", "token_hi", "token_neg",
+                                  "domain"])
 def test_invalid_block_is_flagged_alone(kind):
     d = synth.chain_inputs(B=3, gamma=3, V=20, dtype="f32", T=1.0, seed=12)
     tgt, drf, tok = d["target"].copy(), d["draft"].copy(), d["draft_tokens"].copy()
@@ -369,6 +370,8 @@ def test_invalid_block_is_flagged_alone(kind):
         tgt[1, 0, :] = -np.inf
     elif kind == "token_hi":
         tok[1, 2] = 20
+    elif kind == "domain":
+        drf[1, 1, 3] = 3.0e8  # |m| / T > 2^28
     else:
         tok[1, 0] = -1
     ref = oracle.chain(d["target"], d["draft"], d["draft_tokens"], d["uniforms"], 1.0)
