@@ -42,7 +42,7 @@ void plan_segments(int64_t rows_total, int V, int epv, int64_t target, int min_v
 
 struct ChainPlan {
     int rows, nseg, seg_len, nchunk, chunk_len;
-    size_t off_part, off_dec, off_chunk, off_fin, off_cnt1, off_cnt2, bytes;
+    size_t off_part, off_dec, off_chunk, off_fin, off_cnt1, off_cnt2, off_cnt3, bytes;
 };
 
 int32_t chain_plan(int32_t B, int32_t gamma, int32_t V, int32_t dtype, ChainPlan* p) {
@@ -71,6 +71,8 @@ int32_t chain_plan(int32_t B, int32_t gamma, int32_t V, int32_t dtype, ChainPlan
     p->off_cnt1 = off;
     off = align_up(off + sizeof(unsigned) * static_cast<size_t>(B), 256);
     p->off_cnt2 = off;
+    off = align_up(off + sizeof(unsigned) * static_cast<size_t>(B), 256);
+    p->off_cnt3 = off;
     off = align_up(off + sizeof(unsigned) * static_cast<size_t>(B), 256);
     p->bytes = off;
     return SV_OK;
@@ -182,6 +184,7 @@ extern "C" int32_t spec_verify_chain(const void* target_logits, const void* draf
     a.fin = reinterpret_cast<FinalState*>(ws + p.off_fin);
     a.cnt_stats = reinterpret_cast<unsigned*>(ws + p.off_cnt1);
     a.cnt_final = reinterpret_cast<unsigned*>(ws + p.off_cnt2);
+    a.cnt_dist = reinterpret_cast<unsigned*>(ws + p.off_cnt3);
     a.accept_len = accept_len;
     a.out_tokens = out_tokens;
     a.final_dist = final_dist;

@@ -136,9 +136,10 @@ __device__ void chain_decide(const ChainArgs& a, int b) {
     }
     __syncthreads();
     for (int r = tid; r < rows; r += kThreads) {
-        const Stat* p = a.part + (static_cast<int64_t>(b) * rows + r) * a.nseg;
+        Stat* p = a.part + (static_cast<int64_t>(b) * rows + r) * a.nseg;
         Stat t = p[0];
         for (int s = 1; s < a.nseg; ++s) t = stat_merge(t, p[s]);
+        for (int s = 0; s < a.nseg; ++s) p[s] = Stat{0.0f, 0.0f, 0.0};  // this call's last reader
         const bool ok = isfinite(t.S) && t.S > 0.0 && fabs(static_cast<double>(t.m) / a.T) <= kDomain;
         if (!ok) atomicOr(&s_bad, 1);
         s_L[r] = static_cast<double>(t.R) + log2(t.S);
@@ -328,7 +329,8 @@ __device__ void write_outputs(const ChainArgs& a, int b, int k, int token) {
     if (threadIdx.x == 0) a.accept_len[b] = k;
 }
 
-// Token selection for block b: runs in the last final-draw workgroup.
+// Token selection for block b: runs in the last final-draw workgroup, after
+// every chunk sum of the block is in.  Clears the chunk sums it read.
 template <class E>
 __device__ void chain_select(const ChainArgs& a, int b, const ChainDecision& d, FinalRows<E> rows,
                              DrawRow r) {
@@ -338,7 +340,12 @@ __device__ void chain_select(const ChainArgs& a, int b, const ChainDecision& d, 
     __shared__ int s_int;
     const int tid = threadIdx.x;
     const int g = a.gamma;
-    double wc = tid < a.nchunk ? a.chunk_sum[static_cast<int64_t>(b) * a.nchunk + tid] : 0.0;
+    double wc = 0.0;
+    if (tid < a.nchunk) {
+        double* slot = a.chunk_sum + static_cast<int64_t>(b) * a.nchunk + tid;
+        wc = *slot;
+        *slot = 0.0;
+    }
     double total;
     double excl = block_exclusive_scan(wc, s_waves, &total);
     int fallback = 0;
@@ -399,10 +406,7 @@ __device__ void chain_select(const ChainArgs& a, int b, const ChainDecision& d, 
         token = block_max_int(lastpos, &s_int);
     }
     write_outputs<E>(a, b, d.k, token);
-    if (tid == 0) {
-        a.fin[b] = FinalState{total, fallback, 0};
-        a.cnt_final[b] = 0u;
-    }
+    if (tid == 0 && a.final_dist) a.fin[b] = FinalState{total, fallback, 0};
 }
 
 template <class E>
@@ -420,21 +424,27 @@ __device__ inline DrawRow draw_row(const ChainArgs& a, const ChainDecision& d, b
     return DrawRow{d.Rp, d.Rq, d.dL, a.c_hi, a.c_lo, resid};
 }
 
+// The decision of block b as written by the statistics kernel.  k is clamped
+// to the invalid marker unless it lies in [0, gamma], so no row pointer is
+// ever formed from an out-of-range value.
+__device__ inline ChainDecision load_decision(const ChainArgs& a, int b) {
+    ChainDecision d = a.dec[b];
+    if (d.k < 0 || d.k > a.gamma) d.k = -1;
+    return d;
+}
+
 template <class E>
 __global__ __launch_bounds__(kThreads) void chain_final_kernel(ChainArgs a) {
     __shared__ double s_waves[kWaves];
     __shared__ int s_last;
     const int b = blockIdx.x / a.nchunk;
     const int c = blockIdx.x % a.nchunk;
-    const ChainDecision d = a.dec[b];
-    if (d.k < 0) {
-        if (c == 0) write_outputs<E>(a, b, -1, -1);
-        return;
-    }
-    const FinalRows<E> rows = final_rows<E>(a, b, d.k);
-    const DrawRow r = draw_row(a, d, d.k < a.gamma);
+    const ChainDecision d = load_decision(a, b);
+    const bool valid = d.k >= 0;
+    const FinalRows<E> rows = final_rows<E>(a, b, valid ? d.k : 0);
+    const DrawRow r = draw_row(a, d, valid && d.k < a.gamma);
     const int e0 = c * a.chunk_len, e1 = min(a.V, e0 + a.chunk_len);
-    const double s = block_sum(range_weight_sum<E>(rows, e0, e1, r), s_waves);
+    const double s = valid ? block_sum(range_weight_sum<E>(rows, e0, e1, r), s_waves) : 0.0;
     if (threadIdx.x == 0) {
         a.chunk_sum[static_cast<int64_t>(b) * a.nchunk + c] = s;
         const unsigned prev = arrive(&a.cnt_final[b]);
@@ -443,26 +453,50 @@ __global__ __launch_bounds__(kThreads) void chain_final_kernel(ChainArgs a) {
     __syncthreads();
     if (!s_last) return;
     __threadfence();
-    chain_select<E>(a, b, d, rows, r);
+    if (valid) {
+        chain_select<E>(a, b, d, rows, r);
+    } else {
+        for (int i = threadIdx.x; i < a.nchunk; i += kThreads)
+            a.chunk_sum[static_cast<int64_t>(b) * a.nchunk + i] = 0.0;
+        write_outputs<E>(a, b, -1, -1);
+    }
+    if (threadIdx.x == 0) {
+        // every workgroup of this block has read the decision by now; the
+        // final_dist pass, when requested, still needs it (and clears it)
+        if (!a.final_dist) a.dec[b] = ChainDecision{0, 0.0f, 0.0f, 0.0f};
+        a.cnt_final[b] = 0u;
+    }
 }
 
 template <class E>
 __global__ __launch_bounds__(kThreads) void chain_dist_kernel(ChainArgs a) {
+    __shared__ int s_last;
     const int b = blockIdx.x / a.nchunk;
     const int c = blockIdx.x % a.nchunk;
-    const ChainDecision d = a.dec[b];
+    const ChainDecision d = load_decision(a, b);
+    const FinalState f = a.fin[b];
     const int e0 = c * a.chunk_len, e1 = min(a.V, e0 + a.chunk_len);
     float* out = a.final_dist + static_cast<int64_t>(b) * a.V;
     if (d.k < 0) {
         for (int e = e0 + threadIdx.x; e < e1; e += kThreads) out[e] = 0.0f;
-        return;
+    } else {
+        const FinalRows<E> rows = final_rows<E>(a, b, d.k);
+        const DrawRow r = draw_row(a, d, d.k < a.gamma && !f.fallback);
+        const double inv = 1.0 / f.W;
+        for (int e = e0 + threadIdx.x; e < e1; e += kThreads)
+            out[e] = static_cast<float>(static_cast<double>(weight_at<E>(rows, e, r)) * inv);
     }
-    const FinalState f = a.fin[b];
-    const FinalRows<E> rows = final_rows<E>(a, b, d.k);
-    const DrawRow r = draw_row(a, d, d.k < a.gamma && !f.fallback);
-    const double inv = 1.0 / f.W;
-    for (int e = e0 + threadIdx.x; e < e1; e += kThreads)
-        out[e] = static_cast<float>(static_cast<double>(weight_at<E>(rows, e, r)) * inv);
+    __syncthreads();  // every thread of this workgroup has read dec[b] and fin[b]
+    if (threadIdx.x == 0) {
+        const unsigned prev = arrive(&a.cnt_dist[b]);
+        s_last = (prev == static_cast<unsigned>(a.nchunk - 1));
+    }
+    __syncthreads();
+    if (s_last && threadIdx.x == 0) {
+        a.dec[b] = ChainDecision{0, 0.0f, 0.0f, 0.0f};
+        a.fin[b] = FinalState{0.0, 0, 0};
+        a.cnt_dist[b] = 0u;
+    }
 }
 
 }  // namespace

@@ -50,8 +50,11 @@ struct ChainArgs {
     ChainDecision* dec;     // [B]
     double* chunk_sum;      // [B][nchunk]
     FinalState* fin;        // [B]
-    unsigned* cnt_stats;    // [B] arrival counters (left at zero)
+    // Arrival counters, one per block and kernel.  Every call leaves every
+    // workspace byte it used at zero: the last reader of each region clears it.
+    unsigned* cnt_stats;    // [B]
     unsigned* cnt_final;    // [B]
+    unsigned* cnt_dist;     // [B]
     int32_t* accept_len;
     int32_t* out_tokens;
     float* final_dist;

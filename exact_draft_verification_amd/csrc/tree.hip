@@ -145,13 +145,15 @@ __device__ void tree_resolve(const TreeArgs& a, int b) {
     }
     __syncthreads();
     for (int j = tid; j < n; j += kThreads) {
-        const ArgmaxPart* p = a.part + (static_cast<int64_t>(b) * n + j) * a.nseg;
+        ArgmaxPart* p = a.part + (static_cast<int64_t>(b) * n + j) * a.nseg;
         Best best{p[0].best, p[0].idx};
         uint32_t bad = p[0].bad;
         for (int s = 1; s < a.nseg; ++s) {
             best = best_merge(best, Best{p[s].best, p[s].idx});
             bad |= p[s].bad;
         }
+        // this workgroup is the partials' last reader: leave them cleared
+        for (int s = 0; s < a.nseg; ++s) p[s] = ArgmaxPart{0.0f, 0, 0u, 0u};
         // a valid row has no NaN, no +inf and at least one finite logit
         if (bad || !(best.v > -INFINITY) || best.v == INFINITY) s_bad = 1;
         s_amax[j] = best.idx;

@@ -151,7 +151,7 @@ def test_repeated_calls_share_workspace():
         again = gpu_chain(d, workspace=ws)
         assert np.array_equal(first["accept_len"], again["accept_len"])
         assert np.array_equal(first["out_tokens"], again["out_tokens"])
-    assert (ws.cpu().numpy()[-64:] == 0).all()
+    assert int(torch.count_nonzero(ws)) == 0
 
 
 def test_acceptance_frequency_matches_sum_min():
