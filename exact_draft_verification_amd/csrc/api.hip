@@ -168,9 +168,14 @@ extern "C" int32_t spec_verify_chain(const void* target_logits, const void* draf
     a.B = B;
     a.gamma = gamma;
     a.V = V;
-    const double c = 1.4426950408889634074 / temperature;  // log2(e) / T
-    a.c_hi = static_cast<float>(c);
-    a.c_lo = static_cast<float>(c - static_cast<double>(a.c_hi));
+    // log2(e)/T as c_hi + c_lo with c_hi the largest float strictly below c,
+    // so c_lo > 0: a -inf logit then scales to -inf in both parts and never
+    // meets +inf (which would give NaN) when the two products are added.
+    const double c = 1.4426950408889634074 / temperature;
+    float c_hi = static_cast<float>(c);
+    if (static_cast<double>(c_hi) >= c) c_hi = std::nextafter(c_hi, 0.0f);
+    a.c_hi = c_hi;
+    a.c_lo = static_cast<float>(c - static_cast<double>(c_hi));
     a.c_d = static_cast<double>(a.c_hi) + static_cast<double>(a.c_lo);
     a.T = temperature;
     a.nseg = p.nseg;

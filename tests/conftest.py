@@ -22,3 +22,25 @@ def oracle_mod():
 
     oracle.build(force=False)
     return oracle
+
+
+def pytest_terminal_summary(terminalreporter):
+    import sys
+
+    mod = sys.modules.get("gpu_util")
+    recs = getattr(mod, "RECORDS", None) if mod else None
+    if not recs:
+        return
+    total = sum(r[1] for r in recs)
+    near = sum(r[2] for r in recs)
+    terminalreporter.write_line(
+        f"chain parity: {len(recs)} comparisons, {total} blocks compared exactly, "
+        f"{near} blocks inside the 1e-6 boundary band (excluded)")
+    groups = {}
+    for label, n, b in recs:
+        key = label.split("-s")[0].split("-u")[0]
+        g = groups.setdefault(key, [0, 0])
+        g[0] += n
+        g[1] += b
+    for key, (n, b) in sorted(groups.items()):
+        terminalreporter.write_line(f"  {key}: compared {n}, in band {b}")

@@ -15,6 +15,10 @@ import numpy as np
 BAND = 1e-6
 DIST_TOL = 1e-5
 
+# (label, blocks compared, blocks inside the boundary band) of every chain
+# comparison in this session; printed at the end of the run.
+RECORDS = []
+
 
 def torch_mod():
     import torch
@@ -90,6 +94,7 @@ def compare_chain(gpu, orc, label="", check_dist=True):
             assert err.max() <= DIST_TOL, f"{label}: final_dist max abs error {err.max():.3g}"
         if invalid.any():
             assert (gpu["final_dist"][invalid] == 0).all(), f"{label}: invalid block dist not zero"
+    RECORDS.append((label, int(cmp.sum()), int(near.sum())))
     return int(cmp.sum()), int(near.sum())
 
 
