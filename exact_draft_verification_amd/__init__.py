@@ -2,7 +2,7 @@
 
 Thin Python binding of ``libspecverify.so`` (declared in
 ``include/spec_verify.h``).  It only marshals arguments: it checks dtypes,
-shapes, devices and contiguity, allocates outputs and a zero-filled workspace
+shapes, devices and contiguity, allocates outputs and a scratch workspace
 with torch when the caller passes none, and hands raw device pointers plus the
 current HIP stream to the C ABI.  Every step of the verification runs in the
 library's HIP kernels; there is no CPU path.
@@ -19,8 +19,7 @@ import os as _os
 __all__ = [
     "SV_DTYPE_F32", "SV_DTYPE_BF16", "SpecVerifyError", "library_path", "load_library",
     "spec_verify_chain", "spec_verify_tree_greedy", "spec_verify_chain_workspace_bytes",
-    "spec_verify_tree_greedy_workspace_bytes", "spec_verify_workspace_zero",
-    "spec_verify_status_string",
+    "spec_verify_tree_greedy_workspace_bytes", "spec_verify_status_string",
 ]
 
 SV_DTYPE_F32 = 0
@@ -69,8 +68,6 @@ def load_library():
     lib.spec_verify_chain.restype = I32
     lib.spec_verify_tree_greedy.argtypes = [P, I32, P, P, I32, I32, I32, P, P, P, P, SZ, P, P]
     lib.spec_verify_tree_greedy.restype = I32
-    lib.spec_verify_workspace_zero.argtypes = [P, SZ, P]
-    lib.spec_verify_workspace_zero.restype = I32
     _lib = lib
     return lib
 
@@ -139,16 +136,15 @@ _ws_cache: dict = {}
 
 
 def _workspace(nbytes: int, device, stream):
-    """A zero-filled workspace reused across calls on one device and stream
-    (each call leaves its workspace zero-filled again; calls on one stream
-    never overlap)."""
+    """A scratch workspace reused across calls on one device and stream (calls
+    on one stream never overlap; the library needs no initialised contents)."""
     torch = _torch()
     if stream is None:
         stream = torch.cuda.current_stream(device)
     key = (str(device), int(stream.cuda_stream))
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
     return ws
 
@@ -241,13 +237,3 @@ def spec_verify_tree_greedy(target, parents, tokens, *, accept_len=None, accept_
     if st != 0:
         raise SpecVerifyError(st, "spec_verify_tree_greedy")
     return accept_len, accept_node, out_tokens
-
-
-def spec_verify_workspace_zero(workspace, stream=None) -> None:
-    """Zero-fill a workspace tensor with the library's fill kernel."""
-    lib = load_library()
-    st = lib.spec_verify_workspace_zero(_ptr(workspace),
-                                        workspace.numel() * workspace.element_size(),
-                                        _stream_handle(stream, workspace.device))
-    if st != 0:
-        raise SpecVerifyError(st, "spec_verify_workspace_zero")

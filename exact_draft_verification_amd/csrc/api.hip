@@ -15,7 +15,6 @@ namespace {
 
 constexpr int kThreadsHost = 256;
 constexpr int64_t kTargetUnits = 8192;  // statistics/argmax workgroups to aim for
-constexpr int64_t kTargetChunks = 1024; // final-draw workgroups to aim for
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -42,8 +41,16 @@ void plan_segments(int64_t rows_total, int V, int epv, int64_t target, int min_v
 
 struct ChainPlan {
     int rows, nseg, seg_len, nchunk, chunk_len;
-    size_t off_part, off_dec, off_chunk, off_fin, off_cnt1, off_cnt2, off_cnt3, bytes;
+    size_t off_part, off_zx, off_dec, off_chunk, off_fin, bytes;
 };
+
+// Carves `n` objects of `size` bytes out of the workspace at *off (256-byte
+// aligned regions); returns the region's offset.
+size_t carve(size_t* off, size_t size, size_t n) {
+    const size_t at = *off;
+    *off = align_up(at + size * n, 256);
+    return at;
+}
 
 int32_t chain_plan(int32_t B, int32_t gamma, int32_t V, int32_t dtype, ChainPlan* p) {
     if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
@@ -55,32 +62,31 @@ int32_t chain_plan(int32_t B, int32_t gamma, int32_t V, int32_t dtype, ChainPlan
     // grid sizes in int32
     if (static_cast<double>(rows_total) * V * E > 9.0e18) return SV_ERR_SHAPE;
     p->rows = static_cast<int>(rows);
-    plan_segments(rows_total, V, epv, kTargetUnits, 4, 1 << 16, &p->nseg, &p->seg_len);
+    // a block's rows*nseg partials are staged in LDS by the chunk kernel
+    plan_segments(rows_total, V, epv, kTargetUnits, 4,
+                  static_cast<int>(kMaxBlockParts / rows), &p->nseg, &p->seg_len);
     if (rows_total * p->nseg > INT32_MAX) return SV_ERR_SHAPE;
-    plan_segments(B, V, epv, kTargetChunks, 2, kMaxChunks, &p->nchunk, &p->chunk_len);
+    // final draw: chunks of whole tiles (one 16-byte vector per thread), at
+    // most kMaxChunks per row
+    const int64_t tile = static_cast<int64_t>(kThreadsHost) * epv;
+    const int64_t tiles = ceil_div(V, tile);
+    p->chunk_len = static_cast<int>(tile * ceil_div(tiles, kMaxChunks));
+    p->nchunk = static_cast<int>(ceil_div(V, p->chunk_len));
     if (static_cast<int64_t>(B) * p->nchunk > INT32_MAX) return SV_ERR_SHAPE;
+    const size_t nb = static_cast<size_t>(B), nr = static_cast<size_t>(rows_total);
     size_t off = 0;
-    p->off_part = off;
-    off = align_up(off + sizeof(Stat) * static_cast<size_t>(rows_total) * p->nseg, 256);
-    p->off_dec = off;
-    off = align_up(off + sizeof(ChainDecision) * static_cast<size_t>(B), 256);
-    p->off_chunk = off;
-    off = align_up(off + sizeof(double) * static_cast<size_t>(B) * p->nchunk, 256);
-    p->off_fin = off;
-    off = align_up(off + sizeof(FinalState) * static_cast<size_t>(B), 256);
-    p->off_cnt1 = off;
-    off = align_up(off + sizeof(unsigned) * static_cast<size_t>(B), 256);
-    p->off_cnt2 = off;
-    off = align_up(off + sizeof(unsigned) * static_cast<size_t>(B), 256);
-    p->off_cnt3 = off;
-    off = align_up(off + sizeof(unsigned) * static_cast<size_t>(B), 256);
+    p->off_part = carve(&off, sizeof(Stat), nr * p->nseg);
+    p->off_zx = carve(&off, sizeof(float), nr);
+    p->off_dec = carve(&off, sizeof(ChainDecision), nb);
+    p->off_chunk = carve(&off, sizeof(double), nb * p->nchunk);
+    p->off_fin = carve(&off, sizeof(FinalState), nb);
     p->bytes = off;
     return SV_OK;
 }
 
 struct TreePlan {
     int nseg, seg_len;
-    size_t off_part, off_cnt, bytes;
+    size_t off_part, bytes;
 };
 
 int32_t tree_plan(int32_t B, int32_t n, int32_t V, int32_t dtype, TreePlan* p) {
@@ -89,13 +95,12 @@ int32_t tree_plan(int32_t B, int32_t n, int32_t V, int32_t dtype, TreePlan* p) {
     const int E = elem_bytes(dtype), epv = 16 / E;
     const int64_t rows_total = static_cast<int64_t>(B) * n;
     if (static_cast<double>(rows_total) * V * E > 9.0e18) return SV_ERR_SHAPE;
-    plan_segments(rows_total, V, epv, kTargetUnits, 4, 1 << 16, &p->nseg, &p->seg_len);
+    // a request's n*nseg partials are staged in LDS by the resolve kernel
+    plan_segments(rows_total, V, epv, kTargetUnits, 4, kMaxBlockParts / n, &p->nseg,
+                  &p->seg_len);
     if (rows_total * p->nseg > INT32_MAX) return SV_ERR_SHAPE;
     size_t off = 0;
-    p->off_part = off;
-    off = align_up(off + sizeof(ArgmaxPart) * static_cast<size_t>(rows_total) * p->nseg, 256);
-    p->off_cnt = off;
-    off = align_up(off + sizeof(unsigned) * static_cast<size_t>(B), 256);
+    p->off_part = carve(&off, sizeof(ArgmaxPart), static_cast<size_t>(rows_total) * p->nseg);
     p->bytes = off;
     return SV_OK;
 }
@@ -184,12 +189,10 @@ extern "C" int32_t spec_verify_chain(const void* target_logits, const void* draf
     a.chunk_len = p.chunk_len;
     char* ws = static_cast<char*>(workspace);
     a.part = reinterpret_cast<Stat*>(ws + p.off_part);
+    a.zx = reinterpret_cast<float*>(ws + p.off_zx);
     a.dec = reinterpret_cast<ChainDecision*>(ws + p.off_dec);
     a.chunk_sum = reinterpret_cast<double*>(ws + p.off_chunk);
     a.fin = reinterpret_cast<FinalState*>(ws + p.off_fin);
-    a.cnt_stats = reinterpret_cast<unsigned*>(ws + p.off_cnt1);
-    a.cnt_final = reinterpret_cast<unsigned*>(ws + p.off_cnt2);
-    a.cnt_dist = reinterpret_cast<unsigned*>(ws + p.off_cnt3);
     a.accept_len = accept_len;
     a.out_tokens = out_tokens;
     a.final_dist = final_dist;
@@ -198,7 +201,8 @@ extern "C" int32_t spec_verify_chain(const void* target_logits, const void* draf
     if (record(phase_events, 0, s) != SV_OK) return SV_ERR_HIP;
     if (launch_chain_stats(a, dtype, s) != hipSuccess) return SV_ERR_HIP;
     if (record(phase_events, 1, s) != SV_OK) return SV_ERR_HIP;
-    if (launch_chain_final(a, dtype, s) != hipSuccess) return SV_ERR_HIP;
+    if (launch_chain_chunks(a, dtype, s) != hipSuccess) return SV_ERR_HIP;
+    if (launch_chain_select(a, dtype, s) != hipSuccess) return SV_ERR_HIP;
     if (record(phase_events, 2, s) != SV_OK) return SV_ERR_HIP;
     if (final_dist && launch_chain_dist(a, dtype, s) != hipSuccess) return SV_ERR_HIP;
     return SV_OK;
@@ -232,45 +236,13 @@ extern "C" int32_t spec_verify_tree_greedy(const void* target_logits, int32_t dt
     a.seg_len = p.seg_len;
     char* ws = static_cast<char*>(workspace);
     a.part = reinterpret_cast<ArgmaxPart*>(ws + p.off_part);
-    a.cnt = reinterpret_cast<unsigned*>(ws + p.off_cnt);
     a.accept_len = accept_len;
     a.accept_node = accept_node;
     a.out_tokens = out_tokens;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (record(phase_events, 0, s) != SV_OK) return SV_ERR_HIP;
-    if (launch_tree(a, dtype, s) != hipSuccess) return SV_ERR_HIP;
+    if (launch_tree_argmax(a, dtype, s) != hipSuccess) return SV_ERR_HIP;
     if (record(phase_events, 1, s) != SV_OK) return SV_ERR_HIP;
+    if (launch_tree_resolve(a, s) != hipSuccess) return SV_ERR_HIP;
     return SV_OK;
-}
-
-namespace sv {
-namespace {
-__global__ void zero_kernel(uint4* p, size_t nvec, unsigned char* tail, size_t ntail) {
-    const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
-    for (size_t v = i; v < nvec; v += stride) p[v] = make_uint4(0u, 0u, 0u, 0u);
-    if (i < ntail) tail[i] = 0;
-}
-}  // namespace
-
-hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
-    const size_t nvec = bytes / 16, ntail = bytes % 16;
-    size_t blocks = (nvec + kThreadsHost - 1) / kThreadsHost;
-    if (blocks < 1) blocks = 1;
-    if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreadsHost), 0, s,
-                       static_cast<uint4*>(p), nvec,
-                       static_cast<unsigned char*>(p) + nvec * 16, ntail);
-    return hipGetLastError();
-}
-}  // namespace sv
-
-extern "C" int32_t spec_verify_workspace_zero(void* workspace, size_t workspace_bytes,
-                                              void* stream) {
-    if (!workspace) return SV_ERR_NULL;
-    if (!aligned(workspace, 16)) return SV_ERR_WORKSPACE;
-    if (workspace_bytes == 0) return SV_OK;
-    return launch_zero(workspace, workspace_bytes, static_cast<hipStream_t>(stream)) == hipSuccess
-               ? SV_OK
-               : SV_ERR_HIP;
 }

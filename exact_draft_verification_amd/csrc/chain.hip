@@ -12,24 +12,28 @@
 // from the bonus row p_gamma if every test passed ("A fully accepted block
 // yields more than one committed token"; "JetSpec++", Appendix F.1).
 //
-// Kernels, in stream order:
+// Kernels, in stream order (data crosses workgroups only at kernel
+// boundaries, so no workgroup ever waits on another):
 //  1. chain_stats: one workgroup per (block, row, segment) streams its share
-//     of the 2*gamma+1 rows once and folds it into (m, R, S) statistics; the
-//     last workgroup to finish a block (arrival counter) merges the block's
-//     statistics, evaluates every ratio in fp64 and finds k.
-//  2. chain_final: one workgroup per (block, chunk of the final row) sums the
-//     draw weights of its chunk; the last workgroup of a block scans the chunk
-//     sums, finds the chunk holding u_gamma * W and rescans that chunk alone
-//     in token order to pick the token.
-//  3. chain_dist (only when final_dist is requested): writes the normalised
+//     of the 2*gamma+1 rows once, folds it into (m, R, S) statistics and
+//     writes them as one partial; the workgroup whose segment holds a row's
+//     draft token also records that token's logit.
+//  2. chain_chunks: one workgroup per (block, chunk of the vocabulary) merges
+//     the block's partials (staged in LDS), evaluates every ratio of the block
+//     in fp64, finds the first rejection k, and sums the draw weights of its
+//     chunk of the final row (residual row k, or the bonus row).
+//  3. chain_select: one workgroup per block scans the chunk sums, finds the
+//     chunk holding u_gamma * W and resolves the token inside it with one
+//     workgroup-wide prefix sum in token order.
+//  4. chain_dist (only when final_dist is requested): writes the normalised
 //     draw distribution.
 //
 // Numerics.  Ratios are evaluated in the log2 domain in fp64 from the row
 // statistics, so they are accurate to about 1e-8 whatever the dynamic range.
 // The residual weight is formed as p(v) * (1 - 2^-D(v)) with
-// D(v) = log2 p(v) - log2 q(v) computed from the logit difference, which
-// avoids the cancellation of p - q when the two rows are close; weights are
-// fp32, sums and prefix sums fp64.
+// D(v) = log2 p(v) - log2 q(v) computed in fp64 from the logit difference, so
+// neither the subtraction p - q nor a constant offset between the target and
+// draft logits costs precision; weights are fp32, sums and prefix sums fp64.
 #include "sv_device.hpp"
 
 namespace sv {
@@ -38,6 +42,7 @@ namespace {
 
 constexpr double kDomain = 268435456.0;  // |m| / T limit (2^28)
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr int kStreamU = 4;              // 16-byte vectors per thread per batch
 
 template <class E>
 __device__ inline const typename E::storage* chain_row(const ChainArgs& a, int b, int rho) {
@@ -49,113 +54,123 @@ __device__ inline const typename E::storage* chain_row(const ChainArgs& a, int b
            (static_cast<int64_t>(b) * a.gamma + (rho - a.gamma - 1)) * static_cast<int64_t>(a.V);
 }
 
-// Statistics of elements [e0, e1) of one row, folded by the whole workgroup.
+template <class E>
+struct StatFolder {
+    Stat s;
+    float c_hi, c_lo;
+    template <int N>
+    __device__ inline void batch(const uint4* v, int) {
+        float x[N * E::kPerVec];
+#pragma unroll
+        for (int u = 0; u < N; ++u) E::unpack(v[u], x + u * E::kPerVec);
+        stat_fold<N * E::kPerVec>(s, x, c_hi, c_lo);
+    }
+};
+
+// Statistics of elements [e0, e1) of one row, folded by the whole workgroup
+// (one partial per thread).
 template <class E>
 __device__ inline Stat row_range_stats(const typename E::storage* row, int e0, int e1, float c_hi,
                                        float c_lo) {
-    constexpr int U = 4;                 // 16-byte vectors per thread per batch
-    constexpr int NB = U * E::kPerVec;   // elements per thread per batch
-    constexpr int kBatchVec = kThreads * U;
+    StatFolder<E> f{stat_empty(), c_hi, c_lo};
+    if (e0 >= e1) return f.s;
     const int tid = threadIdx.x;
-    Stat st = stat_empty();
-    if (e0 >= e1) return st;
     const RangeSplit<E> sp = split_range<E>(row, e0, e1);
     for (int e = sp.head_begin + tid; e < sp.head_end; e += kThreads) {
         float x = E::one(row + e);
-        stat_fold<1>(st, &x, c_hi, c_lo);
+        stat_fold<1>(f.s, &x, c_hi, c_lo);
     }
-    const char* body = reinterpret_cast<const char*>(row + sp.body_begin);
-    const int nfull = sp.nvec / kBatchVec;
-    if (nfull > 0) {
-        // Two register buffers alternate so that the loads of batch t+1 are in
-        // flight while batch t is folded.
-        uint4 A[U], Bv[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) A[u] = load16(body + static_cast<size_t>(u * kThreads + tid) * 16);
-        for (int t = 0; t < nfull; t += 2) {
-            const bool has1 = t + 1 < nfull;
-            if (has1) {
-                const char* nb = body + static_cast<size_t>(t + 1) * kBatchVec * 16;
-#pragma unroll
-                for (int u = 0; u < U; ++u) Bv[u] = load16(nb + static_cast<size_t>(u * kThreads + tid) * 16);
-            }
-            {
-                float x[NB];
-#pragma unroll
-                for (int u = 0; u < U; ++u) E::unpack(A[u], x + u * E::kPerVec);
-                if (t + 2 < nfull) {
-                    const char* nb = body + static_cast<size_t>(t + 2) * kBatchVec * 16;
-#pragma unroll
-                    for (int u = 0; u < U; ++u) A[u] = load16(nb + static_cast<size_t>(u * kThreads + tid) * 16);
-                }
-                stat_fold<NB>(st, x, c_hi, c_lo);
-            }
-            if (has1) {
-                float x[NB];
-#pragma unroll
-                for (int u = 0; u < U; ++u) E::unpack(Bv[u], x + u * E::kPerVec);
-                stat_fold<NB>(st, x, c_hi, c_lo);
+    stream_vectors<kStreamU>(reinterpret_cast<const char*>(row + sp.body_begin), sp.nvec, f);
+    for (int e = sp.tail_begin + tid; e < sp.tail_end; e += kThreads) {
+        float x = E::one(row + e);
+        stat_fold<1>(f.s, &x, c_hi, c_lo);
+    }
+    return f.s;
+}
+
+template <class E>
+__global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
+    __shared__ Stat s_w[kWaves];
+    const int rows = 2 * a.gamma + 1;
+    const int unit = blockIdx.x;
+    const int seg = unit % a.nseg;
+    const int rr = unit / a.nseg;  // b * rows + rho
+    const int rho = rr % rows;
+    const int b = rr / rows;
+    const int tid = threadIdx.x;
+    const auto* row = chain_row<E>(a, b, rho);
+    const int e0 = seg * a.seg_len;
+    const int e1 = min(a.V, e0 + a.seg_len);
+    // The logit of this row's draft token, if it lies in this segment (the
+    // load is issued before the stream so its latency is hidden).  Rows
+    // i < gamma (target) and gamma+1+i (draft) belong to draft position i.
+    float zx = 0.0f;
+    bool have_zx = false;
+    if (tid == 0) {
+        const int i = rho < a.gamma ? rho : (rho > a.gamma ? rho - a.gamma - 1 : -1);
+        if (i >= 0) {
+            const int x = a.tokens[static_cast<int64_t>(b) * a.gamma + i];
+            if (x >= e0 && x < e1) {
+                zx = E::one(row + x);
+                have_zx = true;
             }
         }
     }
-    for (int v = nfull * kBatchVec + tid; v < sp.nvec; v += kThreads) {
-        float x[E::kPerVec];
-        E::unpack(load16(body + static_cast<size_t>(v) * 16), x);
-        stat_fold<E::kPerVec>(st, x, c_hi, c_lo);
+    Stat st = row_range_stats<E>(row, e0, e1, a.c_hi, a.c_lo);
+    st = block_reduce_stat(st, s_w);
+    if (tid == 0) {
+        a.part[unit] = st;
+        if (have_zx) a.zx[rr] = zx;
     }
-    for (int e = sp.tail_begin + tid; e < sp.tail_end; e += kThreads) {
-        float x = E::one(row + e);
-        stat_fold<1>(st, &x, c_hi, c_lo);
-    }
-    return st;
 }
 
-__device__ inline Stat block_reduce_stat(Stat st) {
-    __shared__ Stat s_w[kWaves];
-    st = wave_reduce_stat(st);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane == 0) s_w[wave] = st;
-    __syncthreads();
-    Stat r = s_w[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) r = stat_merge(r, s_w[w]);
-    return r;
-}
-
-// Ratio tests of block b: runs in the last statistics workgroup of the block.
+// Ratio tests of block b (every workgroup of the block's final draw takes
+// them for itself): merges the block's row partials, staged in LDS, then for
+// each draft position i evaluates r_i = min(1, p_i(x_i)/q_i(x_i)) in the
+// log2 domain in fp64 and keeps the first i with u_i >= r_i.
 template <class E>
-__device__ void chain_decide(const ChainArgs& a, int b) {
-    using S = typename E::storage;
+__device__ ChainDecision chain_decide(const ChainArgs& a, int b, Stat* s_part) {
     __shared__ double s_L[2 * kMaxGamma + 1];
     __shared__ float s_R[2 * kMaxGamma + 1];
     __shared__ int s_bad, s_k;
+    constexpr int kPer = kMaxBlockParts / kThreads;
     const int g = a.gamma, rows = 2 * g + 1, tid = threadIdx.x;
+    const int np = rows * a.nseg;
+    const Stat* src = a.part + static_cast<int64_t>(b) * np;
+    {
+        // every load issued before any LDS store (indices past the end
+        // re-read the last partial and are not stored)
+        Stat t[kPer];
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) t[m] = src[min(tid + m * kThreads, np - 1)];
+#pragma unroll
+        for (int m = 0; m < kPer; ++m)
+            if (tid + m * kThreads < np) s_part[tid + m * kThreads] = t[m];
+    }
     if (tid == 0) {
         s_bad = 0;
         s_k = g;
     }
     __syncthreads();
     for (int r = tid; r < rows; r += kThreads) {
-        Stat* p = a.part + (static_cast<int64_t>(b) * rows + r) * a.nseg;
+        const Stat* p = s_part + r * a.nseg;
         Stat t = p[0];
         for (int s = 1; s < a.nseg; ++s) t = stat_merge(t, p[s]);
-        for (int s = 0; s < a.nseg; ++s) p[s] = Stat{0.0f, 0.0f, 0.0};  // this call's last reader
         const bool ok = isfinite(t.S) && t.S > 0.0 && fabs(static_cast<double>(t.m) / a.T) <= kDomain;
         if (!ok) atomicOr(&s_bad, 1);
         s_L[r] = static_cast<double>(t.R) + log2(t.S);
         s_R[r] = t.R;
     }
     __syncthreads();
-    const S* tg = static_cast<const S*>(a.target) + static_cast<int64_t>(b) * (g + 1) * a.V;
-    const S* dr = static_cast<const S*>(a.draft) + static_cast<int64_t>(b) * g * a.V;
+    const float* zx = a.zx + static_cast<int64_t>(b) * rows;
     for (int i = tid; i < g; i += kThreads) {
         const int x = a.tokens[static_cast<int64_t>(b) * g + i];
         if (x < 0 || x >= a.V) {
             atomicOr(&s_bad, 1);
             continue;
         }
-        const float zp = E::one(tg + static_cast<int64_t>(i) * a.V + x);
-        const float zq = E::one(dr + static_cast<int64_t>(i) * a.V + x);
+        const float zp = zx[i];
+        const float zq = zx[g + 1 + i];
         double r;
         if (zp == -INFINITY) {
             r = 0.0;
@@ -171,58 +186,26 @@ __device__ void chain_decide(const ChainArgs& a, int b) {
         if (!(u < r)) atomicMin(&s_k, i);
     }
     __syncthreads();
-    if (tid == 0) {
-        ChainDecision d;
-        if (s_bad) {
-            d.k = -1;
-            d.Rp = d.Rq = d.dL = 0.0f;
-        } else {
-            const int k = s_k;
-            d.k = k;
-            d.Rp = s_R[k];
-            if (k < g) {
-                d.Rq = s_R[g + 1 + k];
-                d.dL = static_cast<float>(s_L[k] - s_L[g + 1 + k]);
-            } else {
-                d.Rq = 0.0f;
-                d.dL = 0.0f;
-            }
-        }
-        a.dec[b] = d;
-        a.cnt_stats[b] = 0u;  // leave the counter ready for the next call
+    ChainDecision d;
+    if (s_bad) {
+        d.k = -1;
+        d.Rp = 0.0f;
+        d.dL = 0.0;
+    } else {
+        const int k = s_k;
+        d.k = k;
+        d.Rp = s_R[k];
+        d.dL = k < g ? s_L[k] - s_L[g + 1 + k] : 0.0;
     }
-}
-
-template <class E>
-__global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
-    const int rows = 2 * a.gamma + 1;
-    const int unit = blockIdx.x;
-    const int seg = unit % a.nseg;
-    const int rr = unit / a.nseg;
-    const int rho = rr % rows;
-    const int b = rr / rows;
-    const auto* row = chain_row<E>(a, b, rho);
-    const int e0 = seg * a.seg_len;
-    const int e1 = min(a.V, e0 + a.seg_len);
-    Stat st = row_range_stats<E>(row, e0, e1, a.c_hi, a.c_lo);
-    st = block_reduce_stat(st);
-    __shared__ int s_last;
-    if (threadIdx.x == 0) {
-        a.part[unit] = st;
-        const unsigned prev = arrive(&a.cnt_stats[b]);
-        s_last = (prev == static_cast<unsigned>(rows * a.nseg - 1));
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    chain_decide<E>(a, b);
+    return d;
 }
 
 // ---------------------------------------------------------------------------
 // Final draw.
 
 struct DrawRow {
-    float Rp, Rq, dL, c_hi, c_lo;
+    float Rp, c_hi, c_lo;
+    double c_d, dL;
     bool resid;  // residual of p_k and q_k (else p_k itself, unnormalised)
 };
 
@@ -235,10 +218,9 @@ __device__ inline float draw_weight(float zp, float zq, const DrawRow& r) {
     t = fmaf(zp, r.c_lo, t);
     const float P = __builtin_amdgcn_exp2f(t);
     if (!r.resid || zq == -INFINITY) return P;
-    const float dz = zp - zq;
-    const float D = fmaf(dz, r.c_hi, fmaf(dz, r.c_lo, -r.dL));
-    if (!(D > 0.0f)) return 0.0f;
-    return P * (-expm1f(-D * kLn2));
+    const double D = fma(static_cast<double>(zp) - static_cast<double>(zq), r.c_d, -r.dL);
+    if (!(D > 0.0)) return 0.0f;
+    return P * (-expm1f(static_cast<float>(-D) * kLn2));
 }
 
 template <class E>
@@ -250,7 +232,8 @@ struct FinalRows {
 // Sum of draw weights over elements [e0, e1) by the whole workgroup (per
 // thread partial, fp64).
 template <class E>
-__device__ inline double range_weight_sum(const FinalRows<E>& rows, int e0, int e1, const DrawRow& r) {
+__device__ inline double range_weight_sum(const FinalRows<E>& rows, int e0, int e1,
+                                          const DrawRow& r) {
     const int tid = threadIdx.x;
     double acc = 0.0;
     if (e0 >= e1) return acc;
@@ -260,56 +243,34 @@ __device__ inline double range_weight_sum(const FinalRows<E>& rows, int e0, int 
         !r.resid || ((reinterpret_cast<uintptr_t>(q) - reinterpret_cast<uintptr_t>(p)) & 15u) == 0;
     if (!same_align) {
         for (int e = e0 + tid; e < e1; e += kThreads)
-            acc += draw_weight(E::one(p + e), E::one(q + e), r);
+            acc += static_cast<double>(draw_weight(E::one(p + e), E::one(q + e), r));
         return acc;
     }
     const RangeSplit<E> sp = split_range<E>(p, e0, e1);
     for (int e = sp.head_begin + tid; e < sp.head_end; e += kThreads)
-        acc += draw_weight(E::one(p + e), r.resid ? E::one(q + e) : 0.0f, r);
+        acc += static_cast<double>(draw_weight(E::one(p + e), r.resid ? E::one(q + e) : 0.0f, r));
     const char* pb = reinterpret_cast<const char*>(p + sp.body_begin);
     const char* qb = r.resid ? reinterpret_cast<const char*>(q + sp.body_begin) : nullptr;
     for (int v = tid; v < sp.nvec; v += kThreads) {
         float xp[E::kPerVec], xq[E::kPerVec];
-        E::unpack(load16(pb + static_cast<size_t>(v) * 16), xp);
+        E::unpack(load16_stream(pb + static_cast<size_t>(v) * 16), xp);
         if (r.resid) {
-            E::unpack(load16(qb + static_cast<size_t>(v) * 16), xq);
+            E::unpack(load16_stream(qb + static_cast<size_t>(v) * 16), xq);
         } else {
 #pragma unroll
             for (int i = 0; i < E::kPerVec; ++i) xq[i] = 0.0f;
         }
-        float s = 0.0f;
 #pragma unroll
-        for (int i = 0; i < E::kPerVec; ++i) s += draw_weight(xp[i], xq[i], r);
-        acc += static_cast<double>(s);
+        for (int i = 0; i < E::kPerVec; ++i) acc += static_cast<double>(draw_weight(xp[i], xq[i], r));
     }
     for (int e = sp.tail_begin + tid; e < sp.tail_end; e += kThreads)
-        acc += draw_weight(E::one(p + e), r.resid ? E::one(q + e) : 0.0f, r);
+        acc += static_cast<double>(draw_weight(E::one(p + e), r.resid ? E::one(q + e) : 0.0f, r));
     return acc;
 }
 
 template <class E>
 __device__ inline float weight_at(const FinalRows<E>& rows, int e, const DrawRow& r) {
     return draw_weight(E::one(rows.p + e), r.resid ? E::one(rows.q + e) : 0.0f, r);
-}
-
-__device__ inline int block_min_int(int v, int* lds) {
-    if (threadIdx.x == 0) *lds = INT32_MAX;
-    __syncthreads();
-    atomicMin(lds, v);
-    __syncthreads();
-    const int r = *lds;
-    __syncthreads();
-    return r;
-}
-
-__device__ inline int block_max_int(int v, int* lds) {
-    if (threadIdx.x == 0) *lds = INT32_MIN;
-    __syncthreads();
-    atomicMax(lds, v);
-    __syncthreads();
-    const int r = *lds;
-    __syncthreads();
-    return r;
 }
 
 template <class E>
@@ -329,23 +290,27 @@ __device__ void write_outputs(const ChainArgs& a, int b, int k, int token) {
     if (threadIdx.x == 0) a.accept_len[b] = k;
 }
 
-// Token selection for block b: runs in the last final-draw workgroup, after
-// every chunk sum of the block is in.  Clears the chunk sums it read.
+// Token selection for block b (one workgroup), from the chunk sums of the
+// chunk kernel.
+//
+// The draw is the smallest token v whose inclusive prefix sum of weights
+// exceeds u * W (W the total).  The chunk holding that crossing is found from
+// the chunk sums (one per thread, one workgroup-wide scan); inside the chunk,
+// tile by tile, thread t holds the kPerVec consecutive tokens starting at
+// tile + t*kPerVec, so one more workgroup scan of the per-thread sums puts
+// every token's prefix in token order.  If rounding leaves no crossing, the
+// last token of positive weight is taken.
 template <class E>
-__device__ void chain_select(const ChainArgs& a, int b, const ChainDecision& d, FinalRows<E> rows,
-                             DrawRow r) {
+__device__ void chain_select(const ChainArgs& a, int b, const ChainDecision& d,
+                             const FinalRows<E>& rows, DrawRow r) {
     __shared__ double s_waves[kWaves];
-    __shared__ double s_chunk[kMaxChunks];
-    __shared__ double s_excl;
+    __shared__ double s_base;
     __shared__ int s_int;
+    constexpr int kTile = kThreads * E::kPerVec;
     const int tid = threadIdx.x;
     const int g = a.gamma;
     double wc = 0.0;
-    if (tid < a.nchunk) {
-        double* slot = a.chunk_sum + static_cast<int64_t>(b) * a.nchunk + tid;
-        wc = *slot;
-        *slot = 0.0;
-    }
+    if (tid < a.nchunk) wc = a.chunk_sum[static_cast<int64_t>(b) * a.nchunk + tid];
     double total;
     double excl = block_exclusive_scan(wc, s_waves, &total);
     int fallback = 0;
@@ -354,57 +319,64 @@ __device__ void chain_select(const ChainArgs& a, int b, const ChainDecision& d, 
         // rejection): sample from p_k instead.
         fallback = 1;
         r.resid = false;
+        double mine = 0.0;
         for (int c = 0; c < a.nchunk; ++c) {
             const int e0 = c * a.chunk_len, e1 = min(a.V, e0 + a.chunk_len);
             const double s = block_sum(range_weight_sum<E>(rows, e0, e1, r), s_waves);
-            if (tid == 0) s_chunk[c] = s;
+            if (tid == c) mine = s;
         }
-        __syncthreads();
-        wc = tid < a.nchunk ? s_chunk[tid] : 0.0;
+        wc = mine;
         excl = block_exclusive_scan(wc, s_waves, &total);
     }
-    const double target = static_cast<double>(a.uniforms[static_cast<int64_t>(b) * (g + 1) + g]) * total;
+    const double target =
+        static_cast<double>(a.uniforms[static_cast<int64_t>(b) * (g + 1) + g]) * total;
     // first chunk whose inclusive prefix exceeds the target
-    int cand = (tid < a.nchunk && wc > 0.0 && excl + wc > target) ? tid : INT32_MAX;
+    const int cand = (tid < a.nchunk && wc > 0.0 && excl + wc > target) ? tid : INT32_MAX;
     int cstar = block_min_int(cand, &s_int);
     bool last_positive = false;
     if (cstar == INT32_MAX) {
-        // no crossing (rounding, or u >= 1): last token of positive weight
+        // no crossing (rounding): the last token of positive weight
         cstar = block_max_int((tid < a.nchunk && wc > 0.0) ? tid : -1, &s_int);
         last_positive = true;
         if (cstar < 0) cstar = 0;  // no positive weight at all: keep every read in range
     }
-    if (tid == 0) s_excl = 0.0;
+    if (tid == cstar) s_base = excl;
     __syncthreads();
-    if (tid == cstar) s_excl = excl;
-    __syncthreads();
-    const double base = s_excl;
+    double base = s_base;
     const int e0 = cstar * a.chunk_len, e1 = min(a.V, e0 + a.chunk_len);
-    const int len = e1 - e0;
-    const int per = (len + kThreads - 1) / kThreads;
-    const int m0 = min(e1, e0 + tid * per), m1 = min(e1, m0 + per);
-    double mine = 0.0;
-    for (int e = m0; e < m1; ++e) mine += static_cast<double>(weight_at<E>(rows, e, r));
-    double tot2;
-    const double my_excl = block_exclusive_scan(mine, s_waves, &tot2);
-    int found = INT32_MAX;
-    if (!last_positive) {
+    int token = -1, lastpos = -1;
+    for (int t0 = e0; t0 < e1; t0 += kTile) {
+        float w[E::kPerVec];
+        double mine = 0.0;
+        const int my0 = t0 + tid * E::kPerVec;
+#pragma unroll
+        for (int i = 0; i < E::kPerVec; ++i) {
+            const int e = my0 + i;
+            w[i] = e < e1 ? weight_at<E>(rows, e, r) : 0.0f;
+            mine += static_cast<double>(w[i]);
+        }
+        double tile_total;
+        const double my_excl = block_exclusive_scan(mine, s_waves, &tile_total);
+        int found = INT32_MAX, lp = -1;
         double run = base + my_excl;
-        for (int e = m0; e < m1; ++e) {
-            run += static_cast<double>(weight_at<E>(rows, e, r));
-            if (run > target) {
-                found = e;
-                break;
+#pragma unroll
+        for (int i = 0; i < E::kPerVec; ++i) {
+            run += static_cast<double>(w[i]);
+            if (w[i] > 0.0f) {
+                lp = my0 + i;
+                if (!last_positive && found == INT32_MAX && run > target) found = my0 + i;
             }
         }
+        found = block_min_int(found, &s_int);
+        lp = block_max_int(lp, &s_int);
+        if (lp >= 0) lastpos = lp;
+        if (found != INT32_MAX) {
+            token = found;
+            break;
+        }
+        base += tile_total;
     }
-    int token = block_min_int(found, &s_int);
-    if (token == INT32_MAX) {
-        int lastpos = -1;
-        for (int e = m0; e < m1; ++e)
-            if (weight_at<E>(rows, e, r) > 0.0f) lastpos = e;
-        token = block_max_int(lastpos, &s_int);
-    }
+    if (token < 0) token = lastpos >= 0 ? lastpos : e0;
     write_outputs<E>(a, b, d.k, token);
     if (tid == 0 && a.final_dist) a.fin[b] = FinalState{total, fallback, 0};
 }
@@ -421,12 +393,12 @@ __device__ inline FinalRows<E> final_rows(const ChainArgs& a, int b, int k) {
 }
 
 __device__ inline DrawRow draw_row(const ChainArgs& a, const ChainDecision& d, bool resid) {
-    return DrawRow{d.Rp, d.Rq, d.dL, a.c_hi, a.c_lo, resid};
+    return DrawRow{d.Rp, a.c_hi, a.c_lo, a.c_d, d.dL, resid};
 }
 
-// The decision of block b as written by the statistics kernel.  k is clamped
-// to the invalid marker unless it lies in [0, gamma], so no row pointer is
-// ever formed from an out-of-range value.
+// The decision of block b as written by the chunk kernel.  k is clamped to
+// the invalid marker unless it lies in [0, gamma], so no row pointer is ever
+// formed from an out-of-range value.
 __device__ inline ChainDecision load_decision(const ChainArgs& a, int b) {
     ChainDecision d = a.dec[b];
     if (d.k < 0 || d.k > a.gamma) d.k = -1;
@@ -434,12 +406,12 @@ __device__ inline ChainDecision load_decision(const ChainArgs& a, int b) {
 }
 
 template <class E>
-__global__ __launch_bounds__(kThreads) void chain_final_kernel(ChainArgs a) {
+__global__ __launch_bounds__(kThreads) void chain_chunks_kernel(ChainArgs a) {
+    extern __shared__ Stat s_part[];  // [2*gamma+1][nseg]
     __shared__ double s_waves[kWaves];
-    __shared__ int s_last;
     const int b = blockIdx.x / a.nchunk;
     const int c = blockIdx.x % a.nchunk;
-    const ChainDecision d = load_decision(a, b);
+    const ChainDecision d = chain_decide<E>(a, b, s_part);
     const bool valid = d.k >= 0;
     const FinalRows<E> rows = final_rows<E>(a, b, valid ? d.k : 0);
     const DrawRow r = draw_row(a, d, valid && d.k < a.gamma);
@@ -447,56 +419,39 @@ __global__ __launch_bounds__(kThreads) void chain_final_kernel(ChainArgs a) {
     const double s = valid ? block_sum(range_weight_sum<E>(rows, e0, e1, r), s_waves) : 0.0;
     if (threadIdx.x == 0) {
         a.chunk_sum[static_cast<int64_t>(b) * a.nchunk + c] = s;
-        const unsigned prev = arrive(&a.cnt_final[b]);
-        s_last = (prev == static_cast<unsigned>(a.nchunk - 1));
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    if (valid) {
-        chain_select<E>(a, b, d, rows, r);
-    } else {
-        for (int i = threadIdx.x; i < a.nchunk; i += kThreads)
-            a.chunk_sum[static_cast<int64_t>(b) * a.nchunk + i] = 0.0;
-        write_outputs<E>(a, b, -1, -1);
-    }
-    if (threadIdx.x == 0) {
-        // every workgroup of this block has read the decision by now; the
-        // final_dist pass, when requested, still needs it (and clears it)
-        if (!a.final_dist) a.dec[b] = ChainDecision{0, 0.0f, 0.0f, 0.0f};
-        a.cnt_final[b] = 0u;
+        if (c == 0) a.dec[b] = d;
     }
 }
 
 template <class E>
+__global__ __launch_bounds__(kThreads) void chain_select_kernel(ChainArgs a) {
+    const int b = blockIdx.x;
+    const ChainDecision d = load_decision(a, b);
+    if (d.k < 0) {
+        write_outputs<E>(a, b, -1, -1);
+        return;
+    }
+    const FinalRows<E> rows = final_rows<E>(a, b, d.k);
+    chain_select<E>(a, b, d, rows, draw_row(a, d, d.k < a.gamma));
+}
+
+template <class E>
 __global__ __launch_bounds__(kThreads) void chain_dist_kernel(ChainArgs a) {
-    __shared__ int s_last;
     const int b = blockIdx.x / a.nchunk;
     const int c = blockIdx.x % a.nchunk;
     const ChainDecision d = load_decision(a, b);
-    const FinalState f = a.fin[b];
     const int e0 = c * a.chunk_len, e1 = min(a.V, e0 + a.chunk_len);
     float* out = a.final_dist + static_cast<int64_t>(b) * a.V;
     if (d.k < 0) {
         for (int e = e0 + threadIdx.x; e < e1; e += kThreads) out[e] = 0.0f;
-    } else {
-        const FinalRows<E> rows = final_rows<E>(a, b, d.k);
-        const DrawRow r = draw_row(a, d, d.k < a.gamma && !f.fallback);
-        const double inv = 1.0 / f.W;
-        for (int e = e0 + threadIdx.x; e < e1; e += kThreads)
-            out[e] = static_cast<float>(static_cast<double>(weight_at<E>(rows, e, r)) * inv);
+        return;
     }
-    __syncthreads();  // every thread of this workgroup has read dec[b] and fin[b]
-    if (threadIdx.x == 0) {
-        const unsigned prev = arrive(&a.cnt_dist[b]);
-        s_last = (prev == static_cast<unsigned>(a.nchunk - 1));
-    }
-    __syncthreads();
-    if (s_last && threadIdx.x == 0) {
-        a.dec[b] = ChainDecision{0, 0.0f, 0.0f, 0.0f};
-        a.fin[b] = FinalState{0.0, 0, 0};
-        a.cnt_dist[b] = 0u;
-    }
+    const FinalState f = a.fin[b];
+    const FinalRows<E> rows = final_rows<E>(a, b, d.k);
+    const DrawRow r = draw_row(a, d, d.k < a.gamma && !f.fallback);
+    const double inv = 1.0 / f.W;
+    for (int e = e0 + threadIdx.x; e < e1; e += kThreads)
+        out[e] = static_cast<float>(static_cast<double>(weight_at<E>(rows, e, r)) * inv);
 }
 
 }  // namespace
@@ -510,12 +465,21 @@ hipError_t launch_chain_stats(const ChainArgs& a, int dtype, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_chain_final(const ChainArgs& a, int dtype, hipStream_t s) {
+hipError_t launch_chain_chunks(const ChainArgs& a, int dtype, hipStream_t s) {
     const int grid = a.B * a.nchunk;
+    const size_t lds = sizeof(Stat) * static_cast<size_t>(2 * a.gamma + 1) * a.nseg;
     if (dtype == 0)
-        hipLaunchKernelGGL(chain_final_kernel<F32>, dim3(grid), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(chain_chunks_kernel<F32>, dim3(grid), dim3(kThreads), lds, s, a);
     else
-        hipLaunchKernelGGL(chain_final_kernel<BF16>, dim3(grid), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(chain_chunks_kernel<BF16>, dim3(grid), dim3(kThreads), lds, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_chain_select(const ChainArgs& a, int dtype, hipStream_t s) {
+    if (dtype == 0)
+        hipLaunchKernelGGL(chain_select_kernel<F32>, dim3(a.B), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(chain_select_kernel<BF16>, dim3(a.B), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -84,6 +84,65 @@ __device__ inline RangeSplit<E> split_range(const typename E::storage* row, int 
 // Plain 16-byte load that the compiler may schedule freely.
 __device__ inline uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Streaming 16-byte load: the logits are read exactly once, so the load is
+// marked non-temporal and does not displace reusable lines in the caches.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ inline uint4 load16_stream(const void* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Streams the 16-byte vectors [0, nvec) of `body` through f.  Batches of U
+// vectors per thread (kThreads*U per workgroup) are software-pipelined: the
+// loads of batch t+1 are issued before batch t is folded, and every load is
+// unconditional, so the only wait before a fold is for that batch's own
+// loads.  The fewer than kThreads*U vectors left after the whole batches are
+// loaded before the last whole batch is folded (a thread whose index falls
+// past the end re-reads the final vector and discards it).
+//
+// f.template batch<N>(const uint4* v, int v0) folds N vectors; vector u of
+// the call is body vector v0 + u*kThreads.
+template <int U, class F>
+__device__ inline void stream_vectors(const char* body, int nvec, F& f) {
+    if (nvec <= 0) return;
+    const int tid = threadIdx.x;
+    constexpr int kBatch = kThreads * U;
+    const int nb = nvec / kBatch;
+    const int rest0 = nb * kBatch;
+    uint4 rest[U];
+    if (nb > 0) {
+        uint4 cur[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) cur[u] = load16_stream(body + static_cast<size_t>(u * kThreads + tid) * 16);
+        for (int t = 0; t + 1 < nb; ++t) {
+            uint4 nxt[U];
+            const char* nbp = body + static_cast<size_t>(t + 1) * kBatch * 16;
+#pragma unroll
+            for (int u = 0; u < U; ++u) nxt[u] = load16_stream(nbp + static_cast<size_t>(u * kThreads + tid) * 16);
+            f.template batch<U>(cur, t * kBatch + tid);
+#pragma unroll
+            for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = min(rest0 + u * kThreads + tid, nvec - 1);
+            rest[u] = load16_stream(body + static_cast<size_t>(v) * 16);
+        }
+        f.template batch<U>(cur, (nb - 1) * kBatch + tid);
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = min(u * kThreads + tid, nvec - 1);
+            rest[u] = load16_stream(body + static_cast<size_t>(v) * 16);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int v = rest0 + u * kThreads + tid;
+        if (v < nvec) f.template batch<1>(&rest[u], v);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Row statistics of a temperature softmax, kept as (m, R, S):
 //   m  the largest logit seen (for the domain check),
@@ -168,10 +227,19 @@ __device__ inline Stat wave_reduce_stat(Stat s) {
     return s;
 }
 
-__device__ inline double wave_sum(double v) {
+// Workgroup-wide merge of one Stat per thread; every thread gets the result.
+// Uses kWaves Stats of LDS and is safe to call repeatedly (it synchronises
+// before reusing the LDS slots).
+__device__ inline Stat block_reduce_stat(Stat st, Stat* lds_waves) {
+    st = wave_reduce_stat(st);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) lds_waves[wave] = st;
+    __syncthreads();
+    Stat r = lds_waves[0];
 #pragma unroll
-    for (int mask = 32; mask >= 1; mask >>= 1) v += wave_xor(v, mask);
-    return v;
+    for (int w = 1; w < kWaves; ++w) r = stat_merge(r, lds_waves[w]);
+    return r;
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave (Hillis-Steele).
@@ -191,6 +259,7 @@ __device__ inline double block_exclusive_scan(double v, double* lds_waves, doubl
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     double incl = wave_inclusive_scan(v);
+    __syncthreads();
     if (lane == 63) lds_waves[wave] = incl;
     __syncthreads();
     double base = 0.0, all = 0.0;
@@ -200,7 +269,6 @@ __device__ inline double block_exclusive_scan(double v, double* lds_waves, doubl
         if (w < wave) base += t;
         all += t;
     }
-    __syncthreads();
     *total = all;
     return base + incl - v;
 }
@@ -211,7 +279,28 @@ __device__ inline double block_sum(double v, double* lds_waves) {
     return t;
 }
 
-// Device-scope release/acquire around the "last workgroup to arrive" counters.
+// Workgroup-wide min / max of one int per thread (every thread gets it).
+__device__ inline int block_min_int(int v, int* lds) {
+    __syncthreads();
+    if (threadIdx.x == 0) *lds = INT32_MAX;
+    __syncthreads();
+    atomicMin(lds, v);
+    __syncthreads();
+    return *lds;
+}
+
+__device__ inline int block_max_int(int v, int* lds) {
+    __syncthreads();
+    if (threadIdx.x == 0) *lds = INT32_MIN;
+    __syncthreads();
+    atomicMax(lds, v);
+    __syncthreads();
+    return *lds;
+}
+
+// Device-scope release before the "last workgroup to arrive" counters; the
+// workgroup that sees the final count issues another fence (acquire) before
+// reading what the others wrote.
 __device__ inline unsigned arrive(unsigned* counter) {
     __threadfence();
     return atomicAdd(counter, 1u);

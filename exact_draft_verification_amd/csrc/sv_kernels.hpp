@@ -1,5 +1,12 @@
 // Kernel argument blocks and launch entry points shared by the host API
 // (api.hip) and the kernel translation units (chain.hip, tree.hip).
+//
+// Data moves between workgroups only across kernel boundaries: a kernel writes
+// per-workgroup partial results to the workspace and the next kernel on the
+// stream reads them.  No kernel waits on, or publishes to, another workgroup
+// of the same launch, so no device-scope fence (which on gfx950 writes back and
+// invalidates a whole L2) is ever issued per workgroup, and the workspace
+// needs no initialisation.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -7,9 +14,10 @@
 
 namespace sv {
 
-constexpr int kMaxGamma = 255;       // draft positions per chain block
-constexpr int kMaxTreeNodes = 1024;  // nodes per tree, root included
-constexpr int kMaxChunks = 256;      // final-draw chunks per row (one per thread)
+constexpr int kMaxGamma = 255;        // draft positions per chain block
+constexpr int kMaxTreeNodes = 1024;   // nodes per tree, root included
+constexpr int kMaxChunks = 256;       // final-draw chunks per row (one per thread)
+constexpr int kMaxBlockParts = 2048;  // row partials of one block / request (staged in LDS)
 
 // Row statistics of a temperature softmax (see stat_fold in sv_device.hpp):
 // m = largest logit, R = integer-valued reference, S = sum 2^(z*c - R).
@@ -19,13 +27,11 @@ struct Stat {
     double S;
 };
 
-// Outcome of the ratio tests of one chain block, written by the last
-// statistics workgroup of that block.
+// Outcome of the ratio tests of one chain block.
 struct ChainDecision {
     int32_t k;   // first rejected position, gamma if none, -1 if the block is invalid
     float Rp;    // integer reference R of target row k
-    float Rq;    // integer reference R of draft row k (k < gamma)
-    float dL;    // (R_p + log2 S_p) - (R_q + log2 S_q) at row k, rounded to fp32
+    double dL;   // (R_p + log2 S_p) - (R_q + log2 S_q) at row k (k < gamma), else 0
 };
 
 // Normaliser of the final draw of one block, kept for the final_dist pass.
@@ -47,14 +53,11 @@ struct ChainArgs {
     int nseg, seg_len;      // statistics: segments per row, elements per segment
     int nchunk, chunk_len;  // final draw: chunks per row, elements per chunk
     Stat* part;             // [B][2*gamma+1][nseg]
+    float* zx;              // [B][2*gamma+1]: logit of the draft token in rows i < gamma
+                            // (target) and gamma+1+i (draft); other entries unused
     ChainDecision* dec;     // [B]
     double* chunk_sum;      // [B][nchunk]
     FinalState* fin;        // [B]
-    // Arrival counters, one per block and kernel.  Every call leaves every
-    // workspace byte it used at zero: the last reader of each region clears it.
-    unsigned* cnt_stats;    // [B]
-    unsigned* cnt_final;    // [B]
-    unsigned* cnt_dist;     // [B]
     int32_t* accept_len;
     int32_t* out_tokens;
     float* final_dist;
@@ -74,7 +77,6 @@ struct TreeArgs {
     int B, n, V;
     int nseg, seg_len;
     ArgmaxPart* part;  // [B][n][nseg]
-    unsigned* cnt;     // [B]
     int32_t* accept_len;
     int32_t* accept_node;
     int32_t* out_tokens;
@@ -82,9 +84,10 @@ struct TreeArgs {
 
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_chain_stats(const ChainArgs& a, int dtype, hipStream_t s);
-hipError_t launch_chain_final(const ChainArgs& a, int dtype, hipStream_t s);
+hipError_t launch_chain_chunks(const ChainArgs& a, int dtype, hipStream_t s);
+hipError_t launch_chain_select(const ChainArgs& a, int dtype, hipStream_t s);
 hipError_t launch_chain_dist(const ChainArgs& a, int dtype, hipStream_t s);
-hipError_t launch_tree(const TreeArgs& a, int dtype, hipStream_t s);
-hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_tree_argmax(const TreeArgs& a, int dtype, hipStream_t s);
+hipError_t launch_tree_resolve(const TreeArgs& a, hipStream_t s);
 
 }  // namespace sv

@@ -7,11 +7,14 @@
 // lowest node index among equally deep ones), its path is committed and the
 // target argmax after v* is emitted as the extra token.
 //
-// One launch.  Each workgroup takes one segment of one node row and finds the
-// largest logit and the lowest index holding it (plus a NaN flag); the last
-// workgroup to finish a request (arrival counter) merges the row results,
-// validates the parent array and resolves every node's acceptance and depth
-// by pointer jumping in LDS (ceil(log2 n) rounds), then writes the path.
+// Two launches (data crosses workgroups only at the kernel boundary):
+//  1. tree_argmax: one workgroup per segment of one node row finds the largest
+//     logit and the lowest index holding it (plus a NaN flag) and writes it as
+//     one partial.
+//  2. tree_resolve: one workgroup per request merges its rows' partials
+//     (staged in LDS), validates the parent array and resolves every node's
+//     acceptance and depth by pointer jumping in LDS (ceil(log2 n) rounds),
+//     then writes the path.
 #include "sv_device.hpp"
 
 namespace sv {
@@ -60,11 +63,29 @@ __device__ inline uint32_t nan_mask(F32) { return 0x80000000u; }
 __device__ inline uint32_t nan_mask(BF16) { return 0x80008000u; }
 
 template <class E>
+struct ArgmaxFolder {
+    Best best;
+    uint32_t nanacc;
+    int body_begin;
+    template <int N>
+    __device__ inline void batch(const uint4* v, int v0) {
+        float x[N * E::kPerVec];
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            E::unpack(v[u], x + u * E::kPerVec);
+            nanacc |= nan_bits(v[u], E{});
+        }
+        // element i of the batch is element w of vector v0 + u*kThreads
+        argmax_fold<N * E::kPerVec>(best, x, [&](int i) {
+            const int u = i / E::kPerVec, w = i % E::kPerVec;
+            return body_begin + (v0 + u * kThreads) * E::kPerVec + w;
+        });
+    }
+};
+
+template <class E>
 __device__ inline void range_argmax(const typename E::storage* row, int e0, int e1, Best& best,
                                     uint32_t& nanacc, bool& nan_scalar) {
-    constexpr int U = 4;
-    constexpr int NB = U * E::kPerVec;
-    constexpr int kBatchVec = kThreads * U;
     const int tid = threadIdx.x;
     if (e0 >= e1) return;
     const RangeSplit<E> sp = split_range<E>(row, e0, e1);
@@ -73,52 +94,10 @@ __device__ inline void range_argmax(const typename E::storage* row, int e0, int 
         nan_scalar |= isnan(x);
         argmax_fold<1>(best, &x, [&](int) { return e; });
     }
-    const char* body = reinterpret_cast<const char*>(row + sp.body_begin);
-    const int nfull = sp.nvec / kBatchVec;
-    auto fold_batch = [&](const uint4* V4, int vbase) {
-        float x[NB];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            E::unpack(V4[u], x + u * E::kPerVec);
-            nanacc |= nan_bits(V4[u], E{});
-        }
-        argmax_fold<NB>(best, x, [&](int i) {
-            const int u = i / E::kPerVec, w = i % E::kPerVec;
-            return sp.body_begin + (vbase + u * kThreads + tid) * E::kPerVec + w;
-        });
-    };
-    if (nfull > 0) {
-        uint4 A[U], Bv[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) A[u] = load16(body + static_cast<size_t>(u * kThreads + tid) * 16);
-        for (int t = 0; t < nfull; t += 2) {
-            const bool has1 = t + 1 < nfull;
-            if (has1) {
-                const char* nb = body + static_cast<size_t>(t + 1) * kBatchVec * 16;
-#pragma unroll
-                for (int u = 0; u < U; ++u) Bv[u] = load16(nb + static_cast<size_t>(u * kThreads + tid) * 16);
-            }
-            {
-                uint4 cur[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) cur[u] = A[u];
-                if (t + 2 < nfull) {
-                    const char* nb = body + static_cast<size_t>(t + 2) * kBatchVec * 16;
-#pragma unroll
-                    for (int u = 0; u < U; ++u) A[u] = load16(nb + static_cast<size_t>(u * kThreads + tid) * 16);
-                }
-                fold_batch(cur, t * kBatchVec);
-            }
-            if (has1) fold_batch(Bv, (t + 1) * kBatchVec);
-        }
-    }
-    for (int v = nfull * kBatchVec + tid; v < sp.nvec; v += kThreads) {
-        const uint4 raw = load16(body + static_cast<size_t>(v) * 16);
-        float x[E::kPerVec];
-        E::unpack(raw, x);
-        nanacc |= nan_bits(raw, E{});
-        argmax_fold<E::kPerVec>(best, x, [&](int i) { return sp.body_begin + v * E::kPerVec + i; });
-    }
+    ArgmaxFolder<E> f{best, nanacc, sp.body_begin};
+    stream_vectors<4>(reinterpret_cast<const char*>(row + sp.body_begin), sp.nvec, f);
+    best = f.best;
+    nanacc = f.nanacc;
     for (int e = sp.tail_begin + tid; e < sp.tail_end; e += kThreads) {
         const float x = E::one(row + e);
         nan_scalar |= isnan(x);
@@ -126,8 +105,8 @@ __device__ inline void range_argmax(const typename E::storage* row, int e0, int 
     }
 }
 
-// Path resolution for request b: runs in the last workgroup of the request.
-__device__ void tree_resolve(const TreeArgs& a, int b) {
+// Path resolution for request b (one workgroup).
+__device__ void tree_resolve(const TreeArgs& a, int b, ArgmaxPart* s_part) {
     __shared__ int s_par[kMaxTreeNodes];
     __shared__ int s_anc[kMaxTreeNodes];
     __shared__ int s_dep[kMaxTreeNodes];
@@ -135,25 +114,37 @@ __device__ void tree_resolve(const TreeArgs& a, int b) {
     __shared__ unsigned char s_ok[kMaxTreeNodes];
     __shared__ int s_bad, s_key;
     constexpr int kPer = kMaxTreeNodes / kThreads;
+    constexpr int kStage = kMaxBlockParts / kThreads;
     const int n = a.n, tid = threadIdx.x;
     const int32_t* par = a.parents + static_cast<int64_t>(b) * n;
     const int32_t* tok = a.tokens + static_cast<int64_t>(b) * n;
     int32_t* out = a.out_tokens + static_cast<int64_t>(b) * n;
+    {
+        // stage the request's n*nseg row partials: every load issued before
+        // any LDS store (indices past the end re-read the last partial and
+        // are not stored)
+        const int np = n * a.nseg;
+        const ArgmaxPart* src = a.part + static_cast<int64_t>(b) * np;
+        ArgmaxPart t[kStage];
+#pragma unroll
+        for (int m = 0; m < kStage; ++m) t[m] = src[min(tid + m * kThreads, np - 1)];
+#pragma unroll
+        for (int m = 0; m < kStage; ++m)
+            if (tid + m * kThreads < np) s_part[tid + m * kThreads] = t[m];
+    }
     if (tid == 0) {
         s_bad = 0;
         s_key = -1;
     }
     __syncthreads();
     for (int j = tid; j < n; j += kThreads) {
-        ArgmaxPart* p = a.part + (static_cast<int64_t>(b) * n + j) * a.nseg;
+        const ArgmaxPart* p = s_part + j * a.nseg;
         Best best{p[0].best, p[0].idx};
         uint32_t bad = p[0].bad;
         for (int s = 1; s < a.nseg; ++s) {
             best = best_merge(best, Best{p[s].best, p[s].idx});
             bad |= p[s].bad;
         }
-        // this workgroup is the partials' last reader: leave them cleared
-        for (int s = 0; s < a.nseg; ++s) p[s] = ArgmaxPart{0.0f, 0, 0u, 0u};
         // a valid row has no NaN, no +inf and at least one finite logit
         if (bad || !(best.v > -INFINITY) || best.v == INFINITY) s_bad = 1;
         s_amax[j] = best.idx;
@@ -171,7 +162,6 @@ __device__ void tree_resolve(const TreeArgs& a, int b) {
         if (tid == 0) {
             a.accept_len[b] = -1;
             a.accept_node[b] = -1;
-            a.cnt[b] = 0u;
         }
         return;
     }
@@ -232,16 +222,38 @@ __device__ void tree_resolve(const TreeArgs& a, int b) {
         out[depth] = s_amax[vstar];
         a.accept_len[b] = depth;
         a.accept_node[b] = vstar;
-        a.cnt[b] = 0u;
     }
 }
 
+// Merge of one ArgmaxPart per thread across the workgroup (every thread
+// gets the result; safe to call repeatedly).
+__device__ inline ArgmaxPart block_reduce_argmax(Best best, uint32_t bad, ArgmaxPart* lds_waves) {
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) {
+        Best o{__shfl_xor(best.v, mask, 64), __shfl_xor(best.idx, mask, 64)};
+        best = best_merge(best, o);
+        bad |= __shfl_xor(bad, mask, 64);
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) lds_waves[wave] = ArgmaxPart{best.v, best.idx, bad, 0u};
+    __syncthreads();
+    Best r{lds_waves[0].best, lds_waves[0].idx};
+    uint32_t rb = lds_waves[0].bad;
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+        r = best_merge(r, Best{lds_waves[w].best, lds_waves[w].idx});
+        rb |= lds_waves[w].bad;
+    }
+    return ArgmaxPart{r.v, r.idx, rb, 0u};
+}
+
 template <class E>
-__global__ __launch_bounds__(kThreads) void tree_kernel(TreeArgs a) {
+__global__ __launch_bounds__(kThreads) void tree_argmax_kernel(TreeArgs a) {
+    __shared__ ArgmaxPart s_w[kWaves];
     const int unit = blockIdx.x;
     const int seg = unit % a.nseg;
     const int rr = unit / a.nseg;  // = b * n + j
-    const int b = rr / a.n;
     using S = typename E::storage;
     const S* row = static_cast<const S*>(a.target) + static_cast<int64_t>(rr) * a.V;
     const int e0 = seg * a.seg_len;
@@ -250,48 +262,30 @@ __global__ __launch_bounds__(kThreads) void tree_kernel(TreeArgs a) {
     uint32_t nanacc = 0;
     bool nan_scalar = false;
     range_argmax<E>(row, e0, e1, best, nanacc, nan_scalar);
-    uint32_t bad = ((nanacc & nan_mask(E{})) != 0u || nan_scalar) ? 1u : 0u;
-    // wave then workgroup reduction
-#pragma unroll
-    for (int mask = 32; mask >= 1; mask >>= 1) {
-        Best o{__shfl_xor(best.v, mask, 64), __shfl_xor(best.idx, mask, 64)};
-        best = best_merge(best, o);
-        bad |= __shfl_xor(bad, mask, 64);
-    }
-    __shared__ Best s_b[kWaves];
-    __shared__ uint32_t s_bad[kWaves];
-    __shared__ int s_last;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane == 0) {
-        s_b[wave] = best;
-        s_bad[wave] = bad;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        Best r = s_b[0];
-        uint32_t rb = s_bad[0];
-        for (int w = 1; w < kWaves; ++w) {
-            r = best_merge(r, s_b[w]);
-            rb |= s_bad[w];
-        }
-        a.part[unit] = ArgmaxPart{r.v, r.idx, rb, 0u};
-        const unsigned prev = arrive(&a.cnt[b]);
-        s_last = (prev == static_cast<unsigned>(a.n * a.nseg - 1));
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    tree_resolve(a, b);
+    const uint32_t bad = ((nanacc & nan_mask(E{})) != 0u || nan_scalar) ? 1u : 0u;
+    const ArgmaxPart res = block_reduce_argmax(best, bad, s_w);
+    if (threadIdx.x == 0) a.part[unit] = res;
+}
+
+__global__ __launch_bounds__(kThreads) void tree_resolve_kernel(TreeArgs a) {
+    extern __shared__ ArgmaxPart s_part[];  // [n][nseg]
+    tree_resolve(a, blockIdx.x, s_part);
 }
 
 }  // namespace
 
-hipError_t launch_tree(const TreeArgs& a, int dtype, hipStream_t s) {
+hipError_t launch_tree_argmax(const TreeArgs& a, int dtype, hipStream_t s) {
     const int grid = a.B * a.n * a.nseg;
     if (dtype == 0)
-        hipLaunchKernelGGL(tree_kernel<F32>, dim3(grid), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(tree_argmax_kernel<F32>, dim3(grid), dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL(tree_kernel<BF16>, dim3(grid), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(tree_argmax_kernel<BF16>, dim3(grid), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_tree_resolve(const TreeArgs& a, hipStream_t s) {
+    const size_t lds = sizeof(ArgmaxPart) * static_cast<size_t>(a.n) * a.nseg;
+    hipLaunchKernelGGL(tree_resolve_kernel, dim3(a.B), dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 

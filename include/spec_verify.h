@@ -51,8 +51,8 @@
  *    finite logit m has |m| / T > 2^28 (outside the supported domain); for
  *    trees, a malformed parent array or a node token outside [0, V).
  *  - -inf logits are legal and mean "masked": that token has probability 0.
- *  - The workspace must be zero-filled before its first use (for example with
- *    spec_verify_workspace_zero); every call leaves it zero-filled again.  Two
+ *  - The workspace is scratch owned by the caller: it needs no
+ *    initialisation and its contents after a call are unspecified.  Two
  *    calls in flight at the same time need distinct workspaces.
  *  - A failure of the HIP runtime to launch returns SV_ERR_HIP.
  */
@@ -114,12 +114,13 @@ size_t spec_verify_chain_workspace_bytes(int32_t B, int32_t gamma, int32_t V, in
  *                 When NULL it is neither computed nor written.
  *  workspace      device scratch of at least
  *                 spec_verify_chain_workspace_bytes(B, gamma, V, dtype)
- *                 bytes, 16-byte aligned, zero-filled before first use.
+ *                 bytes, 16-byte aligned (contents irrelevant).
  *  stream         hipStream_t to enqueue on (NULL = null stream).
  *  phase_events   NULLABLE: if not NULL, points to 3 hipEvent_t handles that
- *                 are recorded on `stream` before the row-statistics kernel,
- *                 after it, and after the final-draw kernel (instrumentation
- *                 for timing; the optional final_dist pass comes later).
+ *                 are recorded on `stream` before the row-statistics kernel
+ *                 (the one pass over every logit), after it, and after the
+ *                 final-draw kernels (instrumentation for timing; the
+ *                 optional final_dist pass comes later).
  */
 int32_t spec_verify_chain(const void *target_logits, const void *draft_logits, int32_t dtype,
                           const int32_t *draft_tokens, const float *uniforms, int32_t B,
@@ -149,16 +150,14 @@ size_t spec_verify_tree_greedy_workspace_bytes(int32_t B, int32_t n, int32_t V, 
  *  workspace      as for spec_verify_chain, sized by
  *                 spec_verify_tree_greedy_workspace_bytes.
  *  phase_events   NULLABLE: 2 hipEvent_t recorded before and after the
- *                 verification kernel.
+ *                 row-argmax kernel (the one pass over every logit); the
+ *                 path-resolution kernel follows.
  */
 int32_t spec_verify_tree_greedy(const void *target_logits, int32_t dtype,
                                 const int32_t *parents, const int32_t *tokens, int32_t B,
                                 int32_t n, int32_t V, int32_t *accept_len, int32_t *accept_node,
                                 int32_t *out_tokens, void *workspace, size_t workspace_bytes,
                                 void *stream, void *const *phase_events);
-
-/* Zero-fill a workspace on `stream` (a plain fill kernel, no memset node). */
-int32_t spec_verify_workspace_zero(void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

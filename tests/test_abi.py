@@ -37,7 +37,8 @@ def header_constants():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) >= 6
+    assert {"spec_verify_chain", "spec_verify_tree_greedy", "spec_verify_chain_workspace_bytes",
+            "spec_verify_tree_greedy_workspace_bytes", "spec_verify_status_string"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
@@ -158,14 +159,6 @@ def test_tree_host_errors(lib):
     assert call(t=ct.c_void_p(t.ctypes.data + 1)) == c["SV_ERR_ALIGN"]
     assert call(wsb=8) == c["SV_ERR_WORKSPACE"]
     assert (acc == 0).all() and (out == 0).all()
-
-
-def test_workspace_zero_host_errors(lib):
-    c = header_constants()
-    assert lib.spec_verify_workspace_zero(None, 16, None) == c["SV_ERR_NULL"]
-    buf = np.zeros(64, np.uint8)
-    mis = ct.c_void_p(buf.ctypes.data + ((-buf.ctypes.data) % 16) + 4)
-    assert lib.spec_verify_workspace_zero(mis, 16, None) == c["SV_ERR_WORKSPACE"]
 
 
 def test_binding_rejects_cpu_tensors():

@@ -115,10 +115,12 @@ def test_invalid_requests(kind):
 def test_repeated_calls():
     torch, sv = require_gpu()
     d = synth.tree_inputs(16, 64, 20000, seed=46)
-    ws = torch.zeros(sv.spec_verify_tree_greedy_workspace_bytes(16, 64, 20000, 1),
-                     dtype=torch.uint8, device="cuda")
+    ws = torch.full((sv.spec_verify_tree_greedy_workspace_bytes(16, 64, 20000, 1),), 0xA5,
+                    dtype=torch.uint8, device="cuda")
     first = gpu_tree(dict(d, dtype="bf16"), workspace=ws)
-    for _ in range(3):
+    compare_tree(first, oracle.tree_greedy(d["target"], d["parents"], d["tokens"]), "reuse")
+    for fill in (0x00, 0xFF):
+        ws.fill_(fill)
         again = gpu_tree(dict(d, dtype="bf16"), workspace=ws)
         for k in first:
             assert np.array_equal(first[k], again[k])
