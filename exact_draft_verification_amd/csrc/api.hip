@@ -40,8 +40,8 @@ void plan_segments(int64_t rows_total, int V, int epv, int64_t target, int min_v
 }
 
 struct ChainPlan {
-    int rows, nseg, seg_len, nchunk, chunk_len;
-    size_t off_part, off_zx, off_dec, off_chunk, off_fin, bytes;
+    int rows, nseg, seg_len, nchunk, nquart;
+    size_t off_part, off_zx, off_dec, off_qsum, off_fin, bytes;
 };
 
 // Carves `n` objects of `size` bytes out of the workspace at *off (256-byte
@@ -66,19 +66,18 @@ int32_t chain_plan(int32_t B, int32_t gamma, int32_t V, int32_t dtype, ChainPlan
     plan_segments(rows_total, V, epv, kTargetUnits, 4,
                   static_cast<int>(kMaxBlockParts / rows), &p->nseg, &p->seg_len);
     if (rows_total * p->nseg > INT32_MAX) return SV_ERR_SHAPE;
-    // final draw: chunks of whole tiles (one 16-byte vector per thread), at
-    // most kMaxChunks per row
+    // final draw: tiles of one 16-byte vector per thread, kChunkTiles tiles
+    // per chunk workgroup, sums kept per quarter tile (64 vectors)
     const int64_t tile = static_cast<int64_t>(kThreadsHost) * epv;
-    const int64_t tiles = ceil_div(V, tile);
-    p->chunk_len = static_cast<int>(tile * ceil_div(tiles, kMaxChunks));
-    p->nchunk = static_cast<int>(ceil_div(V, p->chunk_len));
+    p->nchunk = static_cast<int>(ceil_div(ceil_div(V, tile), kChunkTiles));
+    p->nquart = static_cast<int>(ceil_div(V, 64 * static_cast<int64_t>(epv)));
     if (static_cast<int64_t>(B) * p->nchunk > INT32_MAX) return SV_ERR_SHAPE;
     const size_t nb = static_cast<size_t>(B), nr = static_cast<size_t>(rows_total);
     size_t off = 0;
     p->off_part = carve(&off, sizeof(Stat), nr * p->nseg);
     p->off_zx = carve(&off, sizeof(float), nr);
     p->off_dec = carve(&off, sizeof(ChainDecision), nb);
-    p->off_chunk = carve(&off, sizeof(double), nb * p->nchunk);
+    p->off_qsum = carve(&off, sizeof(double), nb * p->nquart);
     p->off_fin = carve(&off, sizeof(FinalState), nb);
     p->bytes = off;
     return SV_OK;
@@ -186,12 +185,12 @@ extern "C" int32_t spec_verify_chain(const void* target_logits, const void* draf
     a.nseg = p.nseg;
     a.seg_len = p.seg_len;
     a.nchunk = p.nchunk;
-    a.chunk_len = p.chunk_len;
+    a.nquart = p.nquart;
     char* ws = static_cast<char*>(workspace);
     a.part = reinterpret_cast<Stat*>(ws + p.off_part);
     a.zx = reinterpret_cast<float*>(ws + p.off_zx);
     a.dec = reinterpret_cast<ChainDecision*>(ws + p.off_dec);
-    a.chunk_sum = reinterpret_cast<double*>(ws + p.off_chunk);
+    a.qsum = reinterpret_cast<double*>(ws + p.off_qsum);
     a.fin = reinterpret_cast<FinalState*>(ws + p.off_fin);
     a.accept_len = accept_len;
     a.out_tokens = out_tokens;

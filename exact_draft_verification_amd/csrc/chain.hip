@@ -41,7 +41,6 @@ namespace sv {
 namespace {
 
 constexpr double kDomain = 268435456.0;  // |m| / T limit (2^28)
-constexpr float kLn2 = 0.693147180559945309f;
 constexpr int kStreamU = 4;              // 16-byte vectors per thread per batch
 
 template <class E>
@@ -124,10 +123,12 @@ __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
     }
 }
 
-// Ratio tests of block b (every workgroup of the block's final draw takes
-// them for itself): merges the block's row partials, staged in LDS, then for
-// each draft position i evaluates r_i = min(1, p_i(x_i)/q_i(x_i)) in the
-// log2 domain in fp64 and keeps the first i with u_i >= r_i.
+// Ratio tests of block b, taken by every workgroup of the block's final-draw
+// kernel for itself (cheaper than a launch of its own): every input (the
+// block's row partials, the draft tokens, their logits and the uniforms) is
+// requested in one round of loads; the partials are merged per row in LDS;
+// then for each draft position i, r_i = min(1, p_i(x_i)/q_i(x_i)) is
+// evaluated in the log2 domain in fp64 and the first i with u_i >= r_i kept.
 template <class E>
 __device__ ChainDecision chain_decide(const ChainArgs& a, int b, Stat* s_part) {
     __shared__ double s_L[2 * kMaxGamma + 1];
@@ -136,16 +137,28 @@ __device__ ChainDecision chain_decide(const ChainArgs& a, int b, Stat* s_part) {
     constexpr int kPer = kMaxBlockParts / kThreads;
     const int g = a.gamma, rows = 2 * g + 1, tid = threadIdx.x;
     const int np = rows * a.nseg;
-    const Stat* src = a.part + static_cast<int64_t>(b) * np;
+    // per-position inputs (gamma <= 255 < kThreads: one position per thread)
+    int x = 0;
+    float zp = 0.0f, zq = 0.0f, u = 0.0f;
+    if (tid < g) {
+        x = a.tokens[static_cast<int64_t>(b) * g + tid];
+        zp = a.zx[static_cast<int64_t>(b) * rows + tid];
+        zq = a.zx[static_cast<int64_t>(b) * rows + g + 1 + tid];
+        u = a.uniforms[static_cast<int64_t>(b) * (g + 1) + tid];
+    }
     {
-        // every load issued before any LDS store (indices past the end
-        // re-read the last partial and are not stored)
-        Stat t[kPer];
-#pragma unroll
-        for (int m = 0; m < kPer; ++m) t[m] = src[min(tid + m * kThreads, np - 1)];
+        // every load issued before any LDS store; a Stat is one 16-byte
+        // vector (indices past the end re-read the last partial, unstored)
+        static_assert(sizeof(Stat) == 16, "Stat is staged as one 16-byte vector");
+        const uint4* src = reinterpret_cast<const uint4*>(a.part + static_cast<int64_t>(b) * np);
+        uint4* dst = reinterpret_cast<uint4*>(s_part);
+        uint4 t[kPer];
 #pragma unroll
         for (int m = 0; m < kPer; ++m)
-            if (tid + m * kThreads < np) s_part[tid + m * kThreads] = t[m];
+            t[m] = m * kThreads < np ? src[min(tid + m * kThreads, np - 1)] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int m = 0; m < kPer; ++m)
+            if (tid + m * kThreads < np) dst[tid + m * kThreads] = t[m];
     }
     if (tid == 0) {
         s_bad = 0;
@@ -162,28 +175,23 @@ __device__ ChainDecision chain_decide(const ChainArgs& a, int b, Stat* s_part) {
         s_R[r] = t.R;
     }
     __syncthreads();
-    const float* zx = a.zx + static_cast<int64_t>(b) * rows;
-    for (int i = tid; i < g; i += kThreads) {
-        const int x = a.tokens[static_cast<int64_t>(b) * g + i];
+    if (tid < g) {
         if (x < 0 || x >= a.V) {
             atomicOr(&s_bad, 1);
-            continue;
-        }
-        const float zp = zx[i];
-        const float zq = zx[g + 1 + i];
-        double r;
-        if (zp == -INFINITY) {
-            r = 0.0;
-        } else if (zq == -INFINITY) {
-            r = 1.0;
         } else {
-            // log2 p(x) - log2 q(x), both rows' log2-sum-exp in fp64
-            const double d = (static_cast<double>(zp) * a.c_d - s_L[i]) -
-                             (static_cast<double>(zq) * a.c_d - s_L[g + 1 + i]);
-            r = d >= 0.0 ? 1.0 : exp2(d);
+            double r;
+            if (zp == -INFINITY) {
+                r = 0.0;
+            } else if (zq == -INFINITY) {
+                r = 1.0;
+            } else {
+                // log2 p(x) - log2 q(x), both rows' log2-sum-exp in fp64
+                const double d = (static_cast<double>(zp) * a.c_d - s_L[tid]) -
+                                 (static_cast<double>(zq) * a.c_d - s_L[g + 1 + tid]);
+                r = d >= 0.0 ? 1.0 : exp2(d);
+            }
+            if (!(static_cast<double>(u) < r)) atomicMin(&s_k, tid);
         }
-        const double u = static_cast<double>(a.uniforms[static_cast<int64_t>(b) * (g + 1) + i]);
-        if (!(u < r)) atomicMin(&s_k, i);
     }
     __syncthreads();
     ChainDecision d;
@@ -202,82 +210,151 @@ __device__ ChainDecision chain_decide(const ChainArgs& a, int b, Stat* s_part) {
 
 // ---------------------------------------------------------------------------
 // Final draw.
+//
+// The final row (residual row k, or the bonus row) is cut into tiles of
+// kThreads 16-byte vectors; thread t of a workgroup owns vector t of a tile,
+// i.e. the kPerVec consecutive tokens starting at tile + t*kPerVec, and wave w
+// owns the "quarter" of 64 vectors [64w, 64w+64).  Each lane sums its kPerVec
+// weights in token order in fp32; lanes and quarters are summed in fp64.  The
+// chunk kernel writes one weight sum per quarter; the select kernel (one wave
+// per block) scans the quarter sums for the quarter holding u * W, then scans
+// that quarter's 64 lanes in token order.
 
 struct DrawRow {
     float Rp, c_hi, c_lo;
+    float dL_hi, dL_lo;  // dL as a float pair
     double c_d, dL;
     bool resid;  // residual of p_k and q_k (else p_k itself, unnormalised)
 };
 
+// D(v) = log2 p_k(v) - log2 q_k(v) = (z_p - z_q) c - dL.  bf16 logits: the
+// difference of two bf16 values is exact in fp32, and with c and dL carried
+// as float pairs the two fused multiply-adds round once each, at the scale of
+// D itself, so a constant offset between the rows cancels exactly.  fp32
+// logits: the difference is taken in fp64.
+__device__ inline float log_ratio(float zp, float zq, const DrawRow& r, BF16) {
+    const float dz = zp - zq;
+    return fmaf(dz, r.c_hi, -r.dL_hi) + fmaf(dz, r.c_lo, -r.dL_lo);
+}
+__device__ inline float log_ratio(float zp, float zq, const DrawRow& r, F32) {
+    return static_cast<float>(fma(static_cast<double>(zp) - static_cast<double>(zq), r.c_d, -r.dL));
+}
+
+// 1 - 2^-D for D > 0, to about 1e-7 relative.  Below 1: x * g(x) with
+// x = D ln 2 and g(x) = (1 - e^-x)/x approximated on [0, ln 2] by a degree-5
+// polynomial (coefficients fitted here to minimise the relative error, which
+// stays under 1e-8 before fp32 rounding).  From 1 up: 1 - 2^-D with the
+// hardware exp2, where 2^-D <= 1/2 keeps the subtraction well conditioned.
+__device__ inline float one_minus_exp2_neg(float D) {
+    const float x = D * 0.693147180559945309f;
+    float g = -1.033136854e-03f;
+    g = fmaf(g, x, 8.067236282e-03f);
+    g = fmaf(g, x, -4.157199338e-02f);
+    g = fmaf(g, x, 1.666511893e-01f);
+    g = fmaf(g, x, -4.999990761e-01f);
+    g = fmaf(g, x, 1.0f);
+    const float small = x * g;
+    const float large = 1.0f - __builtin_amdgcn_exp2f(-D);
+    return D < 1.0f ? small : large;
+}
+
 // Unnormalised draw weight of token v.  With P(v) = 2^(z_p c - R_p)
 // (proportional to p_k(v)): residual  w = P(v) * (1 - 2^-D(v)) for D > 0,
-// D(v) = log2 p_k(v) - log2 q_k(v) = (z_p - z_q) c - dL; bonus/fallback w = P(v).
+// else 0; bonus row and fallback: w = P(v).  Masked tokens need no test: a
+// -inf target logit gives P = 0 and D = -inf or NaN (w = 0); a -inf draft
+// logit gives D = +inf and w = P(v), as q(v) = 0 requires.
+template <class E>
 __device__ inline float draw_weight(float zp, float zq, const DrawRow& r) {
-    if (zp == -INFINITY) return 0.0f;
     float t = fmaf(zp, r.c_hi, -r.Rp);
     t = fmaf(zp, r.c_lo, t);
     const float P = __builtin_amdgcn_exp2f(t);
-    if (!r.resid || zq == -INFINITY) return P;
-    const double D = fma(static_cast<double>(zp) - static_cast<double>(zq), r.c_d, -r.dL);
-    if (!(D > 0.0)) return 0.0f;
-    return P * (-expm1f(static_cast<float>(-D) * kLn2));
+    if (!r.resid) return P;
+    const float D = log_ratio(zp, zq, r, E{});
+    return D > 0.0f ? P * one_minus_exp2_neg(D) : 0.0f;
 }
 
 template <class E>
 struct FinalRows {
     const typename E::storage* p;
-    const typename E::storage* q;  // nullptr unless resid
+    const typename E::storage* q;  // nullptr unless k < gamma
+    bool vec_ok;                   // both rows 16-byte aligned
 };
 
-// Sum of draw weights over elements [e0, e1) by the whole workgroup (per
-// thread partial, fp64).
 template <class E>
-__device__ inline double range_weight_sum(const FinalRows<E>& rows, int e0, int e1,
-                                          const DrawRow& r) {
-    const int tid = threadIdx.x;
-    double acc = 0.0;
-    if (e0 >= e1) return acc;
-    const auto* p = rows.p;
-    const auto* q = rows.q;
-    const bool same_align =
-        !r.resid || ((reinterpret_cast<uintptr_t>(q) - reinterpret_cast<uintptr_t>(p)) & 15u) == 0;
-    if (!same_align) {
-        for (int e = e0 + tid; e < e1; e += kThreads)
-            acc += static_cast<double>(draw_weight(E::one(p + e), E::one(q + e), r));
-        return acc;
-    }
-    const RangeSplit<E> sp = split_range<E>(p, e0, e1);
-    for (int e = sp.head_begin + tid; e < sp.head_end; e += kThreads)
-        acc += static_cast<double>(draw_weight(E::one(p + e), r.resid ? E::one(q + e) : 0.0f, r));
-    const char* pb = reinterpret_cast<const char*>(p + sp.body_begin);
-    const char* qb = r.resid ? reinterpret_cast<const char*>(q + sp.body_begin) : nullptr;
-    for (int v = tid; v < sp.nvec; v += kThreads) {
-        float xp[E::kPerVec], xq[E::kPerVec];
-        E::unpack(load16_stream(pb + static_cast<size_t>(v) * 16), xp);
-        if (r.resid) {
-            E::unpack(load16_stream(qb + static_cast<size_t>(v) * 16), xq);
-        } else {
+__device__ inline FinalRows<E> final_rows(const ChainArgs& a, int b, int k) {
+    using S = typename E::storage;
+    FinalRows<E> f;
+    f.p = static_cast<const S*>(a.target) + (static_cast<int64_t>(b) * (a.gamma + 1) + k) * a.V;
+    f.q = k < a.gamma
+              ? static_cast<const S*>(a.draft) + (static_cast<int64_t>(b) * a.gamma + k) * a.V
+              : nullptr;
+    f.vec_ok = (reinterpret_cast<uintptr_t>(f.p) & 15u) == 0 &&
+               (f.q == nullptr || (reinterpret_cast<uintptr_t>(f.q) & 15u) == 0);
+    return f;
+}
+
+__device__ inline DrawRow draw_row(const ChainArgs& a, const ChainDecision& d, bool resid) {
+    const float dL_hi = static_cast<float>(d.dL);
+    const float dL_lo = static_cast<float>(d.dL - static_cast<double>(dL_hi));
+    return DrawRow{d.Rp, a.c_hi, a.c_lo, dL_hi, dL_lo, a.c_d, d.dL, resid};
+}
+
+// The kPerVec tokens [e, e + kPerVec) of the final row(s) as floats: one
+// 16-byte load when the whole vector is in range and aligned, else one load
+// per in-range token; tokens at or past V read as -inf (weight 0).
+template <class E>
+__device__ inline void load_tokens(const FinalRows<E>& rows, bool resid, int e, int V, float* zp,
+                                   float* zq) {
+    if (rows.vec_ok && e + E::kPerVec <= V) {
+        E::unpack(load16_stream(rows.p + e), zp);
+        if (resid) E::unpack(load16_stream(rows.q + e), zq);
+    } else {
 #pragma unroll
-            for (int i = 0; i < E::kPerVec; ++i) xq[i] = 0.0f;
+        for (int i = 0; i < E::kPerVec; ++i) {
+            zp[i] = e + i < V ? E::one(rows.p + e + i) : -INFINITY;
+            if (resid) zq[i] = e + i < V ? E::one(rows.q + e + i) : -INFINITY;
         }
-#pragma unroll
-        for (int i = 0; i < E::kPerVec; ++i) acc += static_cast<double>(draw_weight(xp[i], xq[i], r));
     }
-    for (int e = sp.tail_begin + tid; e < sp.tail_end; e += kThreads)
-        acc += static_cast<double>(draw_weight(E::one(p + e), r.resid ? E::one(q + e) : 0.0f, r));
-    return acc;
+    if (!resid) {
+#pragma unroll
+        for (int i = 0; i < E::kPerVec; ++i) zq[i] = 0.0f;
+    }
 }
 
+// A lane's weights and their sum, accumulated in token order in fp32 (the
+// select kernel repeats exactly this order, so its running prefix ends on
+// the very value the quarter sums were built from).
 template <class E>
-__device__ inline float weight_at(const FinalRows<E>& rows, int e, const DrawRow& r) {
-    return draw_weight(E::one(rows.p + e), r.resid ? E::one(rows.q + e) : 0.0f, r);
+__device__ inline float lane_weights(const float* zp, const float* zq, const DrawRow& r, float* w) {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < E::kPerVec; ++i) {
+        w[i] = draw_weight<E>(zp[i], zq[i], r);
+        s += w[i];
+    }
+    return s;
 }
 
+__device__ inline double wave_sum(double v) {
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) v += wave_xor(v, mask);
+    return v;
+}
+
+// Exclusive prefix sum over the lanes of a wave, plus the wave total.
+__device__ inline double wave_exclusive_scan(double v, double* total) {
+    const double incl = wave_inclusive_scan(v);
+    *total = __shfl(incl, 63, 64);
+    return incl - v;
+}
+
+// Outputs of block b: accept length k, then x_0 .. x_{k-1}, the drawn token
+// and -1 padding (all -1 for an invalid block).  Any block size.
 template <class E>
 __device__ void write_outputs(const ChainArgs& a, int b, int k, int token) {
     const int g = a.gamma;
     int32_t* out = a.out_tokens + static_cast<int64_t>(b) * (g + 1);
-    for (int i = threadIdx.x; i <= g; i += kThreads) {
+    for (int i = threadIdx.x; i <= g; i += blockDim.x) {
         int32_t v = -1;
         if (k >= 0) {
             if (i < k)
@@ -288,112 +365,6 @@ __device__ void write_outputs(const ChainArgs& a, int b, int k, int token) {
         out[i] = v;
     }
     if (threadIdx.x == 0) a.accept_len[b] = k;
-}
-
-// Token selection for block b (one workgroup), from the chunk sums of the
-// chunk kernel.
-//
-// The draw is the smallest token v whose inclusive prefix sum of weights
-// exceeds u * W (W the total).  The chunk holding that crossing is found from
-// the chunk sums (one per thread, one workgroup-wide scan); inside the chunk,
-// tile by tile, thread t holds the kPerVec consecutive tokens starting at
-// tile + t*kPerVec, so one more workgroup scan of the per-thread sums puts
-// every token's prefix in token order.  If rounding leaves no crossing, the
-// last token of positive weight is taken.
-template <class E>
-__device__ void chain_select(const ChainArgs& a, int b, const ChainDecision& d,
-                             const FinalRows<E>& rows, DrawRow r) {
-    __shared__ double s_waves[kWaves];
-    __shared__ double s_base;
-    __shared__ int s_int;
-    constexpr int kTile = kThreads * E::kPerVec;
-    const int tid = threadIdx.x;
-    const int g = a.gamma;
-    double wc = 0.0;
-    if (tid < a.nchunk) wc = a.chunk_sum[static_cast<int64_t>(b) * a.nchunk + tid];
-    double total;
-    double excl = block_exclusive_scan(wc, s_waves, &total);
-    int fallback = 0;
-    if (!(total > 0.0)) {
-        // An empty residual (possible only through rounding after a
-        // rejection): sample from p_k instead.
-        fallback = 1;
-        r.resid = false;
-        double mine = 0.0;
-        for (int c = 0; c < a.nchunk; ++c) {
-            const int e0 = c * a.chunk_len, e1 = min(a.V, e0 + a.chunk_len);
-            const double s = block_sum(range_weight_sum<E>(rows, e0, e1, r), s_waves);
-            if (tid == c) mine = s;
-        }
-        wc = mine;
-        excl = block_exclusive_scan(wc, s_waves, &total);
-    }
-    const double target =
-        static_cast<double>(a.uniforms[static_cast<int64_t>(b) * (g + 1) + g]) * total;
-    // first chunk whose inclusive prefix exceeds the target
-    const int cand = (tid < a.nchunk && wc > 0.0 && excl + wc > target) ? tid : INT32_MAX;
-    int cstar = block_min_int(cand, &s_int);
-    bool last_positive = false;
-    if (cstar == INT32_MAX) {
-        // no crossing (rounding): the last token of positive weight
-        cstar = block_max_int((tid < a.nchunk && wc > 0.0) ? tid : -1, &s_int);
-        last_positive = true;
-        if (cstar < 0) cstar = 0;  // no positive weight at all: keep every read in range
-    }
-    if (tid == cstar) s_base = excl;
-    __syncthreads();
-    double base = s_base;
-    const int e0 = cstar * a.chunk_len, e1 = min(a.V, e0 + a.chunk_len);
-    int token = -1, lastpos = -1;
-    for (int t0 = e0; t0 < e1; t0 += kTile) {
-        float w[E::kPerVec];
-        double mine = 0.0;
-        const int my0 = t0 + tid * E::kPerVec;
-#pragma unroll
-        for (int i = 0; i < E::kPerVec; ++i) {
-            const int e = my0 + i;
-            w[i] = e < e1 ? weight_at<E>(rows, e, r) : 0.0f;
-            mine += static_cast<double>(w[i]);
-        }
-        double tile_total;
-        const double my_excl = block_exclusive_scan(mine, s_waves, &tile_total);
-        int found = INT32_MAX, lp = -1;
-        double run = base + my_excl;
-#pragma unroll
-        for (int i = 0; i < E::kPerVec; ++i) {
-            run += static_cast<double>(w[i]);
-            if (w[i] > 0.0f) {
-                lp = my0 + i;
-                if (!last_positive && found == INT32_MAX && run > target) found = my0 + i;
-            }
-        }
-        found = block_min_int(found, &s_int);
-        lp = block_max_int(lp, &s_int);
-        if (lp >= 0) lastpos = lp;
-        if (found != INT32_MAX) {
-            token = found;
-            break;
-        }
-        base += tile_total;
-    }
-    if (token < 0) token = lastpos >= 0 ? lastpos : e0;
-    write_outputs<E>(a, b, d.k, token);
-    if (tid == 0 && a.final_dist) a.fin[b] = FinalState{total, fallback, 0};
-}
-
-template <class E>
-__device__ inline FinalRows<E> final_rows(const ChainArgs& a, int b, int k) {
-    using S = typename E::storage;
-    FinalRows<E> f;
-    f.p = static_cast<const S*>(a.target) + (static_cast<int64_t>(b) * (a.gamma + 1) + k) * a.V;
-    f.q = k < a.gamma
-              ? static_cast<const S*>(a.draft) + (static_cast<int64_t>(b) * a.gamma + k) * a.V
-              : nullptr;
-    return f;
-}
-
-__device__ inline DrawRow draw_row(const ChainArgs& a, const ChainDecision& d, bool resid) {
-    return DrawRow{d.Rp, a.c_hi, a.c_lo, a.c_d, d.dL, resid};
 }
 
 // The decision of block b as written by the chunk kernel.  k is clamped to
@@ -408,50 +379,172 @@ __device__ inline ChainDecision load_decision(const ChainArgs& a, int b) {
 template <class E>
 __global__ __launch_bounds__(kThreads) void chain_chunks_kernel(ChainArgs a) {
     extern __shared__ Stat s_part[];  // [2*gamma+1][nseg]
-    __shared__ double s_waves[kWaves];
+    constexpr int kTile = kThreads * E::kPerVec;
     const int b = blockIdx.x / a.nchunk;
     const int c = blockIdx.x % a.nchunk;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const ChainDecision d = chain_decide<E>(a, b, s_part);
-    const bool valid = d.k >= 0;
-    const FinalRows<E> rows = final_rows<E>(a, b, valid ? d.k : 0);
-    const DrawRow r = draw_row(a, d, valid && d.k < a.gamma);
-    const int e0 = c * a.chunk_len, e1 = min(a.V, e0 + a.chunk_len);
-    const double s = valid ? block_sum(range_weight_sum<E>(rows, e0, e1, r), s_waves) : 0.0;
-    if (threadIdx.x == 0) {
-        a.chunk_sum[static_cast<int64_t>(b) * a.nchunk + c] = s;
-        if (c == 0) a.dec[b] = d;
+    if (c == 0 && tid == 0) a.dec[b] = d;
+    if (d.k < 0) return;  // invalid block: the select kernel writes -1s
+    const FinalRows<E> rows = final_rows<E>(a, b, d.k);
+    const DrawRow r = draw_row(a, d, d.k < a.gamma);
+    const int ntile = (a.V + kTile - 1) / kTile;
+    // every load of this workgroup's tiles before any weight is computed; a
+    // tile past the row's end reads as -inf (weight 0) without a load
+    float zp[kChunkTiles][E::kPerVec], zq[kChunkTiles][E::kPerVec];
+#pragma unroll
+    for (int m = 0; m < kChunkTiles; ++m) {
+        const int j = c * kChunkTiles + m;
+        load_tokens<E>(rows, r.resid, j * kTile + tid * E::kPerVec, a.V, zp[m], zq[m]);
+    }
+    double* qs = a.qsum + static_cast<int64_t>(b) * a.nquart;
+#pragma unroll
+    for (int m = 0; m < kChunkTiles; ++m) {
+        const int j = c * kChunkTiles + m;
+        float w[E::kPerVec];
+        const double sw = wave_sum(static_cast<double>(lane_weights<E>(zp[m], zq[m], r, w)));
+        const int qi = j * kWaves + wave;
+        if (lane == 0 && j < ntile && qi < a.nquart) qs[qi] = sw;
     }
 }
 
+// Token selection for block b, by one wave.
+//
+// The draw is the smallest token v whose inclusive prefix sum of weights
+// exceeds u * W (W the total).  Lane l takes a contiguous run of quarters;
+// one wave scan of the runs' sums and a walk inside the crossing lane's run
+// give the quarter; lane l of that quarter holds the kPerVec consecutive
+// tokens starting at quarter + l*kPerVec, so a second wave scan gives the
+// token.  If rounding leaves no crossing, the last token of positive weight
+// is taken.  A residual that sums to zero (possible only through rounding
+// after a rejection) falls back to p_k: the wave then recomputes the quarter
+// sums from p_k itself (slow, but never on a normal path).
 template <class E>
-__global__ __launch_bounds__(kThreads) void chain_select_kernel(ChainArgs a) {
-    const int b = blockIdx.x;
+__global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
+    constexpr int kQuart = 64 * E::kPerVec;
+    const int b = blockIdx.x, lane = threadIdx.x;
+    const int g = a.gamma;
     const ChainDecision d = load_decision(a, b);
+    const double u = static_cast<double>(a.uniforms[static_cast<int64_t>(b) * (g + 1) + g]);
     if (d.k < 0) {
         write_outputs<E>(a, b, -1, -1);
         return;
     }
+    double* qs = a.qsum + static_cast<int64_t>(b) * a.nquart;
+    const int per = (a.nquart + 63) / 64;
+    const int q0 = min(a.nquart, lane * per), q1 = min(a.nquart, q0 + per);
     const FinalRows<E> rows = final_rows<E>(a, b, d.k);
-    chain_select<E>(a, b, d, rows, draw_row(a, d, d.k < a.gamma));
+    double mine = 0.0;
+    for (int q = q0; q < q1; ++q) mine += qs[q];
+    int fallback = 0;
+    DrawRow r = draw_row(a, d, d.k < g);
+    if (r.resid && !(wave_sum(mine) > 0.0)) {
+        fallback = 1;
+        r.resid = false;
+        // quarter sums of p_k, each by one lane, in the chunk kernel's order
+        mine = 0.0;
+        for (int q = q0; q < q1; ++q) {
+            double sq = 0.0;
+            for (int l = 0; l < 64; ++l) {
+                float zp[E::kPerVec], zq[E::kPerVec], w[E::kPerVec];
+                load_tokens<E>(rows, false, q * kQuart + l * E::kPerVec, a.V, zp, zq);
+                sq += static_cast<double>(lane_weights<E>(zp, zq, r, w));
+            }
+            qs[q] = sq;
+            mine += sq;
+        }
+    }
+    double W;
+    const double excl = wave_exclusive_scan(mine, &W);
+    const double target = u * W;
+    // the lane whose run holds the crossing, then the quarter inside it
+    const unsigned long long hit = __ballot(mine > 0.0 && excl + mine > target);
+    bool last_positive = false;
+    int src;
+    if (hit) {
+        src = __ffsll(static_cast<long long>(hit)) - 1;
+    } else {
+        // no crossing (rounding): the last quarter of positive weight
+        const unsigned long long pos = __ballot(mine > 0.0);
+        src = pos ? 63 - __clzll(static_cast<long long>(pos)) : 0;
+        last_positive = true;
+    }
+    int qfound = q0;
+    double b0 = excl;
+    if (lane == src) {
+        // walk this lane's run
+        double run = excl, run_last = excl;
+        int lastq = -1;
+        qfound = -1;
+        for (int q = q0; q < q1; ++q) {
+            const double sq = qs[q];
+            if (sq > 0.0) {
+                lastq = q;
+                run_last = run;
+                if (!last_positive && run + sq > target) {
+                    qfound = q;
+                    b0 = run;
+                    break;
+                }
+            }
+            run += sq;
+        }
+        if (qfound < 0) {
+            // rounding: the run's last positive quarter
+            qfound = lastq >= 0 ? lastq : q0;
+            b0 = run_last;
+        }
+    }
+    const int qstar = __shfl(qfound, src, 64);
+    const double base = __shfl(b0, src, 64);
+    // tokens of the chosen quarter, kPerVec per lane in token order
+    const int e0 = qstar * kQuart + lane * E::kPerVec;
+    float zp[E::kPerVec], zq[E::kPerVec], w[E::kPerVec];
+    load_tokens<E>(rows, r.resid, e0, a.V, zp, zq);
+    const float lsum = lane_weights<E>(zp, zq, r, w);
+    double qtot;
+    const double lbase = base + wave_exclusive_scan(static_cast<double>(lsum), &qtot);
+    int found = INT32_MAX, lastpos = -1;
+    float pre = 0.0f;
+#pragma unroll
+    for (int i = 0; i < E::kPerVec; ++i) {
+        pre += w[i];
+        if (w[i] > 0.0f) {
+            lastpos = e0 + i;
+            if (!last_positive && found == INT32_MAX && lbase + static_cast<double>(pre) > target)
+                found = e0 + i;
+        }
+    }
+    const unsigned long long fl = __ballot(found != INT32_MAX);
+    int token;
+    if (fl) {
+        token = __shfl(found, __ffsll(static_cast<long long>(fl)) - 1, 64);
+    } else {
+        const unsigned long long pl = __ballot(lastpos >= 0);
+        token = pl ? __shfl(lastpos, 63 - __clzll(static_cast<long long>(pl)), 64)
+                   : min(qstar * kQuart, a.V - 1);
+    }
+    write_outputs<E>(a, b, d.k, token);
+    if (lane == 0 && a.final_dist) a.fin[b] = FinalState{W, fallback, 0};
 }
 
 template <class E>
 __global__ __launch_bounds__(kThreads) void chain_dist_kernel(ChainArgs a) {
-    const int b = blockIdx.x / a.nchunk;
-    const int c = blockIdx.x % a.nchunk;
+    const int b = blockIdx.x;
     const ChainDecision d = load_decision(a, b);
-    const int e0 = c * a.chunk_len, e1 = min(a.V, e0 + a.chunk_len);
     float* out = a.final_dist + static_cast<int64_t>(b) * a.V;
     if (d.k < 0) {
-        for (int e = e0 + threadIdx.x; e < e1; e += kThreads) out[e] = 0.0f;
+        for (int e = threadIdx.x; e < a.V; e += kThreads) out[e] = 0.0f;
         return;
     }
     const FinalState f = a.fin[b];
     const FinalRows<E> rows = final_rows<E>(a, b, d.k);
     const DrawRow r = draw_row(a, d, d.k < a.gamma && !f.fallback);
     const double inv = 1.0 / f.W;
-    for (int e = e0 + threadIdx.x; e < e1; e += kThreads)
-        out[e] = static_cast<float>(static_cast<double>(weight_at<E>(rows, e, r)) * inv);
+    for (int e = threadIdx.x; e < a.V; e += kThreads) {
+        const float zq = r.resid ? E::one(rows.q + e) : 0.0f;
+        out[e] = static_cast<float>(static_cast<double>(draw_weight<E>(E::one(rows.p + e), zq, r)) * inv);
+    }
 }
 
 }  // namespace
@@ -477,18 +570,17 @@ hipError_t launch_chain_chunks(const ChainArgs& a, int dtype, hipStream_t s) {
 
 hipError_t launch_chain_select(const ChainArgs& a, int dtype, hipStream_t s) {
     if (dtype == 0)
-        hipLaunchKernelGGL(chain_select_kernel<F32>, dim3(a.B), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(chain_select_kernel<F32>, dim3(a.B), dim3(64), 0, s, a);
     else
-        hipLaunchKernelGGL(chain_select_kernel<BF16>, dim3(a.B), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(chain_select_kernel<BF16>, dim3(a.B), dim3(64), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_chain_dist(const ChainArgs& a, int dtype, hipStream_t s) {
-    const int grid = a.B * a.nchunk;
     if (dtype == 0)
-        hipLaunchKernelGGL(chain_dist_kernel<F32>, dim3(grid), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(chain_dist_kernel<F32>, dim3(a.B), dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL(chain_dist_kernel<BF16>, dim3(grid), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(chain_dist_kernel<BF16>, dim3(a.B), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

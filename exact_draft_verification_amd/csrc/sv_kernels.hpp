@@ -16,8 +16,9 @@ namespace sv {
 
 constexpr int kMaxGamma = 255;        // draft positions per chain block
 constexpr int kMaxTreeNodes = 1024;   // nodes per tree, root included
-constexpr int kMaxChunks = 256;       // final-draw chunks per row (one per thread)
 constexpr int kMaxBlockParts = 2048;  // row partials of one block / request (staged in LDS)
+constexpr int kChunkTiles = 4;        // final-draw tiles (one 16-byte vector per thread) per
+                                      // chunk workgroup
 
 // Row statistics of a temperature softmax (see stat_fold in sv_device.hpp):
 // m = largest logit, R = integer-valued reference, S = sum 2^(z*c - R).
@@ -51,12 +52,13 @@ struct ChainArgs {
     double c_d;        // c_hi + c_lo exactly
     double T;
     int nseg, seg_len;      // statistics: segments per row, elements per segment
-    int nchunk, chunk_len;  // final draw: chunks per row, elements per chunk
+    int nchunk;             // final draw: chunk workgroups per row
+    int nquart;             // final draw: quarters (64 16-byte vectors) per row
     Stat* part;             // [B][2*gamma+1][nseg]
     float* zx;              // [B][2*gamma+1]: logit of the draft token in rows i < gamma
                             // (target) and gamma+1+i (draft); other entries unused
     ChainDecision* dec;     // [B]
-    double* chunk_sum;      // [B][nchunk]
+    double* qsum;           // [B][nquart]: draw-weight sum per quarter
     FinalState* fin;        // [B]
     int32_t* accept_len;
     int32_t* out_tokens;

@@ -123,14 +123,17 @@ __device__ void tree_resolve(const TreeArgs& a, int b, ArgmaxPart* s_part) {
         // stage the request's n*nseg row partials: every load issued before
         // any LDS store (indices past the end re-read the last partial and
         // are not stored)
+        static_assert(sizeof(ArgmaxPart) == 16, "ArgmaxPart is staged as one 16-byte vector");
         const int np = n * a.nseg;
-        const ArgmaxPart* src = a.part + static_cast<int64_t>(b) * np;
-        ArgmaxPart t[kStage];
-#pragma unroll
-        for (int m = 0; m < kStage; ++m) t[m] = src[min(tid + m * kThreads, np - 1)];
+        const uint4* src = reinterpret_cast<const uint4*>(a.part + static_cast<int64_t>(b) * np);
+        uint4* dst = reinterpret_cast<uint4*>(s_part);
+        uint4 t[kStage];
 #pragma unroll
         for (int m = 0; m < kStage; ++m)
-            if (tid + m * kThreads < np) s_part[tid + m * kThreads] = t[m];
+            t[m] = m * kThreads < np ? src[min(tid + m * kThreads, np - 1)] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int m = 0; m < kStage; ++m)
+            if (tid + m * kThreads < np) dst[tid + m * kThreads] = t[m];
     }
     if (tid == 0) {
         s_bad = 0;

@@ -112,6 +112,20 @@ def test_draft_logit_offset(dtype, offset):
     run_case(d, f"offset{offset}-{dtype}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_near_identical_draft(dtype):
+    """Draft logits within 0.03 of the target's: acceptance near 1, so after a
+    rejection the residual max(0, p - q) holds a tiny share of the mass and
+    every weight is a difference of nearly equal probabilities.  Uniforms are
+    pushed toward 1 so that rejections (and residual draws) do happen."""
+    d = synth.chain_inputs(64, 6, 20000, dtype, T=1.0, noise=0.03, seed=18)
+    rng = np.random.default_rng(18)
+    d["uniforms"] = (1.0 - 0.02 * rng.random(d["uniforms"].shape)).astype(np.float32)
+    d["uniforms"][:, -1] = rng.random(64, dtype=np.float32)
+    g, o = run_case(d, f"near-identical-{dtype}")
+    assert (o["accept_len"] < 6).sum() >= 10  # the residual path is exercised
+
+
 @pytest.mark.parametrize("T", [0.05, 5.0])
 def test_temperature_extremes(T):
     d = synth.chain_inputs(16, 8, 10000, "bf16", T=T, target=("normal", 2.0), noise=0.3, seed=10)
