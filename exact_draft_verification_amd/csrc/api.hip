@@ -106,6 +106,10 @@ int32_t tree_plan(int32_t B, int32_t n, int32_t V, int32_t dtype, TreePlan* p) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+hipEvent_t event_at(void* const* ev, int i) {
+    return ev ? static_cast<hipEvent_t>(ev[i]) : nullptr;
+}
+
 int32_t record(void* const* ev, int i, hipStream_t s) {
     if (!ev) return SV_OK;
     return hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) == hipSuccess ? SV_OK : SV_ERR_HIP;
@@ -197,9 +201,9 @@ extern "C" int32_t spec_verify_chain(const void* target_logits, const void* draf
     a.final_dist = final_dist;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (record(phase_events, 0, s) != SV_OK) return SV_ERR_HIP;
-    if (launch_chain_stats(a, dtype, s) != hipSuccess) return SV_ERR_HIP;
-    if (record(phase_events, 1, s) != SV_OK) return SV_ERR_HIP;
+    if (launch_chain_stats(a, dtype, s, event_at(phase_events, 0), event_at(phase_events, 1)) !=
+        hipSuccess)
+        return SV_ERR_HIP;
     if (launch_chain_chunks(a, dtype, s) != hipSuccess) return SV_ERR_HIP;
     if (launch_chain_select(a, dtype, s) != hipSuccess) return SV_ERR_HIP;
     if (record(phase_events, 2, s) != SV_OK) return SV_ERR_HIP;
@@ -239,9 +243,9 @@ extern "C" int32_t spec_verify_tree_greedy(const void* target_logits, int32_t dt
     a.accept_node = accept_node;
     a.out_tokens = out_tokens;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (record(phase_events, 0, s) != SV_OK) return SV_ERR_HIP;
-    if (launch_tree_argmax(a, dtype, s) != hipSuccess) return SV_ERR_HIP;
-    if (record(phase_events, 1, s) != SV_OK) return SV_ERR_HIP;
+    if (launch_tree_argmax(a, dtype, s, event_at(phase_events, 0), event_at(phase_events, 1)) !=
+        hipSuccess)
+        return SV_ERR_HIP;
     if (launch_tree_resolve(a, s) != hipSuccess) return SV_ERR_HIP;
     return SV_OK;
 }

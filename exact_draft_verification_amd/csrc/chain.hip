@@ -549,13 +549,12 @@ __global__ __launch_bounds__(kThreads) void chain_dist_kernel(ChainArgs a) {
 
 }  // namespace
 
-hipError_t launch_chain_stats(const ChainArgs& a, int dtype, hipStream_t s) {
-    const int grid = a.B * (2 * a.gamma + 1) * a.nseg;
+hipError_t launch_chain_stats(const ChainArgs& a, int dtype, hipStream_t s, hipEvent_t ev_start,
+                              hipEvent_t ev_stop) {
+    const dim3 grid(a.B * (2 * a.gamma + 1) * a.nseg);
     if (dtype == 0)
-        hipLaunchKernelGGL(chain_stats_kernel<F32>, dim3(grid), dim3(kThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL(chain_stats_kernel<BF16>, dim3(grid), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
+        return launch_timed(chain_stats_kernel<F32>, grid, dim3(kThreads), 0, s, ev_start, ev_stop, a);
+    return launch_timed(chain_stats_kernel<BF16>, grid, dim3(kThreads), 0, s, ev_start, ev_stop, a);
 }
 
 hipError_t launch_chain_chunks(const ChainArgs& a, int dtype, hipStream_t s) {

@@ -8,6 +8,7 @@
 // 16-byte boundary and after the last one are read one at a time.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -298,12 +299,17 @@ __device__ inline int block_max_int(int v, int* lds) {
     return *lds;
 }
 
-// Device-scope release before the "last workgroup to arrive" counters; the
-// workgroup that sees the final count issues another fence (acquire) before
-// reading what the others wrote.
-__device__ inline unsigned arrive(unsigned* counter) {
-    __threadfence();
-    return atomicAdd(counter, 1u);
+// Launch of a kernel on `s`, optionally bracketed by events that the launch
+// itself records at the kernel's start and end.
+template <class K, class... Args>
+inline hipError_t launch_timed(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                               hipEvent_t ev_start, hipEvent_t ev_stop, Args... args) {
+    if (ev_start && ev_stop)
+        hipExtLaunchKernelGGL(kernel, grid, block, static_cast<uint32_t>(lds), s, ev_start, ev_stop,
+                              0u, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+    return hipGetLastError();
 }
 
 }  // namespace sv

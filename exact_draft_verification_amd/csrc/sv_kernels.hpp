@@ -85,11 +85,17 @@ struct TreeArgs {
 };
 
 // Launchers (return the hipError_t of the launch).
-hipError_t launch_chain_stats(const ChainArgs& a, int dtype, hipStream_t s);
+// The streaming launchers take an optional pair of events (both null, or
+// both valid): when given, the launch itself records them at the kernel's
+// start and end (hipExtLaunchKernel), so their interval is the kernel's own
+// execution time.
+hipError_t launch_chain_stats(const ChainArgs& a, int dtype, hipStream_t s, hipEvent_t ev_start,
+                              hipEvent_t ev_stop);
 hipError_t launch_chain_chunks(const ChainArgs& a, int dtype, hipStream_t s);
 hipError_t launch_chain_select(const ChainArgs& a, int dtype, hipStream_t s);
 hipError_t launch_chain_dist(const ChainArgs& a, int dtype, hipStream_t s);
-hipError_t launch_tree_argmax(const TreeArgs& a, int dtype, hipStream_t s);
+hipError_t launch_tree_argmax(const TreeArgs& a, int dtype, hipStream_t s, hipEvent_t ev_start,
+                              hipEvent_t ev_stop);
 hipError_t launch_tree_resolve(const TreeArgs& a, hipStream_t s);
 
 }  // namespace sv

@@ -277,13 +277,12 @@ __global__ __launch_bounds__(kThreads) void tree_resolve_kernel(TreeArgs a) {
 
 }  // namespace
 
-hipError_t launch_tree_argmax(const TreeArgs& a, int dtype, hipStream_t s) {
-    const int grid = a.B * a.n * a.nseg;
+hipError_t launch_tree_argmax(const TreeArgs& a, int dtype, hipStream_t s, hipEvent_t ev_start,
+                              hipEvent_t ev_stop) {
+    const dim3 grid(a.B * a.n * a.nseg);
     if (dtype == 0)
-        hipLaunchKernelGGL(tree_argmax_kernel<F32>, dim3(grid), dim3(kThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL(tree_argmax_kernel<BF16>, dim3(grid), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
+        return launch_timed(tree_argmax_kernel<F32>, grid, dim3(kThreads), 0, s, ev_start, ev_stop, a);
+    return launch_timed(tree_argmax_kernel<BF16>, grid, dim3(kThreads), 0, s, ev_start, ev_stop, a);
 }
 
 hipError_t launch_tree_resolve(const TreeArgs& a, hipStream_t s) {

@@ -116,11 +116,12 @@ size_t spec_verify_chain_workspace_bytes(int32_t B, int32_t gamma, int32_t V, in
  *                 spec_verify_chain_workspace_bytes(B, gamma, V, dtype)
  *                 bytes, 16-byte aligned (contents irrelevant).
  *  stream         hipStream_t to enqueue on (NULL = null stream).
- *  phase_events   NULLABLE: if not NULL, points to 3 hipEvent_t handles that
- *                 are recorded on `stream` before the row-statistics kernel
- *                 (the one pass over every logit), after it, and after the
- *                 final-draw kernels (instrumentation for timing; the
- *                 optional final_dist pass comes later).
+ *  phase_events   NULLABLE: if not NULL, points to 3 hipEvent_t handles
+ *                 (created with timing enabled): [0] and [1] are recorded by
+ *                 the launch of the row-statistics kernel (the one pass over
+ *                 every logit) at that kernel's start and end, [2] on
+ *                 `stream` after the final-draw kernels (instrumentation for
+ *                 timing; the optional final_dist pass comes later).
  */
 int32_t spec_verify_chain(const void *target_logits, const void *draft_logits, int32_t dtype,
                           const int32_t *draft_tokens, const float *uniforms, int32_t B,
@@ -149,9 +150,10 @@ size_t spec_verify_tree_greedy_workspace_bytes(int32_t B, int32_t n, int32_t V, 
  *                 token id on ties), then -1.
  *  workspace      as for spec_verify_chain, sized by
  *                 spec_verify_tree_greedy_workspace_bytes.
- *  phase_events   NULLABLE: 2 hipEvent_t recorded before and after the
- *                 row-argmax kernel (the one pass over every logit); the
- *                 path-resolution kernel follows.
+ *  phase_events   NULLABLE: 2 hipEvent_t (timing enabled) recorded by the
+ *                 launch of the row-argmax kernel (the one pass over every
+ *                 logit) at that kernel's start and end; the path-resolution
+ *                 kernel follows.
  */
 int32_t spec_verify_tree_greedy(const void *target_logits, int32_t dtype,
                                 const int32_t *parents, const int32_t *tokens, int32_t B,
