@@ -40,7 +40,7 @@ void plan_segments(int64_t rows_total, int V, int epv, int64_t target, int min_v
 }
 
 struct ChainPlan {
-    int rows, nseg, seg_len, nchunk, nquart;
+    int rows, nseg, seg_len, nchunk, chunk_tiles, nquart;
     size_t off_part, off_zx, off_dec, off_qsum, off_fin, bytes;
 };
 
@@ -66,10 +66,14 @@ int32_t chain_plan(int32_t B, int32_t gamma, int32_t V, int32_t dtype, ChainPlan
     plan_segments(rows_total, V, epv, kTargetUnits, 4,
                   static_cast<int>(kMaxBlockParts / rows), &p->nseg, &p->seg_len);
     if (rows_total * p->nseg > INT32_MAX) return SV_ERR_SHAPE;
-    // final draw: tiles of one 16-byte vector per thread, kChunkTiles tiles
-    // per chunk workgroup, sums kept per quarter tile (64 vectors)
+    // final draw: tiles of one 16-byte vector per thread, sums kept per
+    // quarter tile (64 vectors); a chunk workgroup takes 1 or 4 tiles: few
+    // tiles in all (a small batch) favour many short workgroups, many tiles
+    // favour fewer, longer ones that repeat the block's decision less
     const int64_t tile = static_cast<int64_t>(kThreadsHost) * epv;
-    p->nchunk = static_cast<int>(ceil_div(ceil_div(V, tile), kChunkTiles));
+    const int64_t tiles_total = static_cast<int64_t>(B) * ceil_div(V, tile);
+    p->chunk_tiles = tiles_total <= 2048 ? 1 : 4;
+    p->nchunk = static_cast<int>(ceil_div(ceil_div(V, tile), p->chunk_tiles));
     p->nquart = static_cast<int>(ceil_div(V, 64 * static_cast<int64_t>(epv)));
     if (static_cast<int64_t>(B) * p->nchunk > INT32_MAX) return SV_ERR_SHAPE;
     const size_t nb = static_cast<size_t>(B), nr = static_cast<size_t>(rows_total);
@@ -189,6 +193,7 @@ extern "C" int32_t spec_verify_chain(const void* target_logits, const void* draf
     a.nseg = p.nseg;
     a.seg_len = p.seg_len;
     a.nchunk = p.nchunk;
+    a.chunk_tiles = p.chunk_tiles;
     a.nquart = p.nquart;
     char* ws = static_cast<char*>(workspace);
     a.part = reinterpret_cast<Stat*>(ws + p.off_part);

@@ -41,7 +41,6 @@ namespace sv {
 namespace {
 
 constexpr double kDomain = 268435456.0;  // |m| / T limit (2^28)
-constexpr int kStreamU = 4;              // 16-byte vectors per thread per batch
 
 template <class E>
 __device__ inline const typename E::storage* chain_row(const ChainArgs& a, int b, int rho) {
@@ -67,8 +66,8 @@ struct StatFolder {
 };
 
 // Statistics of elements [e0, e1) of one row, folded by the whole workgroup
-// (one partial per thread).
-template <class E>
+// (one partial per thread); U 16-byte vectors per thread per batch.
+template <class E, int U>
 __device__ inline Stat row_range_stats(const typename E::storage* row, int e0, int e1, float c_hi,
                                        float c_lo) {
     StatFolder<E> f{stat_empty(), c_hi, c_lo};
@@ -79,7 +78,7 @@ __device__ inline Stat row_range_stats(const typename E::storage* row, int e0, i
         float x = E::one(row + e);
         stat_fold<1>(f.s, &x, c_hi, c_lo);
     }
-    stream_vectors<kStreamU>(reinterpret_cast<const char*>(row + sp.body_begin), sp.nvec, f);
+    stream_vectors<U>(reinterpret_cast<const char*>(row + sp.body_begin), sp.nvec, f);
     for (int e = sp.tail_begin + tid; e < sp.tail_end; e += kThreads) {
         float x = E::one(row + e);
         stat_fold<1>(f.s, &x, c_hi, c_lo);
@@ -87,7 +86,7 @@ __device__ inline Stat row_range_stats(const typename E::storage* row, int e0, i
     return f.s;
 }
 
-template <class E>
+template <class E, int U>
 __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
     __shared__ Stat s_w[kWaves];
     const int rows = 2 * a.gamma + 1;
@@ -115,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
             }
         }
     }
-    Stat st = row_range_stats<E>(row, e0, e1, a.c_hi, a.c_lo);
+    Stat st = row_range_stats<E, U>(row, e0, e1, a.c_hi, a.c_lo);
     st = block_reduce_stat(st, s_w);
     if (tid == 0) {
         a.part[unit] = st;
@@ -259,18 +258,31 @@ __device__ inline float one_minus_exp2_neg(float D) {
 }
 
 // Unnormalised draw weight of token v.  With P(v) = 2^(z_p c - R_p)
-// (proportional to p_k(v)): residual  w = P(v) * (1 - 2^-D(v)) for D > 0,
-// else 0; bonus row and fallback: w = P(v).  Masked tokens need no test: a
-// -inf target logit gives P = 0 and D = -inf or NaN (w = 0); a -inf draft
-// logit gives D = +inf and w = P(v), as q(v) = 0 requires.
-template <class E>
+// (proportional to p_k(v)): residual  w = P(v) * (1 - 2^-max(D(v), 0)), which
+// is 0 for D <= 0; bonus row and fallback: w = P(v).  Branch-free, and
+// masked tokens need no test: a -inf target logit gives P = 0 and D = -inf or
+// NaN (clamped to 0, so w = 0); a -inf draft logit gives D = +inf and
+// w = P(v), as q(v) = 0 requires.
+template <class E, bool RESID>
 __device__ inline float draw_weight(float zp, float zq, const DrawRow& r) {
     float t = fmaf(zp, r.c_hi, -r.Rp);
     t = fmaf(zp, r.c_lo, t);
-    const float P = __builtin_amdgcn_exp2f(t);
-    if (!r.resid) return P;
-    const float D = log_ratio(zp, zq, r, E{});
-    return D > 0.0f ? P * one_minus_exp2_neg(D) : 0.0f;
+    if constexpr (!RESID) {
+        return __builtin_amdgcn_exp2f(t);
+    } else {
+        // R_p is the integer ceiling of the row's largest z*c, so t > -60
+        // keeps every token whose target weight is within 2^-60 of the
+        // largest; the others get weight 0.  Together they could move any
+        // point of the CDF by at most V * 2^-60 relative (1.3e-13 at
+        // V = 151,936), far below the fp32 rounding of the sums, and the
+        // skip saves the residual arithmetic for the bulk of a peaked row.
+        float w = 0.0f;
+        if (t > -60.0f) {
+            const float D = fmaxf(log_ratio(zp, zq, r, E{}), 0.0f);
+            w = __builtin_amdgcn_exp2f(t) * one_minus_exp2_neg(D);
+        }
+        return w;
+    }
 }
 
 template <class E>
@@ -323,16 +335,22 @@ __device__ inline void load_tokens(const FinalRows<E>& rows, bool resid, int e, 
 
 // A lane's weights and their sum, accumulated in token order in fp32 (the
 // select kernel repeats exactly this order, so its running prefix ends on
-// the very value the quarter sums were built from).
-template <class E>
-__device__ inline float lane_weights(const float* zp, const float* zq, const DrawRow& r, float* w) {
+// the very value the quarter sums were built from).  The residual/bonus
+// choice is taken once here, outside the per-token code.
+template <class E, bool RESID>
+__device__ inline float lane_weights_t(const float* zp, const float* zq, const DrawRow& r, float* w) {
     float s = 0.0f;
 #pragma unroll
     for (int i = 0; i < E::kPerVec; ++i) {
-        w[i] = draw_weight<E>(zp[i], zq[i], r);
+        w[i] = draw_weight<E, RESID>(zp[i], zq[i], r);
         s += w[i];
     }
     return s;
+}
+
+template <class E>
+__device__ inline float lane_weights(const float* zp, const float* zq, const DrawRow& r, float* w) {
+    return r.resid ? lane_weights_t<E, true>(zp, zq, r, w) : lane_weights_t<E, false>(zp, zq, r, w);
 }
 
 __device__ inline double wave_sum(double v) {
@@ -376,7 +394,9 @@ __device__ inline ChainDecision load_decision(const ChainArgs& a, int b) {
     return d;
 }
 
-template <class E>
+// Chunk workgroup: the block's decision, then TILES consecutive tiles of the
+// final row, every load issued before any weight is computed.
+template <class E, int TILES>
 __global__ __launch_bounds__(kThreads) void chain_chunks_kernel(ChainArgs a) {
     extern __shared__ Stat s_part[];  // [2*gamma+1][nseg]
     constexpr int kTile = kThreads * E::kPerVec;
@@ -389,18 +409,17 @@ __global__ __launch_bounds__(kThreads) void chain_chunks_kernel(ChainArgs a) {
     const FinalRows<E> rows = final_rows<E>(a, b, d.k);
     const DrawRow r = draw_row(a, d, d.k < a.gamma);
     const int ntile = (a.V + kTile - 1) / kTile;
-    // every load of this workgroup's tiles before any weight is computed; a
-    // tile past the row's end reads as -inf (weight 0) without a load
-    float zp[kChunkTiles][E::kPerVec], zq[kChunkTiles][E::kPerVec];
+    // a tile past the row's end reads as -inf (weight 0) without a load
+    float zp[TILES][E::kPerVec], zq[TILES][E::kPerVec];
 #pragma unroll
-    for (int m = 0; m < kChunkTiles; ++m) {
-        const int j = c * kChunkTiles + m;
+    for (int m = 0; m < TILES; ++m) {
+        const int j = c * TILES + m;
         load_tokens<E>(rows, r.resid, j * kTile + tid * E::kPerVec, a.V, zp[m], zq[m]);
     }
     double* qs = a.qsum + static_cast<int64_t>(b) * a.nquart;
 #pragma unroll
-    for (int m = 0; m < kChunkTiles; ++m) {
-        const int j = c * kChunkTiles + m;
+    for (int m = 0; m < TILES; ++m) {
+        const int j = c * TILES + m;
         float w[E::kPerVec];
         const double sw = wave_sum(static_cast<double>(lane_weights<E>(zp[m], zq[m], r, w)));
         const int qi = j * kWaves + wave;
@@ -424,18 +443,26 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
     constexpr int kQuart = 64 * E::kPerVec;
     const int b = blockIdx.x, lane = threadIdx.x;
     const int g = a.gamma;
+    double* qs = a.qsum + static_cast<int64_t>(b) * a.nquart;
+    const int per = (a.nquart + 63) / 64;
+    const int q0 = min(a.nquart, lane * per), q1 = min(a.nquart, q0 + per);
+    // this lane's run of quarter sums, requested together with the decision
+    // and the uniform (runs of up to kRun in registers, longer ones looped)
+    constexpr int kRun = 16;
+    double run_v[kRun];
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) run_v[j] = q0 + j < q1 ? qs[q0 + j] : 0.0;
     const ChainDecision d = load_decision(a, b);
     const double u = static_cast<double>(a.uniforms[static_cast<int64_t>(b) * (g + 1) + g]);
     if (d.k < 0) {
         write_outputs<E>(a, b, -1, -1);
         return;
     }
-    double* qs = a.qsum + static_cast<int64_t>(b) * a.nquart;
-    const int per = (a.nquart + 63) / 64;
-    const int q0 = min(a.nquart, lane * per), q1 = min(a.nquart, q0 + per);
     const FinalRows<E> rows = final_rows<E>(a, b, d.k);
     double mine = 0.0;
-    for (int q = q0; q < q1; ++q) mine += qs[q];
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) mine += run_v[j];
+    for (int q = q0 + kRun; q < q1; ++q) mine += qs[q];
     int fallback = 0;
     DrawRow r = draw_row(a, d, d.k < g);
     if (r.resid && !(wave_sum(mine) > 0.0)) {
@@ -469,34 +496,57 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
         src = pos ? 63 - __clzll(static_cast<long long>(pos)) : 0;
         last_positive = true;
     }
-    int qfound = q0;
-    double b0 = excl;
-    if (lane == src) {
-        // walk this lane's run
-        double run = excl, run_last = excl;
-        int lastq = -1;
-        qfound = -1;
-        for (int q = q0; q < q1; ++q) {
-            const double sq = qs[q];
-            if (sq > 0.0) {
-                lastq = q;
-                run_last = run;
-                if (!last_positive && run + sq > target) {
-                    qfound = q;
-                    b0 = run;
-                    break;
-                }
-            }
-            run += sq;
-        }
-        if (qfound < 0) {
+    // the quarter inside the crossing lane's run: lane j takes the run's
+    // j-th quarter (runs of up to 64 quarters; longer runs are walked by
+    // their own lane), one more wave scan finds the crossing
+    const int sq0 = __shfl(q0, src, 64), sq1 = __shfl(q1, src, 64);
+    const double sbase = __shfl(excl, src, 64);
+    int qstar;
+    double base;
+    if (sq1 - sq0 <= 64) {
+        const int q = sq0 + lane;
+        const double x = q < sq1 ? qs[q] : 0.0;
+        double xt;
+        const double xe = wave_exclusive_scan(x, &xt);
+        const unsigned long long hq = __ballot(!last_positive && x > 0.0 && sbase + xe + x > target);
+        const unsigned long long pq = __ballot(x > 0.0);
+        int jj;
+        if (hq) {
+            jj = __ffsll(static_cast<long long>(hq)) - 1;
+        } else {
             // rounding: the run's last positive quarter
-            qfound = lastq >= 0 ? lastq : q0;
-            b0 = run_last;
+            jj = pq ? 63 - __clzll(static_cast<long long>(pq)) : 0;
         }
+        qstar = sq0 + jj;
+        base = sbase + __shfl(xe, jj, 64);
+    } else {
+        int qfound = q0;
+        double b0 = excl;
+        if (lane == src) {
+            double run = excl, run_last = excl;
+            int lastq = -1;
+            qfound = -1;
+            for (int q = q0; q < q1; ++q) {
+                const double sqv = qs[q];
+                if (sqv > 0.0) {
+                    lastq = q;
+                    run_last = run;
+                    if (!last_positive && run + sqv > target) {
+                        qfound = q;
+                        b0 = run;
+                        break;
+                    }
+                }
+                run += sqv;
+            }
+            if (qfound < 0) {
+                qfound = lastq >= 0 ? lastq : q0;
+                b0 = run_last;
+            }
+        }
+        qstar = __shfl(qfound, src, 64);
+        base = __shfl(b0, src, 64);
     }
-    const int qstar = __shfl(qfound, src, 64);
-    const double base = __shfl(b0, src, 64);
     // tokens of the chosen quarter, kPerVec per lane in token order
     const int e0 = qstar * kQuart + lane * E::kPerVec;
     float zp[E::kPerVec], zq[E::kPerVec], w[E::kPerVec];
@@ -542,8 +592,10 @@ __global__ __launch_bounds__(kThreads) void chain_dist_kernel(ChainArgs a) {
     const DrawRow r = draw_row(a, d, d.k < a.gamma && !f.fallback);
     const double inv = 1.0 / f.W;
     for (int e = threadIdx.x; e < a.V; e += kThreads) {
-        const float zq = r.resid ? E::one(rows.q + e) : 0.0f;
-        out[e] = static_cast<float>(static_cast<double>(draw_weight<E>(E::one(rows.p + e), zq, r)) * inv);
+        const float zp = E::one(rows.p + e);
+        const float w = r.resid ? draw_weight<E, true>(zp, E::one(rows.q + e), r)
+                                : draw_weight<E, false>(zp, 0.0f, r);
+        out[e] = static_cast<float>(static_cast<double>(w) * inv);
     }
 }
 
@@ -552,19 +604,31 @@ __global__ __launch_bounds__(kThreads) void chain_dist_kernel(ChainArgs a) {
 hipError_t launch_chain_stats(const ChainArgs& a, int dtype, hipStream_t s, hipEvent_t ev_start,
                               hipEvent_t ev_stop) {
     const dim3 grid(a.B * (2 * a.gamma + 1) * a.nseg);
+    // 8 vectors per thread per batch once a segment holds two such batches,
+    // else 4 (a short segment would mostly re-read its last vector)
+    const bool deep = a.seg_len / (kThreads * (dtype == 0 ? 4 : 8)) >= 16;
     if (dtype == 0)
-        return launch_timed(chain_stats_kernel<F32>, grid, dim3(kThreads), 0, s, ev_start, ev_stop, a);
-    return launch_timed(chain_stats_kernel<BF16>, grid, dim3(kThreads), 0, s, ev_start, ev_stop, a);
+        return deep ? launch_timed(chain_stats_kernel<F32, 8>, grid, dim3(kThreads), 0, s, ev_start, ev_stop, a)
+                    : launch_timed(chain_stats_kernel<F32, 4>, grid, dim3(kThreads), 0, s, ev_start, ev_stop, a);
+    return deep ? launch_timed(chain_stats_kernel<BF16, 8>, grid, dim3(kThreads), 0, s, ev_start, ev_stop, a)
+                : launch_timed(chain_stats_kernel<BF16, 4>, grid, dim3(kThreads), 0, s, ev_start, ev_stop, a);
 }
 
 hipError_t launch_chain_chunks(const ChainArgs& a, int dtype, hipStream_t s) {
-    const int grid = a.B * a.nchunk;
+    const dim3 grid(a.B * a.nchunk);
     const size_t lds = sizeof(Stat) * static_cast<size_t>(2 * a.gamma + 1) * a.nseg;
-    if (dtype == 0)
-        hipLaunchKernelGGL(chain_chunks_kernel<F32>, dim3(grid), dim3(kThreads), lds, s, a);
-    else
-        hipLaunchKernelGGL(chain_chunks_kernel<BF16>, dim3(grid), dim3(kThreads), lds, s, a);
-    return hipGetLastError();
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, dim3(kThreads), lds, s, a);
+        return hipGetLastError();
+    };
+    if (dtype == 0) {
+        if (a.chunk_tiles == 1) return go(chain_chunks_kernel<F32, 1>);
+        if (a.chunk_tiles == 2) return go(chain_chunks_kernel<F32, 2>);
+        return go(chain_chunks_kernel<F32, 4>);
+    }
+    if (a.chunk_tiles == 1) return go(chain_chunks_kernel<BF16, 1>);
+    if (a.chunk_tiles == 2) return go(chain_chunks_kernel<BF16, 2>);
+    return go(chain_chunks_kernel<BF16, 4>);
 }
 
 hipError_t launch_chain_select(const ChainArgs& a, int dtype, hipStream_t s) {

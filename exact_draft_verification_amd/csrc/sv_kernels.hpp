@@ -17,8 +17,6 @@ namespace sv {
 constexpr int kMaxGamma = 255;        // draft positions per chain block
 constexpr int kMaxTreeNodes = 1024;   // nodes per tree, root included
 constexpr int kMaxBlockParts = 2048;  // row partials of one block / request (staged in LDS)
-constexpr int kChunkTiles = 4;        // final-draw tiles (one 16-byte vector per thread) per
-                                      // chunk workgroup
 
 // Row statistics of a temperature softmax (see stat_fold in sv_device.hpp):
 // m = largest logit, R = integer-valued reference, S = sum 2^(z*c - R).
@@ -53,6 +51,8 @@ struct ChainArgs {
     double T;
     int nseg, seg_len;      // statistics: segments per row, elements per segment
     int nchunk;             // final draw: chunk workgroups per row
+    int chunk_tiles;        // final draw: tiles (one 16-byte vector per thread) per chunk
+                            // workgroup: 1, 2 or 4
     int nquart;             // final draw: quarters (64 16-byte vectors) per row
     Stat* part;             // [B][2*gamma+1][nseg]
     float* zx;              // [B][2*gamma+1]: logit of the draft token in rows i < gamma
