@@ -165,9 +165,19 @@ __device__ ChainDecision chain_decide(const ChainArgs& a, int b, Stat* s_part) {
     }
     __syncthreads();
     for (int r = tid; r < rows; r += kThreads) {
+        // four independent merge chains (the merge is a short dependent
+        // sequence, so one chain over many segments is latency-bound)
         const Stat* p = s_part + r * a.nseg;
-        Stat t = p[0];
-        for (int s = 1; s < a.nseg; ++s) t = stat_merge(t, p[s]);
+        Stat t0 = p[0], t1 = stat_empty(), t2 = stat_empty(), t3 = stat_empty();
+        int s = 1;
+        for (; s + 3 < a.nseg; s += 4) {
+            t0 = stat_merge(t0, p[s]);
+            t1 = stat_merge(t1, p[s + 1]);
+            t2 = stat_merge(t2, p[s + 2]);
+            t3 = stat_merge(t3, p[s + 3]);
+        }
+        for (; s < a.nseg; ++s) t0 = stat_merge(t0, p[s]);
+        const Stat t = stat_merge(stat_merge(t0, t1), stat_merge(t2, t3));
         const bool ok = isfinite(t.S) && t.S > 0.0 && fabs(static_cast<double>(t.m) / a.T) <= kDomain;
         if (!ok) atomicOr(&s_bad, 1);
         s_L[r] = static_cast<double>(t.R) + log2(t.S);
@@ -505,7 +515,20 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
     double base;
     if (sq1 - sq0 <= 64) {
         const int q = sq0 + lane;
-        const double x = q < sq1 ? qs[q] : 0.0;
+        double x;
+        if (per <= kRun && !fallback) {
+            // the run is in the crossing lane's registers (the fallback
+            // rewrote the sums in memory only): lane j takes its j-th entry
+            // by shuffle
+            x = 0.0;
+#pragma unroll
+            for (int j = 0; j < kRun; ++j) {
+                const double v = __shfl(run_v[j], src, 64);
+                if (lane == j) x = v;
+            }
+        } else {
+            x = q < sq1 ? qs[q] : 0.0;
+        }
         double xt;
         const double xe = wave_exclusive_scan(x, &xt);
         const unsigned long long hq = __ballot(!last_positive && x > 0.0 && sbase + xe + x > target);
