@@ -305,7 +305,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the verification kernels run on a single "
-              "device and this build has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
+              "device and the library has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
