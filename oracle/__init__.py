@@ -54,8 +54,10 @@ def _declare(lib):
     lib.oracle_chain_du.argtypes = [P, P, I, P, P, I, I, I, D, P, P, P, P, P, P, I]
     lib.oracle_chain_alpha.argtypes = [P, P, I, I, I, I, D, P]
     lib.oracle_tree_greedy.argtypes = [P, I, P, P, I, I, I, P, P, P, P, I]
+    lib.oracle_chain_pointmass.argtypes = [P, I, P, P, I, I, I, D, P, P, P, P, P, P, I]
+    lib.oracle_chain_pointmass_du.argtypes = [P, I, P, P, I, I, I, D, P, P, P, P, P, P, I]
     for f in (lib.oracle_chain, lib.oracle_chain_du, lib.oracle_chain_alpha,
-              lib.oracle_tree_greedy):
+              lib.oracle_tree_greedy, lib.oracle_chain_pointmass, lib.oracle_chain_pointmass_du):
         f.restype = I
     return lib
 
@@ -116,6 +118,38 @@ def chain(target, draft, draft_tokens, uniforms, T, dtype="f32", want_dist=False
                               _ptr(ratios), _ptr(fb), nt)
     if rc != 0:
         raise ValueError(f"oracle_chain rejected its arguments (rc={rc})")
+    return dict(accept_len=acc, out_tokens=out, margin=margin, ratios=ratios, fallback=fb,
+                final_dist=dist)
+
+
+def chain_pointmass(target, draft_tokens, uniforms, T, dtype="f32", want_dist=False,
+                    threads=None) -> dict:
+    """Point-mass chain verification: the draft proposes each token with
+    certainty, so test i accepts with probability p_i(x_i); a rejection draws
+    from p_k without x_k, renormalised; a full block draws the bonus from
+    p_gamma.  Same outputs as ``chain`` (``ratios`` hold p_i(x_i))."""
+    lib = _load()
+    target = _logits(target, dtype)
+    B, g1, V = target.shape
+    g = g1 - 1
+    tok = np.ascontiguousarray(draft_tokens, dtype=np.int32).reshape(B, g)
+    u = np.ascontiguousarray(uniforms)
+    if u.shape != (B, g + 1):
+        raise ValueError("uniforms must be [B, gamma+1]")
+    acc = np.empty(B, np.int32)
+    out = np.empty((B, g + 1), np.int32)
+    margin = np.empty(B, np.float64)
+    ratios = np.empty((B, g), np.float64)
+    fb = np.empty(B, np.int32)
+    dist = np.empty((B, V), np.float64) if want_dist else None
+    nt = default_threads() if threads is None else threads
+    fn = lib.oracle_chain_pointmass_du if u.dtype == np.float64 else lib.oracle_chain_pointmass
+    if u.dtype != np.float64:
+        u = np.ascontiguousarray(u, dtype=np.float32)
+    rc = fn(_ptr(target), _DT[dtype], _ptr(tok), _ptr(u), B, g, V, float(T), _ptr(acc), _ptr(out),
+            _ptr(dist), _ptr(margin), _ptr(ratios), _ptr(fb), nt)
+    if rc != 0:
+        raise ValueError(f"oracle_chain_pointmass rejected its arguments (rc={rc})")
     return dict(accept_len=acc, out_tokens=out, margin=margin, ratios=ratios, fallback=fb,
                 final_dist=dist)
 

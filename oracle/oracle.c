@@ -355,6 +355,195 @@ int oracle_chain(const void *target, const void *draft, int dtype, const int32_t
     return rc;
 }
 
+/* ------------------------------------------------------- point mass -- */
+
+/* Point-mass ("exact-match") chain verification of one block ([J++]
+ * Appendix F.3 and Proposition 1; the worked example of Appendix F.1).  The
+ * draft proposes x_i with certainty, so the test at position i accepts with
+ * probability p_i(x_i): accept iff u_i < p_i(x_i), left to right, the first
+ * failure k ending the block.  After a rejection at k the extra token is
+ * drawn from p_k with x_k removed and the remainder renormalised (the
+ * residual max(0, p_k - q_k) for q_k = delta_{x_k}); after a fully accepted
+ * block it is drawn from the bonus row p_gamma.  Same readings as the chain:
+ * u[i] drives test i, u[gamma] the final draw by inverse CDF in ascending
+ * token id; an empty residual falls back to p_k (flagged, margin 0). */
+static void pointmass_block(const chain_job *J, int b, double *w)
+{
+    const int g = J->gamma, V = J->V, dt = J->dtype;
+    const double T = J->T;
+    const double *u = J->uniforms + (int64_t)b * (g + 1);
+    int32_t *out = J->out_tokens + (int64_t)b * (g + 1);
+    const int32_t *d = J->draft_tokens + (int64_t)b * g;
+    const int64_t trow = (int64_t)V, tblk = (int64_t)(g + 1) * V;
+
+    for (int i = 0; i <= g; ++i)
+        out[i] = -1;
+    J->accept_len[b] = -1;
+    if (J->margin)
+        J->margin[b] = 0.0;
+    if (J->fallback)
+        J->fallback[b] = 0;
+    if (J->final_dist)
+        for (int v = 0; v < V; ++v)
+            J->final_dist[(int64_t)b * V + v] = 0.0;
+    if (J->ratios)
+        for (int i = 0; i < g; ++i)
+            J->ratios[(int64_t)b * g + i] = NAN;
+
+    for (int i = 0; i < g; ++i)
+        if (d[i] < 0 || d[i] >= V)
+            return;
+    double *mp = malloc(sizeof(double) * (size_t)(g + 1));
+    double *Sp = malloc(sizeof(double) * (size_t)(g + 1));
+    int bad = 0;
+    for (int j = 0; j <= g && !bad; ++j)
+        bad |= row_softmax_stats(J->target, dt, b * tblk + j * trow, V, T, &mp[j], &Sp[j]);
+    if (bad)
+        goto done;
+
+    /* Tests: r_i = p_i(x_i). */
+    double margin = INFINITY;
+    int k = g, decided = 0;
+    for (int i = 0; i < g; ++i) {
+        const double r = prob_at(J->target, dt, b * tblk + i * trow, d[i], T, mp[i], Sp[i]);
+        if (J->ratios)
+            J->ratios[(int64_t)b * g + i] = r;
+        if (!decided) {
+            margin = fmin(margin, fabs(u[i] - r));
+            if (!(u[i] < r)) {
+                k = i;
+                decided = 1;
+            }
+        }
+    }
+
+    /* Final draw: p_k without x_k after a rejection, p_gamma after none. */
+    const int64_t prow = b * tblk + (int64_t)k * trow;
+    double W = 0.0;
+    for (int v = 0; v < V; ++v) {
+        w[v] = (k < g && v == d[k]) ? 0.0 : prob_at(J->target, dt, prow, v, T, mp[k], Sp[k]);
+        W += w[v];
+    }
+    int fell_back = 0;
+    if (!(W > 0.0)) {
+        fell_back = 1;
+        W = 0.0;
+        for (int v = 0; v < V; ++v) {
+            w[v] = prob_at(J->target, dt, prow, v, T, mp[k], Sp[k]);
+            W += w[v];
+        }
+    }
+    const double t = u[g] * W;
+    double C = 0.0, Cprev = 0.0;
+    int tok = -1;
+    for (int v = 0; v < V; ++v) {
+        Cprev = C;
+        C += w[v];
+        if (C > t) {
+            tok = v;
+            break;
+        }
+    }
+    double mf;
+    if (tok < 0) {
+        for (int v = V - 1; v >= 0; --v)
+            if (w[v] > 0.0) {
+                tok = v;
+                break;
+            }
+        mf = 0.0;
+    } else {
+        mf = fmin(t - Cprev, C - t) / W;
+    }
+    margin = fmin(margin, mf);
+    if (fell_back)
+        margin = 0.0;
+
+    J->accept_len[b] = k;
+    for (int i = 0; i < k; ++i)
+        out[i] = d[i];
+    out[k] = tok;
+    if (J->margin)
+        J->margin[b] = margin;
+    if (J->fallback)
+        J->fallback[b] = fell_back;
+    if (J->final_dist)
+        for (int v = 0; v < V; ++v)
+            J->final_dist[(int64_t)b * V + v] = w[v] / W;
+done:
+    free(mp);
+    free(Sp);
+}
+
+static void *pointmass_worker(void *p)
+{
+    const chain_arg *a = (const chain_arg *)p;
+    const chain_job *J = a->J;
+    double *w = J->work + (int64_t)a->tid * J->V;
+    for (int b = a->tid; b < J->B; b += J->nthreads)
+        pointmass_block(J, b, w);
+    return NULL;
+}
+
+/* Point-mass chain verification over B blocks: target [B][gamma+1][V],
+ * draft tokens [B][gamma], double uniforms [B][gamma+1]; outputs as
+ * oracle_chain_du (ratios hold p_i(x_i)). */
+int oracle_chain_pointmass_du(const void *target, int dtype, const int32_t *draft_tokens,
+                              const double *uniforms, int B, int gamma, int V, double T,
+                              int32_t *accept_len, int32_t *out_tokens, double *final_dist,
+                              double *margin, double *ratios, int32_t *fallback, int nthreads)
+{
+    if (!target || !draft_tokens || !uniforms || !accept_len || !out_tokens)
+        return -1;
+    if (B < 1 || gamma < 1 || V < 1 || !(T > 0.0) || !isfinite(T))
+        return -1;
+    if (dtype != ORC_F32 && dtype != ORC_BF16)
+        return -1;
+    chain_job J = {target, NULL, dtype, draft_tokens, uniforms, B, gamma, V, T, accept_len,
+                   out_tokens, final_dist, margin, ratios, fallback, NULL, nthreads};
+    int nt = J.nthreads < 1 ? 1 : J.nthreads;
+    if (nt > B)
+        nt = B;
+    J.nthreads = nt;
+    J.work = malloc(sizeof(double) * (size_t)nt * (size_t)V);
+    if (!J.work)
+        return -2;
+    pthread_t *th = malloc(sizeof(pthread_t) * (size_t)nt);
+    chain_arg *args = malloc(sizeof(chain_arg) * (size_t)nt);
+    for (int i = 0; i < nt; ++i) {
+        args[i].J = &J;
+        args[i].tid = i;
+        pthread_create(&th[i], NULL, pointmass_worker, &args[i]);
+    }
+    for (int i = 0; i < nt; ++i)
+        pthread_join(th[i], NULL);
+    free(th);
+    free(args);
+    free(J.work);
+    return 0;
+}
+
+/* The same with the float32 uniforms of the library interface. */
+int oracle_chain_pointmass(const void *target, int dtype, const int32_t *draft_tokens,
+                           const float *uniforms, int B, int gamma, int V, double T,
+                           int32_t *accept_len, int32_t *out_tokens, double *final_dist,
+                           double *margin, double *ratios, int32_t *fallback, int nthreads)
+{
+    if (!uniforms || B < 1 || gamma < 1)
+        return -1;
+    size_t nu = (size_t)B * (size_t)(gamma + 1);
+    double *ud = malloc(sizeof(double) * nu);
+    if (!ud)
+        return -2;
+    for (size_t i = 0; i < nu; ++i)
+        ud[i] = (double)uniforms[i];
+    int rc = oracle_chain_pointmass_du(target, dtype, draft_tokens, ud, B, gamma, V, T,
+                                       accept_len, out_tokens, final_dist, margin, ratios,
+                                       fallback, nthreads);
+    free(ud);
+    return rc;
+}
+
 /* Per-position acceptance probability alpha_i = sum_v min(p_i(v), q_i(v)),
  * the probability that the test at position i passes when x ~ q_i
  * ([SD] "Rejection uses a residual distribution": accepted and residual

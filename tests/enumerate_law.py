@@ -19,19 +19,34 @@ STEPS = 60
 U_REJECT = float(np.nextafter(1.0, 0.0))  # largest double below 1
 
 
-def _run(target, draft, tokens, U, T, dtype):
+def _chain_runner(tgt, drf, tok, U, T, dtype):
+    return oracle.chain(tgt, drf, tok, U, T, dtype=dtype, threads=1)
+
+
+def _pointmass_runner(tgt, drf, tok, U, T, dtype):
+    return oracle.chain_pointmass(tgt, tok, U, T, dtype=dtype, threads=1)
+
+
+RUNNERS = {"chain": _chain_runner, "pointmass": _pointmass_runner}
+
+
+def _run(target, draft, tokens, U, T, dtype, runner=_chain_runner):
     B = U.shape[0]
     tgt = np.broadcast_to(target, (B,) + target.shape).copy()
     drf = np.broadcast_to(draft, (B,) + draft.shape).copy()
     tok = np.broadcast_to(tokens, (B,) + tokens.shape).copy()
-    return oracle.chain(tgt, drf, tok, U, T, dtype=dtype, threads=1)
+    return runner(tgt, drf, tok, U, T, dtype)
 
 
-def outcome_law(target, draft, tokens, T=1.0, dtype="f32"):
+def outcome_law(target, draft, tokens, T=1.0, dtype="f32", rule="chain"):
     """Return {(k, token): probability} for one block.
 
-    target [gamma+1, V], draft [gamma, V] (stored dtype), tokens [gamma].
+    target [gamma+1, V], draft [gamma, V] (stored dtype; ignored by the
+    point-mass rule), tokens [gamma]; rule "chain" (ratio test against the
+    draft distribution) or "pointmass" (the draft proposes each token with
+    certainty).
     """
+    runner = RUNNERS[rule]
     target = np.asarray(target)
     draft = np.asarray(draft)
     tokens = np.asarray(tokens, dtype=np.int32)
@@ -44,13 +59,13 @@ def outcome_law(target, draft, tokens, T=1.0, dtype="f32"):
     hi = np.ones(g)
     U0 = np.zeros((g, g + 1))
     U0[np.arange(g), np.arange(g)] = 0.0
-    first = _run(target, draft, tokens, U0, T, dtype)["accept_len"]
+    first = _run(target, draft, tokens, U0, T, dtype, runner)["accept_len"]
     passes0 = first > np.arange(g)
     for _ in range(STEPS):
         mid = 0.5 * (lo + hi)
         U = np.zeros((g, g + 1))
         U[np.arange(g), np.arange(g)] = mid
-        acc = _run(target, draft, tokens, U, T, dtype)["accept_len"]
+        acc = _run(target, draft, tokens, U, T, dtype, runner)["accept_len"]
         ok = acc > np.arange(g)
         lo = np.where(ok, mid, lo)
         hi = np.where(ok, hi, mid)
@@ -77,7 +92,7 @@ def outcome_law(target, draft, tokens, T=1.0, dtype="f32"):
     def token_at(u):
         U = base.copy()
         U[:, g] = u
-        res = _run(target, draft, tokens, U, T, dtype)
+        res = _run(target, draft, tokens, U, T, dtype, runner)
         assert np.array_equal(res["accept_len"], kk), "forced outcome k not reached"
         return res["out_tokens"][np.arange(n), kk]
 
