@@ -104,11 +104,18 @@ class Workload:
         import synth
 
         self.cfg = cfg
-        self.spec = dict(synth.CONFIGS[cfg])
+        if isinstance(cfg, str) and cfg.startswith("pm"):
+            base = int(cfg[2:])
+            self.spec = dict(synth.POINTMASS_CONFIGS[base], kind="pointmass")
+            self.bytes = synth.pointmass_config_bytes(base)
+            t0 = time.time()
+            d = synth.pointmass_config_inputs(base, seed=seed)
+        else:
+            self.spec = dict(synth.CONFIGS[cfg])
+            self.bytes = synth.config_bytes(cfg)
+            t0 = time.time()
+            d = synth.config_inputs(cfg, seed=seed)
         self.kind = self.spec["kind"]
-        self.bytes = synth.config_bytes(cfg)
-        t0 = time.time()
-        d = synth.config_inputs(cfg, seed=seed)
         log(f"[bench] config {cfg}: inputs drawn in {time.time() - t0:.1f}s")
         self.host = d
         self.nsets = max(2, math.ceil(CACHE_BYTES / self.bytes))
@@ -123,7 +130,26 @@ class Workload:
         self.lib = sv.load_library()
         self.code = sv.SV_DTYPE_F32 if dt == "f32" else sv.SV_DTYPE_BF16
         P = ctypes.c_void_p
-        if self.kind == "chain":
+        if self.kind == "pointmass":
+            B, g, V = d["B"], d["gamma"], d["V"]
+            t0g = logits(d["target"])
+            tok = torch.from_numpy(d["draft_tokens"]).to(dev)
+            uni = torch.from_numpy(d["uniforms"]).to(dev)
+            self.sets = []
+            for i in range(self.nsets):
+                tg = t0g if i == 0 else t0g.clone()
+                acc = torch.empty(B, dtype=torch.int32, device=dev)
+                out = torch.empty((B, g + 1), dtype=torch.int32, device=dev)
+                self.sets.append((tg, tok, uni, acc, out))
+            nbytes = sv.spec_verify_chain_pointmass_workspace_bytes(B, g, V, self.code)
+            self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+            self.args = [(P(tg.data_ptr()), self.code, P(tk.data_ptr()), P(un.data_ptr()), B, g, V,
+                          float(d["T"]), P(ac.data_ptr()), P(ou.data_ptr()), None,
+                          P(self.ws.data_ptr()), nbytes)
+                         for tg, tk, un, ac, ou in self.sets]
+            self.n_events = 3
+            self.shape = dict(B=B, gamma=g, V=V)
+        elif self.kind == "chain":
             B, g, V = d["B"], d["gamma"], d["V"]
             t0g, d0g = logits(d["target"]), logits(d["draft"])
             tok = torch.from_numpy(d["draft_tokens"]).to(dev)
@@ -173,6 +199,8 @@ class Workload:
             ev = ctypes.cast(arr, ctypes.c_void_p)
         if self.kind == "chain":
             st = self.lib.spec_verify_chain(*a, stream_handle, ev)
+        elif self.kind == "pointmass":
+            st = self.lib.spec_verify_chain_pointmass(*a, stream_handle, ev)
         else:
             st = self.lib.spec_verify_tree_greedy(*a, stream_handle, ev)
         if st != 0:
@@ -183,6 +211,12 @@ class Workload:
 
     def describe(self):
         s = self.spec
+        if self.kind == "pointmass":
+            tgt = f"{s['target'][0]}x{s['target'][1]}"
+            extra = f", +{s['boost'][1]:g} on {s['boost'][0]} ids/row" if s.get("boost") else ""
+            return (f"point-mass chain verify B={s['B']} gamma={s['gamma']} V={s['V']} "
+                    f"{s['dtype']} T={s['T']} (target {tgt}{extra}; draft token = target "
+                    f"argmax w.p. {s['p_match']} else uniform; no draft logits; seeded uniforms)")
         if self.kind == "chain":
             tgt = f"{s['target'][0]}x{s['target'][1]}"
             extra = f", +{s['boost'][1]:g} on {s['boost'][0]} ids/row" if s.get("boost") else ""
@@ -294,8 +328,9 @@ def main():
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default: about 0.2 s of GPU time)")
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=HEADLINE_CFG,
-                    help="workload for the headline line (1-5)")
+    ap.add_argument("--config", type=str, default=str(HEADLINE_CFG),
+                    help="workload for the headline line (1-5, or pm3 / pm5 for the point-mass "
+                         "workloads with the shapes of configs 3 and 5)")
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip the other workloads in the per_config field")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -318,18 +353,20 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     hip = HipEvents()
-    default_steps = {1: 2000, 2: 2000, 3: 200, 4: 100, 5: 50}
+    default_steps = {1: 2000, 2: 2000, 3: 200, 4: 100, 5: 50, "pm3": 200, "pm5": 50}
+    cfg_arg = int(args.config) if args.config.isdigit() else args.config
 
     def run(cfg, steps):
-        w = Workload(cfg, seed=1000 * cfg + 7, torch=torch, sv=sv)
+        seed = 1000 * int(cfg[2:]) + 77 if isinstance(cfg, str) else 1000 * cfg + 7
+        w = Workload(cfg, seed=seed, torch=torch, sv=sv)
         k = steps or default_steps[cfg]
         r = measure(w, k, args.warmup, torch, hip)
         log(f"[bench] config {cfg}: {r['gbps']:.1f} GB/s over {k} steps, "
             f"{r['ms_per_step'] * 1e3:.2f} us/step; dominant kernel {r['dominant_ms'] * 1e3:.2f} us")
         return w, k, r
 
-    w, K, r = run(args.config, args.steps)
-    kernel = ("chain_stats_kernel" if w.kind == "chain" else "tree_kernel") + \
+    w, K, r = run(cfg_arg, args.steps)
+    kernel = ("tree_argmax_kernel" if w.kind == "tree" else "chain_stats_kernel") + \
         ("<F32>" if w.spec["dtype"] == "f32" else "<BF16>")
     traffic = measured_traffic(f"{kernel} config{args.config}")
     line = {
@@ -345,7 +382,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.spec["dtype"],
         "data": "synthetic",
-        "config": {"workload": w.describe(), **w.shape, "config_index": args.config,
+        "config": {"workload": w.describe(), **w.shape, "config_index": cfg_arg,
                    "bytes_per_step": w.bytes, "input_sets": w.nsets, "timing": "hip graph replay"},
         "pct_peak": round(100.0 * r["gbps"] / PEAK_GBPS, 2),
         "rounds_per_s": round(r["rounds_per_s"], 1),
@@ -363,8 +400,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_per_config:
         per = {}
-        for cfg in (3, 4, 5):
-            if cfg == args.config:
+        for cfg in (3, 4, 5, "pm3", "pm5"):
+            if cfg == cfg_arg:
                 continue
             try:
                 wc, kc, rc = run(cfg, None)

@@ -9,6 +9,7 @@ library's HIP kernels; there is no CPU path.
 
 Entry points (same names as the C ABI):
   spec_verify_chain(target, draft, draft_tokens, uniforms, temperature, ...)
+  spec_verify_chain_pointmass(target, draft_tokens, uniforms, temperature, ...)
   spec_verify_tree_greedy(target, parents, tokens, ...)
 """
 from __future__ import annotations
@@ -19,6 +20,7 @@ import os as _os
 __all__ = [
     "SV_DTYPE_F32", "SV_DTYPE_BF16", "SpecVerifyError", "library_path", "load_library",
     "spec_verify_chain", "spec_verify_tree_greedy", "spec_verify_chain_workspace_bytes",
+    "spec_verify_chain_pointmass", "spec_verify_chain_pointmass_workspace_bytes",
     "spec_verify_tree_greedy_workspace_bytes", "spec_verify_status_string",
 ]
 
@@ -66,6 +68,10 @@ def load_library():
     lib.spec_verify_tree_greedy_workspace_bytes.restype = SZ
     lib.spec_verify_chain.argtypes = [P, P, I32, P, P, I32, I32, I32, D, P, P, P, P, SZ, P, P]
     lib.spec_verify_chain.restype = I32
+    lib.spec_verify_chain_pointmass_workspace_bytes.argtypes = [I32, I32, I32, I32]
+    lib.spec_verify_chain_pointmass_workspace_bytes.restype = SZ
+    lib.spec_verify_chain_pointmass.argtypes = [P, I32, P, P, I32, I32, I32, D, P, P, P, P, SZ, P, P]
+    lib.spec_verify_chain_pointmass.restype = I32
     lib.spec_verify_tree_greedy.argtypes = [P, I32, P, P, I32, I32, I32, P, P, P, P, SZ, P, P]
     lib.spec_verify_tree_greedy.restype = I32
     _lib = lib
@@ -78,6 +84,10 @@ def spec_verify_status_string(status: int) -> str:
 
 def spec_verify_chain_workspace_bytes(B: int, gamma: int, V: int, dtype: int) -> int:
     return int(load_library().spec_verify_chain_workspace_bytes(B, gamma, V, dtype))
+
+
+def spec_verify_chain_pointmass_workspace_bytes(B: int, gamma: int, V: int, dtype: int) -> int:
+    return int(load_library().spec_verify_chain_pointmass_workspace_bytes(B, gamma, V, dtype))
 
 
 def spec_verify_tree_greedy_workspace_bytes(B: int, n: int, V: int, dtype: int) -> int:
@@ -196,6 +206,52 @@ def spec_verify_chain(target, draft, draft_tokens, uniforms, temperature, *, acc
                                _stream_handle(stream, dev), None if ev is None else ev[0])
     if st != 0:
         raise SpecVerifyError(st, "spec_verify_chain")
+    return accept_len, out_tokens, final_dist
+
+
+def spec_verify_chain_pointmass(target, draft_tokens, uniforms, temperature, *, accept_len=None,
+                                out_tokens=None, final_dist=None, want_dist=False,
+                                workspace=None, stream=None, phase_events=None):
+    """Point-mass chain verification on the GPU (no draft logits).
+
+    target [B, gamma+1, V] (float32 or bfloat16), draft_tokens int32
+    [B, gamma], uniforms float32 [B, gamma+1], temperature > 0.  Returns
+    (accept_len [B], out_tokens [B, gamma+1], final_dist [B, V] or None)."""
+    torch = _torch()
+    lib = load_library()
+    if target.dim() != 3:
+        raise ValueError("target must be [B, gamma+1, V]")
+    B, g1, V = target.shape
+    g = g1 - 1
+    dev = target.device
+    code = _dtype_code(target)
+    _check(target, "target", (B, g1, V), device=dev)
+    _check(draft_tokens, "draft_tokens", (B, g), dtype=torch.int32, device=dev)
+    _check(uniforms, "uniforms", (B, g1), dtype=torch.float32, device=dev)
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, g1), dtype=torch.int32, device=dev)
+    if final_dist is None and want_dist:
+        final_dist = torch.empty((B, V), dtype=torch.float32, device=dev)
+    _check(accept_len, "accept_len", (B,), dtype=torch.int32, device=dev)
+    _check(out_tokens, "out_tokens", (B, g1), dtype=torch.int32, device=dev)
+    if final_dist is not None:
+        _check(final_dist, "final_dist", (B, V), dtype=torch.float32, device=dev)
+    need = spec_verify_chain_pointmass_workspace_bytes(B, g, V, code)
+    if need == 0:
+        raise SpecVerifyError(2, "spec_verify_chain_pointmass")
+    if workspace is None:
+        workspace = _workspace(need, dev, stream)
+    ev = _events(phase_events)
+    st = lib.spec_verify_chain_pointmass(_ptr(target), code, _ptr(draft_tokens), _ptr(uniforms),
+                                         B, g, V, float(temperature), _ptr(accept_len),
+                                         _ptr(out_tokens), _ptr(final_dist), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(),
+                                         _stream_handle(stream, dev),
+                                         None if ev is None else ev[0])
+    if st != 0:
+        raise SpecVerifyError(st, "spec_verify_chain_pointmass")
     return accept_len, out_tokens, final_dist
 
 

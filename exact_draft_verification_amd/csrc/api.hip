@@ -52,11 +52,14 @@ size_t carve(size_t* off, size_t size, size_t n) {
     return at;
 }
 
-int32_t chain_plan(int32_t B, int32_t gamma, int32_t V, int32_t dtype, ChainPlan* p) {
+// Plan of a chain call: rows per block are 2*gamma+1 (target and draft
+// logits) for the ratio test, gamma+1 (target only) for a point-mass draft.
+int32_t chain_plan(int32_t B, int32_t gamma, int32_t V, int32_t dtype, bool pointmass,
+                   ChainPlan* p) {
     if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
     if (B < 1 || gamma < 1 || V < 1 || gamma > kMaxGamma) return SV_ERR_SHAPE;
     const int E = elem_bytes(dtype), epv = 16 / E;
-    const int64_t rows = 2 * static_cast<int64_t>(gamma) + 1;
+    const int64_t rows = (pointmass ? 1 : 2) * static_cast<int64_t>(gamma) + 1;
     const int64_t rows_total = static_cast<int64_t>(B) * rows;
     // every element index and byte offset must fit comfortably in int64, and
     // grid sizes in int32
@@ -141,7 +144,13 @@ extern "C" const char* spec_verify_status_string(int32_t status) {
 extern "C" size_t spec_verify_chain_workspace_bytes(int32_t B, int32_t gamma, int32_t V,
                                                     int32_t dtype) {
     ChainPlan p;
-    return chain_plan(B, gamma, V, dtype, &p) == SV_OK ? p.bytes : 0;
+    return chain_plan(B, gamma, V, dtype, false, &p) == SV_OK ? p.bytes : 0;
+}
+
+extern "C" size_t spec_verify_chain_pointmass_workspace_bytes(int32_t B, int32_t gamma, int32_t V,
+                                                              int32_t dtype) {
+    ChainPlan p;
+    return chain_plan(B, gamma, V, dtype, true, &p) == SV_OK ? p.bytes : 0;
 }
 
 extern "C" size_t spec_verify_tree_greedy_workspace_bytes(int32_t B, int32_t n, int32_t V,
@@ -150,23 +159,27 @@ extern "C" size_t spec_verify_tree_greedy_workspace_bytes(int32_t B, int32_t n, 
     return tree_plan(B, n, V, dtype, &p) == SV_OK ? p.bytes : 0;
 }
 
-extern "C" int32_t spec_verify_chain(const void* target_logits, const void* draft_logits,
-                                     int32_t dtype, const int32_t* draft_tokens,
-                                     const float* uniforms, int32_t B, int32_t gamma, int32_t V,
-                                     double temperature, int32_t* accept_len,
-                                     int32_t* out_tokens, float* final_dist, void* workspace,
-                                     size_t workspace_bytes, void* stream,
-                                     void* const* phase_events) {
+namespace sv {
+namespace {
+
+// Both chain entry points: validation, workspace layout and the launches.
+// draft_logits is null exactly when `pointmass`.
+int32_t chain_call(const void* target_logits, const void* draft_logits, bool pointmass,
+                   int32_t dtype, const int32_t* draft_tokens, const float* uniforms, int32_t B,
+                   int32_t gamma, int32_t V, double temperature, int32_t* accept_len,
+                   int32_t* out_tokens, float* final_dist, void* workspace,
+                   size_t workspace_bytes, void* stream, void* const* phase_events) {
     ChainPlan p;
-    int32_t st = chain_plan(B, gamma, V, dtype, &p);
+    int32_t st = chain_plan(B, gamma, V, dtype, pointmass, &p);
     if (st != SV_OK) return st;
-    if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !accept_len ||
-        !out_tokens || !workspace)
+    if (!target_logits || (!pointmass && !draft_logits) || !draft_tokens || !uniforms ||
+        !accept_len || !out_tokens || !workspace)
         return SV_ERR_NULL;
     if (!std::isfinite(temperature) || temperature < 1e-6 || temperature > 1e6)
         return SV_ERR_TEMPERATURE;
     const size_t E = static_cast<size_t>(elem_bytes(dtype));
-    if (!aligned(target_logits, E) || !aligned(draft_logits, E) || !aligned(draft_tokens, 4) ||
+    if (!aligned(target_logits, E) || (!pointmass && !aligned(draft_logits, E)) ||
+        !aligned(draft_tokens, 4) ||
         !aligned(uniforms, 4) || !aligned(accept_len, 4) || !aligned(out_tokens, 4) ||
         (final_dist && !aligned(final_dist, 4)))
         return SV_ERR_ALIGN;
@@ -180,6 +193,8 @@ extern "C" int32_t spec_verify_chain(const void* target_logits, const void* draf
     a.B = B;
     a.gamma = gamma;
     a.V = V;
+    a.pointmass = pointmass ? 1 : 0;
+    a.rows = p.rows;
     // log2(e)/T as c_hi + c_lo with c_hi the largest float strictly below c,
     // so c_lo > 0: a -inf logit then scales to -inf in both parts and never
     // meets +inf (which would give NaN) when the two products are added.
@@ -214,6 +229,34 @@ extern "C" int32_t spec_verify_chain(const void* target_logits, const void* draf
     if (record(phase_events, 2, s) != SV_OK) return SV_ERR_HIP;
     if (final_dist && launch_chain_dist(a, dtype, s) != hipSuccess) return SV_ERR_HIP;
     return SV_OK;
+}
+
+}  // namespace
+}  // namespace sv
+
+extern "C" int32_t spec_verify_chain(const void* target_logits, const void* draft_logits,
+                                     int32_t dtype, const int32_t* draft_tokens,
+                                     const float* uniforms, int32_t B, int32_t gamma, int32_t V,
+                                     double temperature, int32_t* accept_len,
+                                     int32_t* out_tokens, float* final_dist, void* workspace,
+                                     size_t workspace_bytes, void* stream,
+                                     void* const* phase_events) {
+    return chain_call(target_logits, draft_logits, false, dtype, draft_tokens, uniforms, B, gamma,
+                      V, temperature, accept_len, out_tokens, final_dist, workspace,
+                      workspace_bytes, stream, phase_events);
+}
+
+extern "C" int32_t spec_verify_chain_pointmass(const void* target_logits, int32_t dtype,
+                                               const int32_t* draft_tokens,
+                                               const float* uniforms, int32_t B, int32_t gamma,
+                                               int32_t V, double temperature,
+                                               int32_t* accept_len, int32_t* out_tokens,
+                                               float* final_dist, void* workspace,
+                                               size_t workspace_bytes, void* stream,
+                                               void* const* phase_events) {
+    return chain_call(target_logits, nullptr, true, dtype, draft_tokens, uniforms, B, gamma, V,
+                      temperature, accept_len, out_tokens, final_dist, workspace,
+                      workspace_bytes, stream, phase_events);
 }
 
 extern "C" int32_t spec_verify_tree_greedy(const void* target_logits, int32_t dtype,

@@ -89,7 +89,7 @@ __device__ inline Stat row_range_stats(const typename E::storage* row, int e0, i
 template <class E, int U>
 __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
     __shared__ Stat s_w[kWaves];
-    const int rows = 2 * a.gamma + 1;
+    const int rows = a.rows;
     const int unit = blockIdx.x;
     const int seg = unit % a.nseg;
     const int rr = unit / a.nseg;  // b * rows + rho
@@ -132,9 +132,10 @@ template <class E>
 __device__ ChainDecision chain_decide(const ChainArgs& a, int b, Stat* s_part) {
     __shared__ double s_L[2 * kMaxGamma + 1];
     __shared__ float s_R[2 * kMaxGamma + 1];
+    __shared__ int s_x[kMaxGamma];
     __shared__ int s_bad, s_k;
     constexpr int kPer = kMaxBlockParts / kThreads;
-    const int g = a.gamma, rows = 2 * g + 1, tid = threadIdx.x;
+    const int g = a.gamma, rows = a.rows, tid = threadIdx.x;
     const int np = rows * a.nseg;
     // per-position inputs (gamma <= 255 < kThreads: one position per thread)
     int x = 0;
@@ -142,8 +143,9 @@ __device__ ChainDecision chain_decide(const ChainArgs& a, int b, Stat* s_part) {
     if (tid < g) {
         x = a.tokens[static_cast<int64_t>(b) * g + tid];
         zp = a.zx[static_cast<int64_t>(b) * rows + tid];
-        zq = a.zx[static_cast<int64_t>(b) * rows + g + 1 + tid];
+        if (!a.pointmass) zq = a.zx[static_cast<int64_t>(b) * rows + g + 1 + tid];
         u = a.uniforms[static_cast<int64_t>(b) * (g + 1) + tid];
+        s_x[tid] = x;
     }
     {
         // every load issued before any LDS store; a Stat is one 16-byte
@@ -191,6 +193,10 @@ __device__ ChainDecision chain_decide(const ChainArgs& a, int b, Stat* s_part) {
             double r;
             if (zp == -INFINITY) {
                 r = 0.0;
+            } else if (a.pointmass) {
+                // the draft proposes x with certainty: r = p(x) = 2^(log2 p(x))
+                const double d = static_cast<double>(zp) * a.c_d - s_L[tid];
+                r = d >= 0.0 ? 1.0 : exp2(d);
             } else if (zq == -INFINITY) {
                 r = 1.0;
             } else {
@@ -204,15 +210,20 @@ __device__ ChainDecision chain_decide(const ChainArgs& a, int b, Stat* s_part) {
     }
     __syncthreads();
     ChainDecision d;
+    d.pad = 0;
     if (s_bad) {
         d.k = -1;
         d.Rp = 0.0f;
         d.dL = 0.0;
+        d.excl = -1;
     } else {
         const int k = s_k;
         d.k = k;
         d.Rp = s_R[k];
-        d.dL = k < g ? s_L[k] - s_L[g + 1 + k] : 0.0;
+        // ratio test: the residual needs the row pair's log-normaliser gap;
+        // point mass: the residual is p_k without the rejected token
+        d.dL = (k < g && !a.pointmass) ? s_L[k] - s_L[g + 1 + k] : 0.0;
+        d.excl = (k < g && a.pointmass) ? s_x[k] : -1;
     }
     return d;
 }
@@ -234,6 +245,7 @@ struct DrawRow {
     float dL_hi, dL_lo;  // dL as a float pair
     double c_d, dL;
     bool resid;  // residual of p_k and q_k (else p_k itself, unnormalised)
+    int excl;    // a token whose weight is 0 (point mass: the rejected one), or -1
 };
 
 // D(v) = log2 p_k(v) - log2 q_k(v) = (z_p - z_q) c - dL.  bf16 logits: the
@@ -307,7 +319,7 @@ __device__ inline FinalRows<E> final_rows(const ChainArgs& a, int b, int k) {
     using S = typename E::storage;
     FinalRows<E> f;
     f.p = static_cast<const S*>(a.target) + (static_cast<int64_t>(b) * (a.gamma + 1) + k) * a.V;
-    f.q = k < a.gamma
+    f.q = (k < a.gamma && !a.pointmass)
               ? static_cast<const S*>(a.draft) + (static_cast<int64_t>(b) * a.gamma + k) * a.V
               : nullptr;
     f.vec_ok = (reinterpret_cast<uintptr_t>(f.p) & 15u) == 0 &&
@@ -315,10 +327,14 @@ __device__ inline FinalRows<E> final_rows(const ChainArgs& a, int b, int k) {
     return f;
 }
 
-__device__ inline DrawRow draw_row(const ChainArgs& a, const ChainDecision& d, bool resid) {
+// The draw of block b: the residual of p_k and q_k after a rejection under
+// the ratio test; p_k without the rejected token under point mass; p_gamma
+// after a fully accepted block.
+__device__ inline DrawRow draw_row(const ChainArgs& a, const ChainDecision& d) {
     const float dL_hi = static_cast<float>(d.dL);
     const float dL_lo = static_cast<float>(d.dL - static_cast<double>(dL_hi));
-    return DrawRow{d.Rp, a.c_hi, a.c_lo, dL_hi, dL_lo, a.c_d, d.dL, resid};
+    const bool resid = d.k < a.gamma && !a.pointmass;
+    return DrawRow{d.Rp, a.c_hi, a.c_lo, dL_hi, dL_lo, a.c_d, d.dL, resid, d.excl};
 }
 
 // The kPerVec tokens [e, e + kPerVec) of the final row(s) as floats: one
@@ -348,19 +364,23 @@ __device__ inline void load_tokens(const FinalRows<E>& rows, bool resid, int e, 
 // the very value the quarter sums were built from).  The residual/bonus
 // choice is taken once here, outside the per-token code.
 template <class E, bool RESID>
-__device__ inline float lane_weights_t(const float* zp, const float* zq, const DrawRow& r, float* w) {
+__device__ inline float lane_weights_t(const float* zp, const float* zq, const DrawRow& r, int e,
+                                       float* w) {
     float s = 0.0f;
 #pragma unroll
     for (int i = 0; i < E::kPerVec; ++i) {
-        w[i] = draw_weight<E, RESID>(zp[i], zq[i], r);
+        w[i] = e + i == r.excl ? 0.0f : draw_weight<E, RESID>(zp[i], zq[i], r);
         s += w[i];
     }
     return s;
 }
 
+// Weights of the lane's kPerVec tokens [e, e + kPerVec) and their sum.
 template <class E>
-__device__ inline float lane_weights(const float* zp, const float* zq, const DrawRow& r, float* w) {
-    return r.resid ? lane_weights_t<E, true>(zp, zq, r, w) : lane_weights_t<E, false>(zp, zq, r, w);
+__device__ inline float lane_weights(const float* zp, const float* zq, const DrawRow& r, int e,
+                                     float* w) {
+    return r.resid ? lane_weights_t<E, true>(zp, zq, r, e, w)
+                   : lane_weights_t<E, false>(zp, zq, r, e, w);
 }
 
 __device__ inline double wave_sum(double v) {
@@ -417,7 +437,7 @@ __global__ __launch_bounds__(kThreads) void chain_chunks_kernel(ChainArgs a) {
     if (c == 0 && tid == 0) a.dec[b] = d;
     if (d.k < 0) return;  // invalid block: the select kernel writes -1s
     const FinalRows<E> rows = final_rows<E>(a, b, d.k);
-    const DrawRow r = draw_row(a, d, d.k < a.gamma);
+    const DrawRow r = draw_row(a, d);
     const int ntile = (a.V + kTile - 1) / kTile;
     // a tile past the row's end reads as -inf (weight 0) without a load
     float zp[TILES][E::kPerVec], zq[TILES][E::kPerVec];
@@ -431,7 +451,8 @@ __global__ __launch_bounds__(kThreads) void chain_chunks_kernel(ChainArgs a) {
     for (int m = 0; m < TILES; ++m) {
         const int j = c * TILES + m;
         float w[E::kPerVec];
-        const double sw = wave_sum(static_cast<double>(lane_weights<E>(zp[m], zq[m], r, w)));
+        const int e = j * kTile + tid * E::kPerVec;
+        const double sw = wave_sum(static_cast<double>(lane_weights<E>(zp[m], zq[m], r, e, w)));
         const int qi = j * kWaves + wave;
         if (lane == 0 && j < ntile && qi < a.nquart) qs[qi] = sw;
     }
@@ -474,18 +495,20 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
     for (int j = 0; j < kRun; ++j) mine += run_v[j];
     for (int q = q0 + kRun; q < q1; ++q) mine += qs[q];
     int fallback = 0;
-    DrawRow r = draw_row(a, d, d.k < g);
-    if (r.resid && !(wave_sum(mine) > 0.0)) {
+    DrawRow r = draw_row(a, d);
+    if ((r.resid || r.excl >= 0) && !(wave_sum(mine) > 0.0)) {
         fallback = 1;
         r.resid = false;
+        r.excl = -1;
         // quarter sums of p_k, each by one lane, in the chunk kernel's order
         mine = 0.0;
         for (int q = q0; q < q1; ++q) {
             double sq = 0.0;
             for (int l = 0; l < 64; ++l) {
                 float zp[E::kPerVec], zq[E::kPerVec], w[E::kPerVec];
-                load_tokens<E>(rows, false, q * kQuart + l * E::kPerVec, a.V, zp, zq);
-                sq += static_cast<double>(lane_weights<E>(zp, zq, r, w));
+                const int e = q * kQuart + l * E::kPerVec;
+                load_tokens<E>(rows, false, e, a.V, zp, zq);
+                sq += static_cast<double>(lane_weights<E>(zp, zq, r, e, w));
             }
             qs[q] = sq;
             mine += sq;
@@ -574,7 +597,7 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
     const int e0 = qstar * kQuart + lane * E::kPerVec;
     float zp[E::kPerVec], zq[E::kPerVec], w[E::kPerVec];
     load_tokens<E>(rows, r.resid, e0, a.V, zp, zq);
-    const float lsum = lane_weights<E>(zp, zq, r, w);
+    const float lsum = lane_weights<E>(zp, zq, r, e0, w);
     double qtot;
     const double lbase = base + wave_exclusive_scan(static_cast<double>(lsum), &qtot);
     int found = INT32_MAX, lastpos = -1;
@@ -612,12 +635,17 @@ __global__ __launch_bounds__(kThreads) void chain_dist_kernel(ChainArgs a) {
     }
     const FinalState f = a.fin[b];
     const FinalRows<E> rows = final_rows<E>(a, b, d.k);
-    const DrawRow r = draw_row(a, d, d.k < a.gamma && !f.fallback);
+    DrawRow r = draw_row(a, d);
+    if (f.fallback) {
+        r.resid = false;
+        r.excl = -1;
+    }
     const double inv = 1.0 / f.W;
     for (int e = threadIdx.x; e < a.V; e += kThreads) {
         const float zp = E::one(rows.p + e);
-        const float w = r.resid ? draw_weight<E, true>(zp, E::one(rows.q + e), r)
-                                : draw_weight<E, false>(zp, 0.0f, r);
+        float w = r.resid ? draw_weight<E, true>(zp, E::one(rows.q + e), r)
+                          : draw_weight<E, false>(zp, 0.0f, r);
+        if (e == r.excl) w = 0.0f;
         out[e] = static_cast<float>(static_cast<double>(w) * inv);
     }
 }
@@ -626,7 +654,7 @@ __global__ __launch_bounds__(kThreads) void chain_dist_kernel(ChainArgs a) {
 
 hipError_t launch_chain_stats(const ChainArgs& a, int dtype, hipStream_t s, hipEvent_t ev_start,
                               hipEvent_t ev_stop) {
-    const dim3 grid(a.B * (2 * a.gamma + 1) * a.nseg);
+    const dim3 grid(a.B * a.rows * a.nseg);
     // 8 vectors per thread per batch once a segment holds two such batches,
     // else 4 (a short segment would mostly re-read its last vector)
     const bool deep = a.seg_len / (kThreads * (dtype == 0 ? 4 : 8)) >= 16;
@@ -639,7 +667,7 @@ hipError_t launch_chain_stats(const ChainArgs& a, int dtype, hipStream_t s, hipE
 
 hipError_t launch_chain_chunks(const ChainArgs& a, int dtype, hipStream_t s) {
     const dim3 grid(a.B * a.nchunk);
-    const size_t lds = sizeof(Stat) * static_cast<size_t>(2 * a.gamma + 1) * a.nseg;
+    const size_t lds = sizeof(Stat) * static_cast<size_t>(a.rows) * a.nseg;
     auto go = [&](auto kernel) {
         hipLaunchKernelGGL(kernel, grid, dim3(kThreads), lds, s, a);
         return hipGetLastError();

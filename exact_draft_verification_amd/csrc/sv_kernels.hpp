@@ -28,9 +28,11 @@ struct Stat {
 
 // Outcome of the ratio tests of one chain block.
 struct ChainDecision {
-    int32_t k;   // first rejected position, gamma if none, -1 if the block is invalid
-    float Rp;    // integer reference R of target row k
-    double dL;   // (R_p + log2 S_p) - (R_q + log2 S_q) at row k (k < gamma), else 0
+    int32_t k;     // first rejected position, gamma if none, -1 if the block is invalid
+    float Rp;      // integer reference R of target row k
+    double dL;     // (R_p + log2 S_p) - (R_q + log2 S_q) at row k (ratio test, k < gamma), else 0
+    int32_t excl;  // point mass, k < gamma: the rejected draft token (weight 0 in the draw); else -1
+    int32_t pad;
 };
 
 // Normaliser of the final draw of one block, kept for the final_dist pass.
@@ -46,6 +48,8 @@ struct ChainArgs {
     const int32_t* tokens;
     const float* uniforms;
     int B, gamma, V;
+    int pointmass;     // 1: the draft proposes each token with certainty (no draft logits)
+    int rows;          // logit rows per block: 2*gamma+1 (target and draft), or gamma+1
     float c_hi, c_lo;  // log2(e)/T as a float pair
     double c_d;        // c_hi + c_lo exactly
     double T;
@@ -54,8 +58,8 @@ struct ChainArgs {
     int chunk_tiles;        // final draw: tiles (one 16-byte vector per thread) per chunk
                             // workgroup: 1, 2 or 4
     int nquart;             // final draw: quarters (64 16-byte vectors) per row
-    Stat* part;             // [B][2*gamma+1][nseg]
-    float* zx;              // [B][2*gamma+1]: logit of the draft token in rows i < gamma
+    Stat* part;             // [B][rows][nseg]
+    float* zx;              // [B][rows]: logit of the draft token in rows i < gamma
                             // (target) and gamma+1+i (draft); other entries unused
     ChainDecision* dec;     // [B]
     double* qsum;           // [B][nquart]: draw-weight sum per quarter

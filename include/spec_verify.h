@@ -129,6 +129,36 @@ int32_t spec_verify_chain(const void *target_logits, const void *draft_logits, i
                           int32_t *out_tokens, float *final_dist, void *workspace,
                           size_t workspace_bytes, void *stream, void *const *phase_events);
 
+/* Bytes of workspace spec_verify_chain_pointmass needs for these sizes; 0 if
+ * the sizes or dtype are invalid. */
+size_t spec_verify_chain_pointmass_workspace_bytes(int32_t B, int32_t gamma, int32_t V,
+                                                   int32_t dtype);
+
+/* Point-mass ("exact-match") chain verification: the draft proposes each
+ * token x_i with certainty (q_i is the point mass on x_i, as for a draft that
+ * emits its argmax), so no draft logits are read ("JetSpec++", Appendix F.3
+ * and Proposition 1; the worked example of Appendix F.1).  Position i passes
+ * iff u_i < p_i(x_i), left to right; after a rejection at k the extra token
+ * is drawn from p_k with x_k removed and the remainder renormalised, after a
+ * fully accepted block from the bonus row p_gamma (inverse CDF in ascending
+ * token id with u_gamma, as for spec_verify_chain).  The law of the outcome
+ * equals that of spec_verify_chain with one-hot draft logits, and so do the
+ * outputs for the same uniforms; the logits read are B*(gamma+1)*V instead
+ * of B*(2*gamma+1)*V.
+ *
+ *  target_logits  [B][gamma+1][V] dtype, as for spec_verify_chain.
+ *  draft_tokens   [B][gamma] int32: x_0 .. x_{gamma-1}.
+ *  uniforms, temperature, accept_len, out_tokens, final_dist, stream and
+ *  phase_events are as for spec_verify_chain; the workspace is sized by
+ *  spec_verify_chain_pointmass_workspace_bytes.  Data-dependent errors: a
+ *  draft token outside [0, V), or a NaN, +inf or all -inf target row. */
+int32_t spec_verify_chain_pointmass(const void *target_logits, int32_t dtype,
+                                    const int32_t *draft_tokens, const float *uniforms,
+                                    int32_t B, int32_t gamma, int32_t V, double temperature,
+                                    int32_t *accept_len, int32_t *out_tokens, float *final_dist,
+                                    void *workspace, size_t workspace_bytes, void *stream,
+                                    void *const *phase_events);
+
 /* Bytes of workspace spec_verify_tree_greedy needs; 0 if the sizes or dtype
  * are invalid. */
 size_t spec_verify_tree_greedy_workspace_bytes(int32_t B, int32_t n, int32_t V, int32_t dtype);

@@ -38,6 +38,10 @@ import numpy as np
 
 __all__ = [
     "CONFIGS",
+    "POINTMASS_CONFIGS",
+    "pointmass_inputs",
+    "pointmass_config_inputs",
+    "pointmass_config_bytes",
     "bf16_bits",
     "bf16_to_f32",
     "chain_inputs",
@@ -174,6 +178,87 @@ def chain_inputs(B: int, gamma: int, V: int, dtype: str = "f32", T: float = 1.0,
             list(ex.map(work, range(B)))
     return dict(kind="chain", target=tgt, draft=drf, draft_tokens=tok, uniforms=uni,
                 B=B, gamma=gamma, V=V, dtype=dtype, T=float(T))
+
+
+# Point-mass ("exact-match") chain workloads: the shapes and target logits of
+# chain configurations 3 and 5, no draft logits, and draft tokens that equal
+# the target row's argmax with probability p_match (a greedy draft that
+# agrees with the target most of the time), else a uniform token.
+POINTMASS_CONFIGS = {
+    3: dict(B=64, gamma=16, V=151936, dtype="bf16", T=0.7, target=("normal", 2.5),
+            boost=(5, 8.0), p_match=0.8),
+    5: dict(B=256, gamma=16, V=151936, dtype="bf16", T=0.6, target=("gumbel", 4.0),
+            boost=None, p_match=0.8),
+}
+
+
+def _pointmass_block(seed_seq, gamma, V, dtype, target, boost, p_match):
+    rng = np.random.default_rng(seed_seq)
+    kind, scale = target
+    if kind == "normal":
+        t = rng.standard_normal((gamma + 1, V), dtype=np.float32) * np.float32(scale)
+    elif kind == "gumbel":
+        t = _gumbel(rng, (gamma + 1, V)) * np.float32(scale)
+    else:
+        raise ValueError(f"unknown target distribution {kind!r}")
+    if boost is not None:
+        count, amount = boost
+        for j in range(gamma + 1):
+            ids = rng.choice(V, size=count, replace=False)
+            t[j, ids] += np.float32(amount)
+    t_st = _store(t, dtype)
+    amax = np.argmax(_as_f32(t_st, dtype)[:gamma], axis=1)
+    match = rng.random(gamma) < p_match
+    other = rng.integers(0, V, gamma)
+    tokens = np.where(match, amax, other).astype(np.int32)
+    u = rng.random(gamma + 1, dtype=np.float32)
+    return t_st, tokens, u
+
+
+def pointmass_inputs(B: int, gamma: int, V: int, dtype: str = "f32", T: float = 1.0,
+                     target=("normal", 2.0), boost=None, p_match: float = 0.8, seed: int = 0,
+                     threads: int | None = None) -> dict:
+    """Inputs for one point-mass chain call: ``target`` [B, gamma+1, V],
+    ``draft_tokens`` int32 [B, gamma] (the target row's argmax with
+    probability p_match, else uniform), ``uniforms`` float32 [B, gamma+1]."""
+    if B < 1 or gamma < 1 or V < 1:
+        raise ValueError("B, gamma and V must be >= 1")
+    st = np.uint16 if dtype == "bf16" else np.float32
+    tgt = np.empty((B, gamma + 1, V), dtype=st)
+    tok = np.empty((B, gamma), dtype=np.int32)
+    uni = np.empty((B, gamma + 1), dtype=np.float32)
+    children = np.random.SeedSequence(seed).spawn(B)
+
+    def work(b):
+        tgt[b], tok[b], uni[b] = _pointmass_block(children[b], gamma, V, dtype, target, boost,
+                                                  p_match)
+
+    nw = _workers(B, threads)
+    if nw == 1:
+        for b in range(B):
+            work(b)
+    else:
+        with _cf.ThreadPoolExecutor(nw) as ex:
+            list(ex.map(work, range(B)))
+    return dict(kind="pointmass", target=tgt, draft_tokens=tok, uniforms=uni, B=B, gamma=gamma,
+                V=V, dtype=dtype, T=float(T))
+
+
+def pointmass_config_inputs(cfg: int, seed: int = 0, threads: int | None = None,
+                            **overrides) -> dict:
+    """Inputs for a point-mass workload with the shape of chain config cfg."""
+    c = dict(POINTMASS_CONFIGS[cfg])
+    c.update(overrides)
+    return pointmass_inputs(c["B"], c["gamma"], c["V"], c["dtype"], c["T"], c["target"],
+                            c["boost"], c["p_match"], seed=seed, threads=threads)
+
+
+def pointmass_config_bytes(cfg: int, **overrides) -> int:
+    """Algorithmic logit bytes of one point-mass call: every target logit once."""
+    c = dict(POINTMASS_CONFIGS[cfg])
+    c.update(overrides)
+    e = 4 if c["dtype"] == "f32" else 2
+    return c["B"] * (c["gamma"] + 1) * c["V"] * e
 
 
 def _tree_parents(rng, n, max_depth, max_children):

@@ -62,6 +62,18 @@ def gpu_chain(d, want_dist=False, workspace=None, stream=None):
                 final_dist=None if dist is None else dist.cpu().numpy())
 
 
+def gpu_pointmass(d, want_dist=False, workspace=None, stream=None):
+    torch, sv = require_gpu()
+    tgt = to_dev_logits(d["target"], d["dtype"])
+    tok = to_dev(d["draft_tokens"], np.int32)
+    uni = to_dev(d["uniforms"], np.float32)
+    acc, out, dist = sv.spec_verify_chain_pointmass(tgt, tok, uni, d["T"], want_dist=want_dist,
+                                                    workspace=workspace, stream=stream)
+    torch.cuda.synchronize()
+    return dict(accept_len=acc.cpu().numpy(), out_tokens=out.cpu().numpy(),
+                final_dist=None if dist is None else dist.cpu().numpy())
+
+
 def gpu_tree(d, workspace=None):
     torch, sv = require_gpu()
     tgt = to_dev_logits(d["target"], d.get("dtype", "bf16"))

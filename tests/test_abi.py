@@ -38,7 +38,8 @@ def header_constants():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"spec_verify_chain", "spec_verify_tree_greedy", "spec_verify_chain_workspace_bytes",
-            "spec_verify_tree_greedy_workspace_bytes", "spec_verify_status_string"} <= set(names)
+            "spec_verify_tree_greedy_workspace_bytes", "spec_verify_status_string",
+            "spec_verify_chain_pointmass", "spec_verify_chain_pointmass_workspace_bytes"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
@@ -129,6 +130,43 @@ def test_chain_host_errors(lib):
     assert chain_call(lib, h, ws=ws_mis, wsb=1 << 15) == c["SV_ERR_WORKSPACE"]
     # nothing was written
     assert (h.acc == 0).all() and (h.out == 0).all()
+
+
+def pointmass_call(lib, h, **over):
+    args = dict(target=p(h.t), dtype=0, tok=p(h.tok), u=p(h.u), B=h.B, g=h.g, V=h.V, T=1.0,
+                acc=p(h.acc), out=p(h.out), dist=None, ws=p(h.ws_aligned), wsb=16, stream=None,
+                ev=None)
+    args.update(over)
+    return lib.spec_verify_chain_pointmass(args["target"], args["dtype"], args["tok"], args["u"],
+                                           args["B"], args["g"], args["V"], args["T"],
+                                           args["acc"], args["out"], args["dist"], args["ws"],
+                                           args["wsb"], args["stream"], args["ev"])
+
+
+def test_pointmass_host_errors(lib):
+    import exact_draft_verification_amd as sv
+
+    c = header_constants()
+    B, g, V = 2, 3, 64
+    h = HostBufs(B, g, V)
+    assert pointmass_call(lib, h, target=None) == c["SV_ERR_NULL"]
+    assert pointmass_call(lib, h, tok=None) == c["SV_ERR_NULL"]
+    assert pointmass_call(lib, h, u=None) == c["SV_ERR_NULL"]
+    assert pointmass_call(lib, h, acc=None) == c["SV_ERR_NULL"]
+    assert pointmass_call(lib, h, B=0) == c["SV_ERR_SHAPE"]
+    assert pointmass_call(lib, h, g=256) == c["SV_ERR_SHAPE"]
+    assert pointmass_call(lib, h, V=0) == c["SV_ERR_SHAPE"]
+    assert pointmass_call(lib, h, dtype=3) == c["SV_ERR_DTYPE"]
+    for T in (0.0, float("nan"), float("inf"), 1e9):
+        assert pointmass_call(lib, h, T=T) == c["SV_ERR_TEMPERATURE"], T
+    assert pointmass_call(lib, h, target=ct.c_void_p(h.t.ctypes.data + 2)) == c["SV_ERR_ALIGN"]
+    assert pointmass_call(lib, h, wsb=16) == c["SV_ERR_WORKSPACE"]
+    assert (h.acc == 0).all() and (h.out == 0).all()
+    # no draft rows: the point-mass workspace is never larger than the chain's
+    for shape in [(64, 16, 151936, 1), (1, 16, 151936, 0), (3, 255, 1000, 0)]:
+        assert 0 < sv.spec_verify_chain_pointmass_workspace_bytes(*shape) <= \
+            sv.spec_verify_chain_workspace_bytes(*shape)
+    assert sv.spec_verify_chain_pointmass_workspace_bytes(1, 256, 100, 0) == 0
 
 
 def test_tree_host_errors(lib):

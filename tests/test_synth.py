@@ -135,3 +135,16 @@ def test_tree_mask_ancestor_property():
 def test_config_bytes(cfg):
     want = {1: 36_864, 2: 20_055_552, 3: 641_777_664, 4: 1_244_659_712, 5: 2_567_110_656}
     assert synth.config_bytes(cfg) == want[cfg]
+
+
+def test_pointmass_inputs():
+    a = synth.pointmass_inputs(6, 4, 500, "bf16", T=0.7, p_match=0.8, seed=5)
+    b = synth.pointmass_inputs(6, 4, 500, "bf16", T=0.7, p_match=0.8, seed=5, threads=1)
+    for k in ("target", "draft_tokens", "uniforms"):
+        assert np.array_equal(a[k], b[k])
+    # tokens are the target row's argmax about p_match of the time
+    d = synth.pointmass_inputs(400, 4, 300, "f32", p_match=0.8, seed=6)
+    amax = np.argmax(d["target"][:, :4], axis=2)
+    rate = (d["draft_tokens"] == amax).mean()
+    assert 0.76 < rate < 0.84
+    assert synth.pointmass_config_bytes(3) == 64 * 17 * 151936 * 2
