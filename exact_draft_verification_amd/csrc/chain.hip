@@ -369,7 +369,9 @@ __device__ inline float lane_weights_t(const float* zp, const float* zq, const D
     float s = 0.0f;
 #pragma unroll
     for (int i = 0; i < E::kPerVec; ++i) {
-        w[i] = e + i == r.excl ? 0.0f : draw_weight<E, RESID>(zp[i], zq[i], r);
+        w[i] = draw_weight<E, RESID>(zp[i], zq[i], r);
+        // only a point-mass draw excludes a token; the residual never does
+        if constexpr (!RESID) w[i] = e + i == r.excl ? 0.0f : w[i];
         s += w[i];
     }
     return s;
