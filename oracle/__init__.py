@@ -56,8 +56,10 @@ def _declare(lib):
     lib.oracle_tree_greedy.argtypes = [P, I, P, P, I, I, I, P, P, P, P, I]
     lib.oracle_chain_pointmass.argtypes = [P, I, P, P, I, I, I, D, P, P, P, P, P, P, I]
     lib.oracle_chain_pointmass_du.argtypes = [P, I, P, P, I, I, I, D, P, P, P, P, P, P, I]
+    lib.oracle_outcome_topk.argtypes = [P, I, P, I, I, I, D, I, P, P, P, P, P]
     for f in (lib.oracle_chain, lib.oracle_chain_du, lib.oracle_chain_alpha,
-              lib.oracle_tree_greedy, lib.oracle_chain_pointmass, lib.oracle_chain_pointmass_du):
+              lib.oracle_tree_greedy, lib.oracle_chain_pointmass, lib.oracle_chain_pointmass_du,
+              lib.oracle_outcome_topk):
         f.restype = I
     return lib
 
@@ -152,6 +154,28 @@ def chain_pointmass(target, draft_tokens, uniforms, T, dtype="f32", want_dist=Fa
         raise ValueError(f"oracle_chain_pointmass rejected its arguments (rc={rc})")
     return dict(accept_len=acc, out_tokens=out, margin=margin, ratios=ratios, fallback=fb,
                 final_dist=dist)
+
+
+def outcome_topk(logits, draft_tokens, T, ncache, dtype="f32", want_all=False) -> dict:
+    """Outcome scores P(k, a) of a block from decoder rows [R, gamma+1, V] and
+    the cache of the ncache most probable outcomes: k, a [R, ncache] (-1 in
+    unused slots), p [R, ncache], hit [R] (the sum of the kept p; -1 for an
+    invalid request) and, if asked, every score [R, gamma+1, V]."""
+    lib = _load()
+    logits = _logits(logits, dtype)
+    R, g1, V = logits.shape
+    g = g1 - 1
+    tok = np.ascontiguousarray(draft_tokens, dtype=np.int32).reshape(R, g)
+    k = np.empty((R, ncache), np.int32)
+    a = np.empty((R, ncache), np.int32)
+    p = np.empty((R, ncache), np.float64)
+    hit = np.empty(R, np.float64)
+    allp = np.empty((R, g1, V), np.float64) if want_all else None
+    rc = lib.oracle_outcome_topk(_ptr(logits), _DT[dtype], _ptr(tok), R, g, V, float(T),
+                                 int(ncache), _ptr(k), _ptr(a), _ptr(p), _ptr(hit), _ptr(allp))
+    if rc != 0:
+        raise ValueError(f"oracle_outcome_topk rejected its arguments (rc={rc})")
+    return dict(k=k, a=a, p=p, hit=hit, all_scores=allp)
 
 
 def chain_alpha(target, draft, T, dtype="f32") -> np.ndarray:

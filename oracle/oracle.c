@@ -544,6 +544,112 @@ int oracle_chain_pointmass(const void *target, int dtype, const int32_t *draft_t
     return rc;
 }
 
+/* ------------------------------------------------- outcome scoring -- */
+
+typedef struct {
+    double p;
+    int k, a;
+} outcome;
+
+/* Descending probability; among equal probabilities the smaller k, then the
+ * smaller token id, comes first. */
+static int outcome_cmp(const void *x, const void *y)
+{
+    const outcome *a = (const outcome *)x, *b = (const outcome *)y;
+    if (a->p != b->p)
+        return a->p > b->p ? -1 : 1;
+    if (a->k != b->k)
+        return a->k < b->k ? -1 : 1;
+    return a->a < b->a ? -1 : (a->a > b->a);
+}
+
+/* Outcome scores and cache selection for R requests ([J++] Section 4.2,
+ * "Outcome Selection"; Appendix F.1 and Proposition 1).  Row j of a request
+ * (j = 0..gamma) is the decoder's estimate of the target's next-token
+ * distribution after the block's first j draft tokens, taken as a softmax at
+ * temperature T.  With p_j(x_j) the probability row j gives draft token x_j:
+ *   P(k, a) = prod_{i<k} p_i(x_i) * p_k(a)   for k < gamma and a != x_k,
+ *   P(gamma, a) = prod_{i<gamma} p_i(x_i) * p_gamma(a),
+ * the probability that verification of the block ends with k accepted tokens
+ * and extra token a.  The cache keeps the ncache most probable outcomes
+ * (ties: smaller k, then smaller a; outcomes of probability 0 are never
+ * kept, their slots hold k = a = -1 and probability 0); the hit probability
+ * is the sum of the kept probabilities.  An invalid request (a token outside
+ * [0, V), a NaN or +inf logit, a row without a finite logit, the |m|/T
+ * domain) gets k = a = -1 everywhere and hit probability -1.  all_scores
+ * (nullable, [R][gamma+1][V]) receives every P(k, a), 0 where a = x_k. */
+int oracle_outcome_topk(const void *logits, int dtype, const int32_t *draft_tokens, int R,
+                        int gamma, int V, double T, int ncache, int32_t *out_k, int32_t *out_a,
+                        double *out_p, double *hit, double *all_scores)
+{
+    if (!logits || !draft_tokens || !out_k || !out_a || !out_p || !hit)
+        return -1;
+    if (R < 1 || gamma < 1 || V < 1 || ncache < 1 || !(T > 0.0) || !isfinite(T))
+        return -1;
+    if (dtype != ORC_F32 && dtype != ORC_BF16)
+        return -1;
+    const int rows = gamma + 1;
+    const int64_t n = (int64_t)rows * V;
+    outcome *cand = malloc(sizeof(outcome) * (size_t)n);
+    double *m = malloc(sizeof(double) * (size_t)rows);
+    double *S = malloc(sizeof(double) * (size_t)rows);
+    if (!cand || !m || !S)
+        return -2;
+    for (int r = 0; r < R; ++r) {
+        const int32_t *x = draft_tokens + (int64_t)r * gamma;
+        const int64_t base = (int64_t)r * n;
+        for (int c = 0; c < ncache; ++c) {
+            out_k[(int64_t)r * ncache + c] = -1;
+            out_a[(int64_t)r * ncache + c] = -1;
+            out_p[(int64_t)r * ncache + c] = 0.0;
+        }
+        hit[r] = -1.0;
+        if (all_scores)
+            for (int64_t i = 0; i < n; ++i)
+                all_scores[base + i] = 0.0;
+        int bad = 0;
+        for (int i = 0; i < gamma; ++i)
+            bad |= (x[i] < 0 || x[i] >= V);
+        for (int j = 0; j < rows && !bad; ++j)
+            bad |= row_softmax_stats(logits, dtype, base + (int64_t)j * V, V, T, &m[j], &S[j]);
+        if (bad)
+            continue;
+        double prefix = 1.0; /* prod_{i<k} p_i(x_i) */
+        int64_t nc = 0;
+        for (int k = 0; k < rows; ++k) {
+            const int64_t row = base + (int64_t)k * V;
+            for (int a = 0; a < V; ++a) {
+                if (k < gamma && a == x[k])
+                    continue;
+                const double P = prefix * prob_at(logits, dtype, row, a, T, m[k], S[k]);
+                if (all_scores)
+                    all_scores[row + a] = P;
+                if (P > 0.0) {
+                    cand[nc].p = P;
+                    cand[nc].k = k;
+                    cand[nc].a = a;
+                    ++nc;
+                }
+            }
+            if (k < gamma)
+                prefix *= prob_at(logits, dtype, row, x[k], T, m[k], S[k]);
+        }
+        qsort(cand, (size_t)nc, sizeof(outcome), outcome_cmp);
+        double h = 0.0;
+        for (int c = 0; c < ncache && c < nc; ++c) {
+            out_k[(int64_t)r * ncache + c] = cand[c].k;
+            out_a[(int64_t)r * ncache + c] = cand[c].a;
+            out_p[(int64_t)r * ncache + c] = cand[c].p;
+            h += cand[c].p;
+        }
+        hit[r] = h;
+    }
+    free(cand);
+    free(m);
+    free(S);
+    return 0;
+}
+
 /* Per-position acceptance probability alpha_i = sum_v min(p_i(v), q_i(v)),
  * the probability that the test at position i passes when x ~ q_i
  * ([SD] "Rejection uses a residual distribution": accepted and residual
