@@ -104,7 +104,12 @@ class Workload:
         import synth
 
         self.cfg = cfg
-        if isinstance(cfg, str) and cfg.startswith("pm"):
+        if cfg == "outcome":
+            self.spec = dict(synth.OUTCOME_CONFIG, kind="outcome")
+            self.bytes = synth.outcome_config_bytes()
+            t0 = time.time()
+            d = synth.outcome_config_inputs(seed=seed)
+        elif isinstance(cfg, str) and cfg.startswith("pm"):
             base = int(cfg[2:])
             self.spec = dict(synth.POINTMASS_CONFIGS[base], kind="pointmass")
             self.bytes = synth.pointmass_config_bytes(base)
@@ -130,7 +135,27 @@ class Workload:
         self.lib = sv.load_library()
         self.code = sv.SV_DTYPE_F32 if dt == "f32" else sv.SV_DTYPE_BF16
         P = ctypes.c_void_p
-        if self.kind == "pointmass":
+        if self.kind == "outcome":
+            R, g, V, nc = d["R"], d["gamma"], d["V"], d["ncache"]
+            t0g = logits(d["target"])
+            tok = torch.from_numpy(d["draft_tokens"]).to(dev)
+            self.sets = []
+            for i in range(self.nsets):
+                lg = t0g if i == 0 else t0g.clone()
+                k = torch.empty((R, nc), dtype=torch.int32, device=dev)
+                a = torch.empty((R, nc), dtype=torch.int32, device=dev)
+                pr = torch.empty((R, nc), dtype=torch.float64, device=dev)
+                hit = torch.empty(R, dtype=torch.float64, device=dev)
+                self.sets.append((lg, tok, k, a, pr, hit))
+            nbytes = sv.spec_outcome_topk_workspace_bytes(R, g, V, self.code, nc)
+            self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+            self.args = [(P(lg.data_ptr()), self.code, P(tk.data_ptr()), R, g, V, float(d["T"]), nc,
+                          P(k_.data_ptr()), P(a_.data_ptr()), P(p_.data_ptr()), P(h_.data_ptr()),
+                          P(self.ws.data_ptr()), nbytes)
+                         for lg, tk, k_, a_, p_, h_ in self.sets]
+            self.n_events = 2
+            self.shape = dict(R=R, gamma=g, V=V, ncache=nc)
+        elif self.kind == "pointmass":
             B, g, V = d["B"], d["gamma"], d["V"]
             t0g = logits(d["target"])
             tok = torch.from_numpy(d["draft_tokens"]).to(dev)
@@ -201,6 +226,8 @@ class Workload:
             st = self.lib.spec_verify_chain(*a, stream_handle, ev)
         elif self.kind == "pointmass":
             st = self.lib.spec_verify_chain_pointmass(*a, stream_handle, ev)
+        elif self.kind == "outcome":
+            st = self.lib.spec_outcome_topk(*a, stream_handle, ev)
         else:
             st = self.lib.spec_verify_tree_greedy(*a, stream_handle, ev)
         if st != 0:
@@ -211,6 +238,10 @@ class Workload:
 
     def describe(self):
         s = self.spec
+        if self.kind == "outcome":
+            return (f"outcome scoring + cache of {s['ncache']} R={s['R']} gamma={s['gamma']} "
+                    f"V={s['V']} {s['dtype']} T={s['T']} (decoder rows {s['target'][0]}x"
+                    f"{s['target'][1]}; draft token = row argmax w.p. {s['p_match']} else uniform)")
         if self.kind == "pointmass":
             tgt = f"{s['target'][0]}x{s['target'][1]}"
             extra = f", +{s['boost'][1]:g} on {s['boost'][0]} ids/row" if s.get("boost") else ""
@@ -329,8 +360,9 @@ def main():
                     help="timed steps (default: about 0.2 s of GPU time)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=str, default=str(HEADLINE_CFG),
-                    help="workload for the headline line (1-5, or pm3 / pm5 for the point-mass "
-                         "workloads with the shapes of configs 3 and 5)")
+                    help="workload for the headline line (1-5; pm3 / pm5 for the point-mass "
+                         "workloads with the shapes of configs 3 and 5; outcome for outcome "
+                         "scoring)")
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip the other workloads in the per_config field")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -353,11 +385,15 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     hip = HipEvents()
-    default_steps = {1: 2000, 2: 2000, 3: 200, 4: 100, 5: 50, "pm3": 200, "pm5": 50}
+    default_steps = {1: 2000, 2: 2000, 3: 200, 4: 100, 5: 50, "pm3": 200, "pm5": 50,
+                     "outcome": 200}
     cfg_arg = int(args.config) if args.config.isdigit() else args.config
 
     def run(cfg, steps):
-        seed = 1000 * int(cfg[2:]) + 77 if isinstance(cfg, str) else 1000 * cfg + 7
+        if cfg == "outcome":
+            seed = 8077
+        else:
+            seed = 1000 * int(cfg[2:]) + 77 if isinstance(cfg, str) else 1000 * cfg + 7
         w = Workload(cfg, seed=seed, torch=torch, sv=sv)
         k = steps or default_steps[cfg]
         r = measure(w, k, args.warmup, torch, hip)
@@ -366,8 +402,8 @@ def main():
         return w, k, r
 
     w, K, r = run(cfg_arg, args.steps)
-    kernel = ("tree_argmax_kernel" if w.kind == "tree" else "chain_stats_kernel") + \
-        ("<F32>" if w.spec["dtype"] == "f32" else "<BF16>")
+    kernel = {"tree": "tree_argmax_kernel", "outcome": "outcome_stats_kernel"}.get(
+        w.kind, "chain_stats_kernel") + ("<F32>" if w.spec["dtype"] == "f32" else "<BF16>")
     traffic = measured_traffic(f"{kernel} config{args.config}")
     line = {
         "metric": METRIC,
@@ -400,7 +436,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_per_config:
         per = {}
-        for cfg in (3, 4, 5, "pm3", "pm5"):
+        for cfg in (3, 4, 5, "pm3", "pm5", "outcome"):
             if cfg == cfg_arg:
                 continue
             try:

@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
   spec_verify_chain(target, draft, draft_tokens, uniforms, temperature, ...)
   spec_verify_chain_pointmass(target, draft_tokens, uniforms, temperature, ...)
   spec_verify_tree_greedy(target, parents, tokens, ...)
+  spec_outcome_topk(logits, draft_tokens, temperature, ncache, ...)
 """
 from __future__ import annotations
 
@@ -21,6 +22,7 @@ __all__ = [
     "SV_DTYPE_F32", "SV_DTYPE_BF16", "SpecVerifyError", "library_path", "load_library",
     "spec_verify_chain", "spec_verify_tree_greedy", "spec_verify_chain_workspace_bytes",
     "spec_verify_chain_pointmass", "spec_verify_chain_pointmass_workspace_bytes",
+    "spec_outcome_topk", "spec_outcome_topk_workspace_bytes",
     "spec_verify_tree_greedy_workspace_bytes", "spec_verify_status_string",
 ]
 
@@ -72,6 +74,10 @@ def load_library():
     lib.spec_verify_chain_pointmass_workspace_bytes.restype = SZ
     lib.spec_verify_chain_pointmass.argtypes = [P, I32, P, P, I32, I32, I32, D, P, P, P, P, SZ, P, P]
     lib.spec_verify_chain_pointmass.restype = I32
+    lib.spec_outcome_topk_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
+    lib.spec_outcome_topk_workspace_bytes.restype = SZ
+    lib.spec_outcome_topk.argtypes = [P, I32, P, I32, I32, I32, D, I32, P, P, P, P, P, SZ, P, P]
+    lib.spec_outcome_topk.restype = I32
     lib.spec_verify_tree_greedy.argtypes = [P, I32, P, P, I32, I32, I32, P, P, P, P, SZ, P, P]
     lib.spec_verify_tree_greedy.restype = I32
     _lib = lib
@@ -88,6 +94,10 @@ def spec_verify_chain_workspace_bytes(B: int, gamma: int, V: int, dtype: int) ->
 
 def spec_verify_chain_pointmass_workspace_bytes(B: int, gamma: int, V: int, dtype: int) -> int:
     return int(load_library().spec_verify_chain_pointmass_workspace_bytes(B, gamma, V, dtype))
+
+
+def spec_outcome_topk_workspace_bytes(R: int, gamma: int, V: int, dtype: int, ncache: int) -> int:
+    return int(load_library().spec_outcome_topk_workspace_bytes(R, gamma, V, dtype, ncache))
 
 
 def spec_verify_tree_greedy_workspace_bytes(B: int, n: int, V: int, dtype: int) -> int:
@@ -253,6 +263,51 @@ def spec_verify_chain_pointmass(target, draft_tokens, uniforms, temperature, *, 
     if st != 0:
         raise SpecVerifyError(st, "spec_verify_chain_pointmass")
     return accept_len, out_tokens, final_dist
+
+
+def spec_outcome_topk(logits, draft_tokens, temperature, ncache, *, out_k=None, out_a=None,
+                      out_p=None, hit=None, workspace=None, stream=None, phase_events=None):
+    """Outcome scores and the ncache most probable outcomes on the GPU.
+
+    logits [R, gamma+1, V] (float32 or bfloat16), draft_tokens int32
+    [R, gamma].  Returns (k [R, ncache] int32, a [R, ncache] int32,
+    p [R, ncache] float64, hit [R] float64)."""
+    torch = _torch()
+    lib = load_library()
+    if logits.dim() != 3:
+        raise ValueError("logits must be [R, gamma+1, V]")
+    R, g1, V = logits.shape
+    g = g1 - 1
+    dev = logits.device
+    code = _dtype_code(logits)
+    _check(logits, "logits", (R, g1, V), device=dev)
+    _check(draft_tokens, "draft_tokens", (R, g), dtype=torch.int32, device=dev)
+    ncache = int(ncache)
+    if out_k is None:
+        out_k = torch.empty((R, ncache), dtype=torch.int32, device=dev)
+    if out_a is None:
+        out_a = torch.empty((R, ncache), dtype=torch.int32, device=dev)
+    if out_p is None:
+        out_p = torch.empty((R, ncache), dtype=torch.float64, device=dev)
+    if hit is None:
+        hit = torch.empty(R, dtype=torch.float64, device=dev)
+    _check(out_k, "out_k", (R, ncache), dtype=torch.int32, device=dev)
+    _check(out_a, "out_a", (R, ncache), dtype=torch.int32, device=dev)
+    _check(out_p, "out_p", (R, ncache), dtype=torch.float64, device=dev)
+    _check(hit, "hit", (R,), dtype=torch.float64, device=dev)
+    need = spec_outcome_topk_workspace_bytes(R, g, V, code, ncache)
+    if need == 0:
+        raise SpecVerifyError(2, "spec_outcome_topk")
+    if workspace is None:
+        workspace = _workspace(need, dev, stream)
+    ev = _events(phase_events)
+    st = lib.spec_outcome_topk(_ptr(logits), code, _ptr(draft_tokens), R, g, V, float(temperature),
+                               ncache, _ptr(out_k), _ptr(out_a), _ptr(out_p), _ptr(hit),
+                               _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream_handle(stream, dev), None if ev is None else ev[0])
+    if st != 0:
+        raise SpecVerifyError(st, "spec_outcome_topk")
+    return out_k, out_a, out_p, hit
 
 
 def spec_verify_tree_greedy(target, parents, tokens, *, accept_len=None, accept_node=None,

@@ -111,6 +111,36 @@ int32_t tree_plan(int32_t B, int32_t n, int32_t V, int32_t dtype, TreePlan* p) {
     return SV_OK;
 }
 
+struct OutcomePlan {
+    int nseg, seg_len, kb;
+    size_t off_part, off_cand, off_zx, bytes;
+};
+
+int32_t outcome_plan(int32_t R, int32_t gamma, int32_t V, int32_t dtype, int32_t ncache,
+                     OutcomePlan* p) {
+    if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
+    if (R < 1 || gamma < 1 || V < 1 || gamma > kMaxGamma || ncache < 1 || ncache > kMaxCache)
+        return SV_ERR_SHAPE;
+    const int E = elem_bytes(dtype), epv = 16 / E;
+    const int64_t rows = static_cast<int64_t>(gamma) + 1;
+    const int64_t rows_total = static_cast<int64_t>(R) * rows;
+    if (static_cast<double>(rows_total) * V * E > 9.0e18) return SV_ERR_SHAPE;
+    p->kb = ncache <= 4 ? 4 : (ncache <= 8 ? 8 : 16);
+    // a request's rows*nseg*kb candidates are staged in LDS by the select
+    // kernel (12 bytes each, at most 4096 of them: 48 KiB)
+    const int64_t max_seg = 4096 / (rows * p->kb);
+    plan_segments(rows_total, V, epv, kTargetUnits, 4, static_cast<int>(max_seg < 1 ? 1 : max_seg),
+                  &p->nseg, &p->seg_len);
+    if (rows_total * p->nseg > INT32_MAX) return SV_ERR_SHAPE;
+    const size_t nr = static_cast<size_t>(rows_total);
+    size_t off = 0;
+    p->off_part = carve(&off, sizeof(Stat), nr * p->nseg);
+    p->off_cand = carve(&off, sizeof(OutcomeCand), nr * p->nseg * p->kb);
+    p->off_zx = carve(&off, sizeof(float), nr);
+    p->bytes = off;
+    return SV_OK;
+}
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 hipEvent_t event_at(void* const* ev, int i) {
@@ -257,6 +287,63 @@ extern "C" int32_t spec_verify_chain_pointmass(const void* target_logits, int32_
     return chain_call(target_logits, nullptr, true, dtype, draft_tokens, uniforms, B, gamma, V,
                       temperature, accept_len, out_tokens, final_dist, workspace,
                       workspace_bytes, stream, phase_events);
+}
+
+extern "C" size_t spec_outcome_topk_workspace_bytes(int32_t R, int32_t gamma, int32_t V,
+                                                    int32_t dtype, int32_t ncache) {
+    OutcomePlan p;
+    return outcome_plan(R, gamma, V, dtype, ncache, &p) == SV_OK ? p.bytes : 0;
+}
+
+extern "C" int32_t spec_outcome_topk(const void* logits, int32_t dtype,
+                                     const int32_t* draft_tokens, int32_t R, int32_t gamma,
+                                     int32_t V, double temperature, int32_t ncache,
+                                     int32_t* out_k, int32_t* out_a, double* out_p, double* hit,
+                                     void* workspace, size_t workspace_bytes, void* stream,
+                                     void* const* phase_events) {
+    OutcomePlan p;
+    int32_t st = outcome_plan(R, gamma, V, dtype, ncache, &p);
+    if (st != SV_OK) return st;
+    if (!logits || !draft_tokens || !out_k || !out_a || !out_p || !hit || !workspace)
+        return SV_ERR_NULL;
+    if (!std::isfinite(temperature) || temperature < 1e-6 || temperature > 1e6)
+        return SV_ERR_TEMPERATURE;
+    const size_t E = static_cast<size_t>(elem_bytes(dtype));
+    if (!aligned(logits, E) || !aligned(draft_tokens, 4) || !aligned(out_k, 4) ||
+        !aligned(out_a, 4) || !aligned(out_p, 8) || !aligned(hit, 8))
+        return SV_ERR_ALIGN;
+    if (!aligned(workspace, 16) || workspace_bytes < p.bytes) return SV_ERR_WORKSPACE;
+    OutcomeArgs a;
+    a.logits = logits;
+    a.tokens = draft_tokens;
+    a.R = R;
+    a.gamma = gamma;
+    a.V = V;
+    const double c = 1.4426950408889634074 / temperature;
+    float c_hi = static_cast<float>(c);
+    if (static_cast<double>(c_hi) >= c) c_hi = std::nextafter(c_hi, 0.0f);
+    a.c_hi = c_hi;
+    a.c_lo = static_cast<float>(c - static_cast<double>(c_hi));
+    a.c_d = static_cast<double>(a.c_hi) + static_cast<double>(a.c_lo);
+    a.T = temperature;
+    a.nseg = p.nseg;
+    a.seg_len = p.seg_len;
+    a.ncache = ncache;
+    a.kb = p.kb;
+    char* ws = static_cast<char*>(workspace);
+    a.part = reinterpret_cast<Stat*>(ws + p.off_part);
+    a.cand = reinterpret_cast<OutcomeCand*>(ws + p.off_cand);
+    a.zx = reinterpret_cast<float*>(ws + p.off_zx);
+    a.out_k = out_k;
+    a.out_a = out_a;
+    a.out_p = out_p;
+    a.hit = hit;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (launch_outcome_stats(a, dtype, s, event_at(phase_events, 0), event_at(phase_events, 1)) !=
+        hipSuccess)
+        return SV_ERR_HIP;
+    if (launch_outcome_select(a, s) != hipSuccess) return SV_ERR_HIP;
+    return SV_OK;
 }
 
 extern "C" int32_t spec_verify_tree_greedy(const void* target_logits, int32_t dtype,

@@ -88,6 +88,33 @@ struct TreeArgs {
     int32_t* out_tokens;
 };
 
+// Outcome scoring: one candidate (logit, token id) of a row segment.
+struct OutcomeCand {
+    float val;    // logit (-inf for an empty slot)
+    int32_t idx;  // token id (INT32_MAX for an empty slot)
+};
+
+constexpr int kMaxCache = 16;  // cache entries per request
+
+struct OutcomeArgs {
+    const void* logits;      // [R][gamma+1][V]
+    const int32_t* tokens;   // [R][gamma]
+    int R, gamma, V;
+    float c_hi, c_lo;
+    double c_d;
+    double T;
+    int nseg, seg_len;
+    int ncache;              // 1..kMaxCache
+    int kb;                  // candidates kept per row segment: 4, 8 or 16 (>= ncache)
+    Stat* part;              // [R][gamma+1][nseg]
+    OutcomeCand* cand;       // [R][gamma+1][nseg][kb]
+    float* zx;               // [R][gamma+1]: logit of row k's draft token (k < gamma)
+    int32_t* out_k;          // [R][ncache]
+    int32_t* out_a;          // [R][ncache]
+    double* out_p;           // [R][ncache]
+    double* hit;             // [R]
+};
+
 // Launchers (return the hipError_t of the launch).
 // The streaming launchers take an optional pair of events (both null, or
 // both valid): when given, the launch itself records them at the kernel's
@@ -101,5 +128,8 @@ hipError_t launch_chain_dist(const ChainArgs& a, int dtype, hipStream_t s);
 hipError_t launch_tree_argmax(const TreeArgs& a, int dtype, hipStream_t s, hipEvent_t ev_start,
                               hipEvent_t ev_stop);
 hipError_t launch_tree_resolve(const TreeArgs& a, hipStream_t s);
+hipError_t launch_outcome_stats(const OutcomeArgs& a, int dtype, hipStream_t s,
+                                hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_outcome_select(const OutcomeArgs& a, hipStream_t s);
 
 }  // namespace sv

@@ -191,6 +191,44 @@ int32_t spec_verify_tree_greedy(const void *target_logits, int32_t dtype,
                                 int32_t *out_tokens, void *workspace, size_t workspace_bytes,
                                 void *stream, void *const *phase_events);
 
+/* Cache entries per request of spec_outcome_topk. */
+#define SV_MAX_CACHE 16
+
+/* Bytes of workspace spec_outcome_topk needs; 0 if the arguments are
+ * invalid. */
+size_t spec_outcome_topk_workspace_bytes(int32_t R, int32_t gamma, int32_t V, int32_t dtype,
+                                         int32_t ncache);
+
+/* Outcome scores and cache selection ("JetSpec++", Section 4.2 "Outcome
+ * Selection"; Appendix F.1 and Proposition 1).  For each of R requests, row j
+ * (j = 0..gamma) of `logits` is the decoder's estimate of the target's
+ * next-token logits after the block's first j draft tokens; with
+ * p_j = softmax(row_j / T) and x_j the draft tokens, the outcome (k, a) of
+ * verifying the block -- k accepted draft tokens, then the extra token a --
+ * has probability
+ *   P(k, a) = prod_{i<k} p_i(x_i) * p_k(a)   for k < gamma and a != x_k,
+ *   P(gamma, a) = prod_{i<gamma} p_i(x_i) * p_gamma(a).
+ * The ncache most probable outcomes are returned, most probable first (equal
+ * probabilities: smaller k, then smaller a); outcomes of probability 0 are
+ * never returned, and unused slots hold k = a = -1, p = 0.  The hit
+ * probability of that cache is the sum of the returned probabilities.
+ *
+ *  logits        [R][gamma+1][V] dtype (f32 or bf16 bits).
+ *  draft_tokens  [R][gamma] int32.
+ *  temperature   T > 0 (finite, in [1e-6, 1e6]); ncache in [1, SV_MAX_CACHE].
+ *  out_k, out_a  out [R][ncache] int32; out_p out [R][ncache] double.
+ *  hit           out [R] double: sum of out_p, or -1 for an invalid request
+ *                (a draft token outside [0, V), a NaN or +inf logit, a row
+ *                without a finite logit, or |max finite logit| / T > 2^28),
+ *                whose slots are then all -1 / 0.
+ *  workspace, stream, phase_events: as for spec_verify_tree_greedy (the two
+ *  events bracket the one pass over the logits). */
+int32_t spec_outcome_topk(const void *logits, int32_t dtype, const int32_t *draft_tokens,
+                          int32_t R, int32_t gamma, int32_t V, double temperature, int32_t ncache,
+                          int32_t *out_k, int32_t *out_a, double *out_p, double *hit,
+                          void *workspace, size_t workspace_bytes, void *stream,
+                          void *const *phase_events);
+
 #ifdef __cplusplus
 }
 #endif

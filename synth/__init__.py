@@ -42,6 +42,9 @@ __all__ = [
     "pointmass_inputs",
     "pointmass_config_inputs",
     "pointmass_config_bytes",
+    "OUTCOME_CONFIG",
+    "outcome_config_inputs",
+    "outcome_config_bytes",
     "bf16_bits",
     "bf16_to_f32",
     "chain_inputs",
@@ -259,6 +262,33 @@ def pointmass_config_bytes(cfg: int, **overrides) -> int:
     c.update(overrides)
     e = 4 if c["dtype"] == "f32" else 2
     return c["B"] * (c["gamma"] + 1) * c["V"] * e
+
+
+# Outcome scoring workload: 32 requests (the request count of config 5, whose
+# 8 anticipated outcomes per request are what this scoring selects), decoder
+# rows with config 5's logits and temperature, draft tokens as for the
+# point-mass workloads, and a cache of 8 outcomes per request.
+OUTCOME_CONFIG = dict(R=32, gamma=16, V=151936, dtype="bf16", T=0.6, target=("gumbel", 4.0),
+                      boost=None, p_match=0.8, ncache=8)
+
+
+def outcome_config_inputs(seed: int = 0, threads: int | None = None, **overrides) -> dict:
+    """Decoder logits [R, gamma+1, V] and draft tokens [R, gamma] for the
+    outcome-scoring workload (uniforms are drawn but unused)."""
+    c = dict(OUTCOME_CONFIG)
+    c.update(overrides)
+    d = pointmass_inputs(c["R"], c["gamma"], c["V"], c["dtype"], c["T"], c["target"], c["boost"],
+                         c["p_match"], seed=seed, threads=threads)
+    d.update(kind="outcome", R=c["R"], ncache=c["ncache"])
+    return d
+
+
+def outcome_config_bytes(**overrides) -> int:
+    """Algorithmic logit bytes of one outcome-scoring call."""
+    c = dict(OUTCOME_CONFIG)
+    c.update(overrides)
+    e = 4 if c["dtype"] == "f32" else 2
+    return c["R"] * (c["gamma"] + 1) * c["V"] * e
 
 
 def _tree_parents(rng, n, max_depth, max_children):

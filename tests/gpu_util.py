@@ -74,6 +74,49 @@ def gpu_pointmass(d, want_dist=False, workspace=None, stream=None):
                 final_dist=None if dist is None else dist.cpu().numpy())
 
 
+def gpu_outcome(d, ncache, workspace=None):
+    torch, sv = require_gpu()
+    lg = to_dev_logits(d["target"], d["dtype"])
+    tok = to_dev(d["draft_tokens"], np.int32)
+    k, a, p, hit = sv.spec_outcome_topk(lg, tok, d["T"], ncache, workspace=workspace)
+    torch.cuda.synchronize()
+    return dict(k=k.cpu().numpy(), a=a.cpu().numpy(), p=p.cpu().numpy(), hit=hit.cpu().numpy())
+
+
+def compare_outcomes(gpu, orc_all, orc, label="", rel=1e-6):
+    """Cache parity.  orc: the oracle's cache of the same size; orc_all: its
+    scores of every outcome [R, gamma+1, V].  Slot by slot the GPU must keep
+    the oracle's outcome, or -- only where the two differ -- an outcome whose
+    oracle probability is within `rel` of the oracle's entry (a near-tie
+    whose order rounding may swap); probabilities and hit probabilities agree
+    to `rel`.  Returns the number of near-tie swaps."""
+    R, nc = orc["k"].shape
+    swaps = 0
+    for r in range(R):
+        if orc["hit"][r] < 0:
+            assert gpu["hit"][r] == -1.0 and (gpu["k"][r] == -1).all(), f"{label} r={r}: invalid"
+            continue
+        seen = set()
+        for c in range(nc):
+            ko, ao, po = orc["k"][r, c], orc["a"][r, c], orc["p"][r, c]
+            kg, ag, pg = gpu["k"][r, c], gpu["a"][r, c], gpu["p"][r, c]
+            if ko < 0:
+                assert kg == -1 and ag == -1 and pg == 0.0, f"{label} r={r} c={c}: slot not empty"
+                continue
+            assert kg >= 0, f"{label} r={r} c={c}: gpu slot empty, oracle {ko, ao, po}"
+            assert (kg, ag) not in seen, f"{label} r={r}: duplicate {kg, ag}"
+            seen.add((kg, ag))
+            if (kg, ag) != (ko, ao):
+                pog = orc_all[r, kg, ag]
+                assert abs(pog - po) <= rel * po, (
+                    f"{label} r={r} c={c}: gpu {(kg, ag)} (oracle p {pog:.12g}) vs oracle "
+                    f"{(ko, ao)} p {po:.12g}")
+                swaps += 1
+            assert abs(pg - orc_all[r, kg, ag]) <= rel * orc_all[r, kg, ag], f"{label} r={r} c={c}: p"
+        assert abs(gpu["hit"][r] - orc["hit"][r]) <= rel * orc["hit"][r], f"{label} r={r}: hit"
+    return swaps
+
+
 def gpu_tree(d, workspace=None):
     torch, sv = require_gpu()
     tgt = to_dev_logits(d["target"], d.get("dtype", "bf16"))

@@ -27,7 +27,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(spec_verify_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(spec_\w+)\s*\(", text)))
 
 
 def header_constants():
@@ -39,7 +39,8 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"spec_verify_chain", "spec_verify_tree_greedy", "spec_verify_chain_workspace_bytes",
             "spec_verify_tree_greedy_workspace_bytes", "spec_verify_status_string",
-            "spec_verify_chain_pointmass", "spec_verify_chain_pointmass_workspace_bytes"} <= set(names)
+            "spec_verify_chain_pointmass", "spec_verify_chain_pointmass_workspace_bytes",
+            "spec_outcome_topk", "spec_outcome_topk_workspace_bytes"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
@@ -167,6 +168,44 @@ def test_pointmass_host_errors(lib):
         assert 0 < sv.spec_verify_chain_pointmass_workspace_bytes(*shape) <= \
             sv.spec_verify_chain_workspace_bytes(*shape)
     assert sv.spec_verify_chain_pointmass_workspace_bytes(1, 256, 100, 0) == 0
+
+
+def test_outcome_host_errors(lib):
+    import exact_draft_verification_amd as sv
+
+    c = header_constants()
+    R, g, V = 2, 3, 64
+    t = np.zeros((R, g + 1, V), np.float32)
+    tok = np.zeros((R, g), np.int32)
+    k = np.zeros((R, 4), np.int32)
+    a = np.zeros((R, 4), np.int32)
+    pp = np.zeros((R, 4), np.float64)
+    hit = np.zeros(R, np.float64)
+    ws = np.zeros(1 << 16, np.uint8)
+    wsa = ws[(-ws.ctypes.data) % 256:]
+
+    def call(**o):
+        args = dict(t=p(t), dt=0, tok=p(tok), R=R, g=g, V=V, T=1.0, nc=4, k=p(k), a=p(a), pp=p(pp),
+                    hit=p(hit), ws=p(wsa), wsb=16)
+        args.update(o)
+        return lib.spec_outcome_topk(args["t"], args["dt"], args["tok"], args["R"], args["g"],
+                                     args["V"], args["T"], args["nc"], args["k"], args["a"],
+                                     args["pp"], args["hit"], args["ws"], args["wsb"], None, None)
+
+    assert call(t=None) == c["SV_ERR_NULL"]
+    assert call(tok=None) == c["SV_ERR_NULL"]
+    assert call(hit=None) == c["SV_ERR_NULL"]
+    assert call(R=0) == c["SV_ERR_SHAPE"]
+    assert call(g=256) == c["SV_ERR_SHAPE"]
+    assert call(nc=0) == c["SV_ERR_SHAPE"]
+    assert call(nc=c["SV_MAX_CACHE"] + 1) == c["SV_ERR_SHAPE"]
+    assert call(dt=2) == c["SV_ERR_DTYPE"]
+    assert call(T=0.0) == c["SV_ERR_TEMPERATURE"]
+    assert call(t=ct.c_void_p(t.ctypes.data + 2)) == c["SV_ERR_ALIGN"]
+    assert call(wsb=16) == c["SV_ERR_WORKSPACE"]
+    assert (k == 0).all() and (hit == 0).all()
+    assert sv.spec_outcome_topk_workspace_bytes(32, 16, 151936, 1, 8) > 0
+    assert sv.spec_outcome_topk_workspace_bytes(32, 16, 151936, 1, 17) == 0
 
 
 def test_tree_host_errors(lib):

@@ -1,0 +1,74 @@
+"""GPU parity of spec_outcome_topk against the fp64 oracle (needs an MI355X).
+Cache entries must be the oracle's outcomes slot by slot (near-ties within
+1e-6 relative may swap order), with probabilities and hit probabilities to
+1e-6 relative."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import compare_outcomes, gpu_outcome, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def run_case(d, ncache, label):
+    print(f"[case] {label} R={d['target'].shape[0]} gamma={d['gamma']} V={d['V']} {d['dtype']} "
+          f"ncache={ncache}", flush=True)
+    g = gpu_outcome(d, ncache)
+    o = oracle.outcome_topk(d["target"], d["draft_tokens"], d["T"], ncache, dtype=d["dtype"],
+                            want_all=True)
+    swaps = compare_outcomes(g, o["all_scores"], o, label)
+    print(f"[case] {label}: near-tie swaps {swaps}", flush=True)
+    return g, o
+
+
+SHAPES = [(3, 1, 2), (5, 2, 7), (4, 31, 1000), (2, 3, 5003), (1, 16, 151937), (6, 4, 4096),
+          (2, 100, 64)]
+
+
+@pytest.mark.parametrize("ncache", [1, 3, 8, 16])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"R{b}g{g}V{v}" for b, g, v in SHAPES])
+def test_shapes(shape, dtype, ncache):
+    R, g, V = shape
+    d = synth.pointmass_inputs(R, g, V, dtype, T=0.9, target=("normal", 2.0), p_match=0.7,
+                               seed=3000 + R + g + ncache)
+    run_case(d, ncache, f"oc-{shape}-{dtype}-c{ncache}")
+
+
+def test_outcome_workload_full_size():
+    d = synth.outcome_config_inputs(seed=8001, R=4)
+    run_case(d, 8, "oc-workload-R4")
+
+
+def test_peaked_and_tied_rows():
+    """bf16 logits with many equal values at the top of each row exercise the
+    lowest-token-first order among equal probabilities."""
+    rng = np.random.default_rng(5)
+    R, g, V = 4, 3, 3000
+    z = rng.integers(-6, 3, (R, g + 1, V)).astype(np.float32)
+    d = dict(target=synth.bf16_bits(z), draft_tokens=rng.integers(0, V, (R, g)).astype(np.int32),
+             gamma=g, V=V, dtype="bf16", T=1.0)
+    run_case(d, 16, "oc-ties")
+
+
+def test_masked_rows_and_invalid_requests():
+    rng = np.random.default_rng(6)
+    R, g, V = 5, 3, 500
+    z = rng.normal(0, 1.0, (R, g + 1, V)).astype(np.float32)
+    tok = rng.integers(0, V, (R, g)).astype(np.int32)
+    z[0, 1, tok[0, 1]] = -np.inf     # a masked draft token: no outcome beyond k = 1
+    z[1, :, 10:] = -np.inf           # few positive outcomes: fewer than the slots
+    tok[1] = [0, 1, 2]
+    tok[2, 0] = V                    # invalid token
+    z[3, 2, 7] = np.nan              # invalid row
+    d = dict(target=z, draft_tokens=tok, gamma=g, V=V, dtype="f32", T=1.0)
+    g_, o = run_case(d, 16, "oc-masked-invalid")
+    assert g_["hit"][2] == -1.0 and g_["hit"][3] == -1.0
+    assert (g_["k"][0][g_["k"][0] >= 0] <= 1).all()
