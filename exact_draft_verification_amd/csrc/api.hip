@@ -15,6 +15,7 @@ namespace {
 
 constexpr int kThreadsHost = 256;
 constexpr int64_t kTargetUnits = 8192;  // statistics/argmax workgroups to aim for
+constexpr int64_t kOutcomeUnits = 1024; // outcome-scoring workgroups to aim for
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -129,8 +130,11 @@ int32_t outcome_plan(int32_t R, int32_t gamma, int32_t V, int32_t dtype, int32_t
     // a request's rows*nseg*kb candidates are staged in LDS by the select
     // kernel (12 bytes each, at most 4096 of them: 48 KiB)
     const int64_t max_seg = 4096 / (rows * p->kb);
-    plan_segments(rows_total, V, epv, kTargetUnits, 4, static_cast<int>(max_seg < 1 ? 1 : max_seg),
-                  &p->nseg, &p->seg_len);
+    // long segments (few workgroups, at least 16 vectors per thread): the
+    // workgroup threshold that keeps top-list insertions rare only becomes
+    // selective after a thread has seen many logits
+    plan_segments(rows_total, V, epv, kOutcomeUnits, 16,
+                  static_cast<int>(max_seg < 1 ? 1 : max_seg), &p->nseg, &p->seg_len);
     if (rows_total * p->nseg > INT32_MAX) return SV_ERR_SHAPE;
     const size_t nr = static_cast<size_t>(rows_total);
     size_t off = 0;

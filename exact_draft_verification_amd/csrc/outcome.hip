@@ -14,13 +14,18 @@
 // candidates are found in the same single pass over the logits that takes
 // the softmax statistics:
 //  1. outcome_stats: one workgroup per (request, row, segment) folds (m, R, S)
-//     as the chain statistics do and keeps the KB largest logits of the
+//     as the chain statistics do and finds the KB largest logits of the
 //     segment (lowest token id first among equal ones), the row's draft token
-//     excluded.  Each thread holds an exact sorted list of its own KB best; a
-//     workgroup-wide threshold in LDS -- the largest of the threads' KB-th
-//     values, a lower bound of the workgroup's KB-th best -- filters the
-//     stream so that insertions stay rare.  The lists are merged by KB
-//     rounds of a workgroup-wide maximum.
+//     excluded.  Candidates are ordered by a 64-bit key (value, then index).
+//     The stream itself only takes the maximum of every 16-byte vector: the
+//     KB best elements lie in the KB+1 best vectors by (maximum, vector
+//     index) -- a vector outside them is behind KB+1 vector maxima, at most
+//     one of which is the excluded token -- so each wave keeps a sorted list
+//     of its best vector keys spread over its lanes, and a vector is offered
+//     to it only when its maximum passes a threshold shared through LDS (the
+//     largest of the waves' (KB+1)-th keys).  At the end the KB+1 best
+//     vectors of the workgroup are re-read and their elements, with the
+//     unaligned head and tail elements, ranked exactly.
 //  2. outcome_select: one workgroup per request merges the row statistics,
 //     forms A_k = sum_{i<k} log2 p_i(x_i) by a prefix sum, scores every
 //     candidate in fp64 as log2 P = A_k + z*c - L_k and keeps the ncache best.
@@ -33,77 +38,214 @@ namespace {
 constexpr double kDomain = 268435456.0;  // |m| / T limit (2^28)
 constexpr float kNegInf = -INFINITY;
 
-// Total order of floats as signed ints (larger float, larger key).
-__device__ inline int order_key(float f) {
-    const int i = __float_as_int(f);
-    return i >= 0 ? i : i ^ 0x7fffffff;
+// Candidate keys: unsigned 64-bit integers ordered like the candidates
+// (value descending, then index ascending).  The high word maps the float
+// value monotonically (-0 counts as +0, as in a float comparison), the low
+// word is 0xffffffff - index.  Key 0 is below every real key and means none.
+__device__ inline uint32_t value_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ inline float key_float(int k) { return __int_as_float(k >= 0 ? k : k ^ 0x7fffffff); }
+__device__ inline float key_value(uint64_t k) {
+    const uint32_t u = static_cast<uint32_t>(k >> 32);
+    return __uint_as_float((u & 0x80000000u) ? (u ^ 0x80000000u) : ~u);
+}
+__device__ inline uint64_t make_key(float v, uint32_t idx) {
+    return (static_cast<uint64_t>(value_key(v)) << 32) | (0xffffffffu - idx);
+}
+__device__ inline uint32_t key_index(uint64_t k) { return 0xffffffffu - static_cast<uint32_t>(k); }
 
-// (value desc, index asc): is (v, i) ahead of (w, j)?
-__device__ inline bool ahead(float v, int i, float w, int j) { return v > w || (v == w && i < j); }
+__device__ inline uint64_t readlane64(uint64_t x, int l) {
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(x), l);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(x >> 32), l);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ inline uint64_t uniform64(uint64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<int>(x));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<int>(x >> 32));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
 
+// Descending bitonic sort of one key per lane over the 64 lanes of a wave.
+__device__ inline uint64_t wave_sort_desc(uint64_t x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const uint64_t o = __shfl_xor(x, j, 64);
+            const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
+            x = keep_max ? (o > x ? o : x) : (o < x ? o : x);
+        }
+    }
+    return x;
+}
+
+// Statistics plus the per-wave list of the best vector keys.  Every member
+// function that uses ballots or cross-lane moves is called by all 64 lanes.
 template <class E, int KB>
-struct TopFolder {
+struct TopVectorFolder {
+    static constexpr int L = KB + 1;  // vectors that hold the KB best elements
     Stat s;
     float c_hi, c_lo;
-    float val[KB];
-    int id[KB];
-    int excl;          // the row's draft token (not an outcome), or -1
-    int body_begin;    // element index of body vector 0
-    int* s_theta;      // workgroup threshold (order key)
+    uint64_t lst;     // sorted (descending) over the wave's lanes; lanes < L matter
+    uint64_t th;      // wave-uniform: a vector whose key is not above it cannot
+                      // be among the workgroup's L best
+    float th_val;     // the value part of th; -inf while th is 0
+    bool seeded;      // the list holds the first batch
+    unsigned long long* s_th;  // workgroup threshold in LDS
 
-    // Insert (z, e) into the sorted list; the caller has checked that it
-    // beats the KB-th entry (elements reach a thread in increasing index, so
-    // an equal value never displaces an earlier one).
-    __device__ inline void insert(float z, int e) {
-        float v = z;
-        int ix = e;
-#pragma unroll
-        for (int j = 0; j < KB; ++j) {
-            const bool b = ahead(v, ix, val[j], id[j]);
-            const float tv = b ? val[j] : v;
-            const int ti = b ? id[j] : ix;
-            val[j] = b ? v : val[j];
-            id[j] = b ? ix : id[j];
-            v = tv;
-            ix = ti;
+    __device__ inline void set_th(uint64_t t) {
+        th = t;
+        th_val = t == 0 ? kNegInf : key_value(t);
+    }
+    // the wave's L-th best key is a valid threshold for the whole workgroup
+    __device__ inline void publish() {
+        const uint64_t w = readlane64(lst, L - 1);
+        if (w > th) {
+            set_th(w);
+            if ((threadIdx.x & 63) == 0) atomicMax(s_th, static_cast<unsigned long long>(w));
         }
     }
-
-    __device__ inline void offer(float z, int e, float theta) {
-        if (z > val[KB - 1] && z >= theta && e != excl) insert(z, e);
+    __device__ inline void refresh() {
+        const uint64_t t =
+            uniform64(__hip_atomic_load(s_th, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        if (t > th) set_th(t);
     }
-
+    // ck > th (so it lands in lanes < L); keeps the lanes sorted
+    __device__ inline void insert(uint64_t ck) {
+        const int lane = threadIdx.x & 63;
+        const int pos = __popcll(__ballot(lst > ck));
+        const uint64_t up = __shfl_up(lst, 1u, 64);
+        lst = lane < pos ? lst : (lane == pos ? ck : up);
+        publish();
+    }
     template <int N>
-    __device__ inline void batch(const uint4* v, int v0) {
-        float x[N * E::kPerVec];
+    __device__ inline void offer(const uint64_t* key) {
 #pragma unroll
-        for (int u = 0; u < N; ++u) E::unpack(v[u], x + u * E::kPerVec);
-        stat_fold<N * E::kPerVec>(s, x, c_hi, c_lo);
-        const float theta = key_float(*s_theta);
-        // the batch max is cheap to test before any per-element work
-        float bm = x[0];
-#pragma unroll
-        for (int i = 1; i < N * E::kPerVec; ++i) bm = fmaxf(bm, x[i]);
-        if (bm > val[KB - 1] && bm >= theta) {
-#pragma unroll
-            for (int u = 0; u < N; ++u)
-#pragma unroll
-                for (int w = 0; w < E::kPerVec; ++w)
-                    offer(x[u * E::kPerVec + w], body_begin + (v0 + u * kThreads) * E::kPerVec + w,
-                          theta);
-            if (val[KB - 1] > kNegInf) atomicMax(s_theta, order_key(val[KB - 1]));
+        for (int u = 0; u < N; ++u) {
+            uint64_t m = __ballot(key[u] > th);
+            while (m) {
+                const int l = __builtin_ctzll(m);
+                insert(readlane64(key[u], l));
+                m &= ~(1ull << l);
+                m &= __ballot(key[u] > th);
+            }
         }
+    }
+
+    // N vectors per thread; vector u is body vector v0 + u*kThreads, present
+    // when FULL or when that index is below nvec.
+    template <int N, bool FULL>
+    __device__ inline void batch(const uint4* v, int v0, int nvec) {
+        constexpr int P = E::kPerVec;
+        float x[N * P];
+#pragma unroll
+        for (int u = 0; u < N; ++u) E::unpack(v[u], x + u * P);
+        float vm[N];
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            vm[u] = x[u * P];
+#pragma unroll
+            for (int i = 1; i < P; ++i) vm[u] = fmaxf(vm[u], x[u * P + i]);
+        }
+        float bm;
+        if (FULL) {
+            bm = vm[0];
+#pragma unroll
+            for (int u = 1; u < N; ++u) bm = fmaxf(bm, vm[u]);
+            stat_fold_max<N * P>(s, x, bm, c_hi, c_lo);
+        } else {
+            bm = kNegInf;
+#pragma unroll
+            for (int u = 0; u < N; ++u) {
+                if (v0 + u * kThreads < nvec) {
+                    stat_fold_max<P>(s, x + u * P, vm[u], c_hi, c_lo);
+                    bm = fmaxf(bm, vm[u]);
+                }
+            }
+        }
+        if (seeded) {
+            refresh();
+            // cheap test first: can any lane's batch reach the threshold?
+            if (!__ballot(!(bm < th_val))) return;
+        }
+        uint64_t key[N];
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            const int vi = v0 + u * kThreads;
+            key[u] = (FULL || vi < nvec) ? make_key(vm[u], static_cast<uint32_t>(vi)) : 0;
+        }
+        if (!seeded) {
+            // the list starts as the sorted best vectors of each lane's first
+            // batch; the lanes' other vectors are offered as usual
+            uint64_t best = key[0];
+#pragma unroll
+            for (int u = 1; u < N; ++u) best = key[u] > best ? key[u] : best;
+            lst = wave_sort_desc(best);
+#pragma unroll
+            for (int u = 0; u < N; ++u) key[u] = key[u] == best ? 0 : key[u];
+            seeded = true;
+            publish();
+            refresh();
+        }
+        offer<N>(key);
     }
 };
 
+// Streams the 16-byte vectors [0, nvec) of `body` through f as
+// stream_vectors does, except that the partial batch at the end is also
+// folded by every thread (f.batch<U, false> skips the vectors past the end),
+// so the wave-wide list operations always run with all 64 lanes.
+template <int U, class F>
+__device__ inline void stream_all_lanes(const char* body, int nvec, F& f) {
+    if (nvec <= 0) return;
+    const int tid = threadIdx.x;
+    constexpr int kBatch = kThreads * U;
+    const int nb = nvec / kBatch;
+    const int rest0 = nb * kBatch;
+    uint4 rest[U];
+    if (nb > 0) {
+        uint4 cur[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) cur[u] = load16_stream(body + static_cast<size_t>(u * kThreads + tid) * 16);
+        for (int t = 0; t + 1 < nb; ++t) {
+            uint4 nxt[U];
+            const char* nbp = body + static_cast<size_t>(t + 1) * kBatch * 16;
+#pragma unroll
+            for (int u = 0; u < U; ++u) nxt[u] = load16_stream(nbp + static_cast<size_t>(u * kThreads + tid) * 16);
+            f.template batch<U, true>(cur, t * kBatch + tid, nvec);
+#pragma unroll
+            for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = min(rest0 + u * kThreads + tid, nvec - 1);
+            rest[u] = load16_stream(body + static_cast<size_t>(v) * 16);
+        }
+        f.template batch<U, true>(cur, (nb - 1) * kBatch + tid, nvec);
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = min(u * kThreads + tid, nvec - 1);
+            rest[u] = load16_stream(body + static_cast<size_t>(v) * 16);
+        }
+    }
+    if (rest0 < nvec) f.template batch<U, false>(rest, rest0 + tid, nvec);
+}
+
 template <class E, int U, int KB>
 __global__ __launch_bounds__(kThreads) void outcome_stats_kernel(OutcomeArgs a) {
+    constexpr int L = KB + 1;
+    constexpr int P = E::kPerVec;
+    constexpr int kMaxCand = L * P + 2 * (P - 1);  // vector elements + head + tail
+    static_assert(kWaves * L <= kThreads && kMaxCand <= kThreads, "one key per thread");
     __shared__ Stat s_w[kWaves];
-    __shared__ int s_theta;
-    __shared__ float s_bv[kWaves];
-    __shared__ int s_bi[kWaves];
+    __shared__ unsigned long long s_th;
+    __shared__ unsigned long long s_lst[kWaves * L];
+    __shared__ unsigned long long s_top[L];
+    __shared__ unsigned long long s_ck[kMaxCand];
     const int rows = a.gamma + 1;
     const int unit = blockIdx.x;
     const int seg = unit % a.nseg;
@@ -115,7 +257,8 @@ __global__ __launch_bounds__(kThreads) void outcome_stats_kernel(OutcomeArgs a) 
     const S* row = static_cast<const S*>(a.logits) + static_cast<int64_t>(rr) * a.V;
     const int e0 = seg * a.seg_len;
     const int e1 = min(a.V, e0 + a.seg_len);
-    if (tid == 0) s_theta = order_key(kNegInf);
+    if (tid == 0) s_th = 0;
+    if (tid < L) s_top[tid] = 0;
     int excl = -1;
     if (k < a.gamma) excl = a.tokens[static_cast<int64_t>(r) * a.gamma + k];
     // the draft token's logit, if this segment holds it
@@ -124,72 +267,66 @@ __global__ __launch_bounds__(kThreads) void outcome_stats_kernel(OutcomeArgs a) 
     if (have_zx) zx = E::one(row + excl);
     __syncthreads();
 
-    TopFolder<E, KB> f;
+    TopVectorFolder<E, KB> f;
     f.s = stat_empty();
     f.c_hi = a.c_hi;
     f.c_lo = a.c_lo;
-#pragma unroll
-    for (int j = 0; j < KB; ++j) {
-        f.val[j] = kNegInf;
-        f.id[j] = INT32_MAX;
+    f.lst = 0;
+    f.set_th(0);
+    f.seeded = false;
+    f.s_th = &s_th;
+    RangeSplit<E> sp{e0, e0, e0, 0, e0, e0};
+    if (e0 < e1) sp = split_range<E>(row, e0, e1);
+    for (int e = sp.head_begin + tid; e < sp.head_end; e += kThreads) {
+        const float x = E::one(row + e);
+        stat_fold<1>(f.s, &x, a.c_hi, a.c_lo);
     }
-    f.excl = excl;
-    f.s_theta = &s_theta;
-    if (e0 < e1) {
-        const RangeSplit<E> sp = split_range<E>(row, e0, e1);
-        f.body_begin = sp.body_begin;
-        for (int e = sp.head_begin + tid; e < sp.head_end; e += kThreads) {
-            const float x = E::one(row + e);
-            stat_fold<1>(f.s, &x, a.c_hi, a.c_lo);
-            f.offer(x, e, kNegInf);
-        }
-        stream_vectors<U>(reinterpret_cast<const char*>(row + sp.body_begin), sp.nvec, f);
-        for (int e = sp.tail_begin + tid; e < sp.tail_end; e += kThreads) {
-            const float x = E::one(row + e);
-            stat_fold<1>(f.s, &x, a.c_hi, a.c_lo);
-            f.offer(x, e, kNegInf);
-        }
+    stream_all_lanes<U>(reinterpret_cast<const char*>(row + sp.body_begin), sp.nvec, f);
+    for (int e = sp.tail_begin + tid; e < sp.tail_end; e += kThreads) {
+        const float x = E::one(row + e);
+        stat_fold<1>(f.s, &x, a.c_hi, a.c_lo);
     }
-    const Stat st = block_reduce_stat(f.s, s_w);
-    // KB rounds of a workgroup-wide maximum over the threads' list heads
+    if (lane < L) s_lst[wave * L + lane] = f.lst;
+    const Stat st = block_reduce_stat(f.s, s_w);  // synchronises the workgroup
+
+    // the workgroup's L best vectors, by rank among the waves' lists
+    if (tid < kWaves * L) {
+        const uint64_t kk = s_lst[tid];
+        int rank = 0;
+        for (int j = 0; j < kWaves * L; ++j) rank += s_lst[j] > kk;
+        if (kk != 0 && rank < L) s_top[rank] = kk;
+    }
+    __syncthreads();
+    // their elements and the head and tail elements, one per thread
+    const int nh = sp.head_end - sp.head_begin;
+    const int nc = L * P + nh + (sp.tail_end - sp.tail_begin);
+    uint64_t ck = 0;
+    float z = kNegInf;
+    int e = -1;
+    if (tid < nc) {
+        if (tid < L * P) {
+            const uint64_t vk = s_top[tid / P];
+            if (vk != 0) e = sp.body_begin + static_cast<int>(key_index(vk)) * P + tid % P;
+        } else {
+            const int j = tid - L * P;
+            e = j < nh ? sp.head_begin + j : sp.tail_begin + (j - nh);
+        }
+        if (e >= 0 && e != excl) {
+            z = E::one(row + e);
+            ck = make_key(z, static_cast<uint32_t>(e));
+        }
+        s_ck[tid] = ck;
+    }
+    __syncthreads();
+    // exact ranks (equal keys, i.e. empty ones, by position)
     OutcomeCand* out = a.cand + static_cast<int64_t>(unit) * KB;
-    for (int round = 0; round < KB; ++round) {
-        float bv = f.val[0];
-        int bi = f.id[0];
-#pragma unroll
-        for (int mask = 32; mask >= 1; mask >>= 1) {
-            const float ov = __shfl_xor(bv, mask, 64);
-            const int oi = __shfl_xor(bi, mask, 64);
-            if (ahead(ov, oi, bv, bi)) {
-                bv = ov;
-                bi = oi;
-            }
+    if (tid < nc) {
+        int rank = 0;
+        for (int j = 0; j < nc; ++j) {
+            const uint64_t o = s_ck[j];
+            rank += (o > ck) || (o == ck && j < tid);
         }
-        __syncthreads();
-        if (lane == 0) {
-            s_bv[wave] = bv;
-            s_bi[wave] = bi;
-        }
-        __syncthreads();
-        float wv = s_bv[0];
-        int wi = s_bi[0];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w)
-            if (ahead(s_bv[w], s_bi[w], wv, wi)) {
-                wv = s_bv[w];
-                wi = s_bi[w];
-            }
-        if (tid == 0) out[round] = OutcomeCand{wv, wi};
-        // the owner of the winning head pops it (token ids are unique)
-        if (wi != INT32_MAX && f.id[0] == wi) {
-#pragma unroll
-            for (int j = 0; j + 1 < KB; ++j) {
-                f.val[j] = f.val[j + 1];
-                f.id[j] = f.id[j + 1];
-            }
-            f.val[KB - 1] = kNegInf;
-            f.id[KB - 1] = INT32_MAX;
-        }
+        if (rank < KB) out[rank] = ck != 0 ? OutcomeCand{z, e} : OutcomeCand{kNegInf, INT32_MAX};
     }
     if (tid == 0) {
         a.part[unit] = st;

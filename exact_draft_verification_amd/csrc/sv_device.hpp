@@ -189,11 +189,9 @@ __device__ inline float pairwise_sum(float* v) {
 // element t = z*c_hi - R + z*c_lo (two fused multiply-adds, the subtraction
 // of R exact inside the first) and 2^t on the hardware exp2 unit; the batch
 // sum is pairwise in fp32 and accumulated in fp64.
+// stat_fold_max takes the batch maximum lm from the caller.
 template <int N>
-__device__ inline void stat_fold(Stat& s, const float* x, float c_hi, float c_lo) {
-    float lm = x[0];
-#pragma unroll
-    for (int i = 1; i < N; ++i) lm = fmaxf(lm, x[i]);
+__device__ inline void stat_fold_max(Stat& s, const float* x, float lm, float c_hi, float c_lo) {
     const float Rn = fmaxf(s.R, ceilf(lm * c_hi));
     s.S = ldexp(s.S, rescale_exponent(s.R, Rn));
     s.R = Rn;
@@ -206,6 +204,14 @@ __device__ inline void stat_fold(Stat& s, const float* x, float c_hi, float c_lo
         e[i] = __builtin_amdgcn_exp2f(t);
     }
     s.S += static_cast<double>(pairwise_sum<N>(e));
+}
+
+template <int N>
+__device__ inline void stat_fold(Stat& s, const float* x, float c_hi, float c_lo) {
+    float lm = x[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) lm = fmaxf(lm, x[i]);
+    stat_fold_max<N>(s, x, lm, c_hi, c_lo);
 }
 
 // ---------------------------------------------------------------------------
