@@ -244,7 +244,6 @@ __global__ __launch_bounds__(kThreads) void outcome_stats_kernel(OutcomeArgs a) 
     __shared__ Stat s_w[kWaves];
     __shared__ unsigned long long s_th;
     __shared__ unsigned long long s_lst[kWaves * L];
-    __shared__ unsigned long long s_top[L];
     __shared__ unsigned long long s_ck[kMaxCand];
     const int rows = a.gamma + 1;
     const int unit = blockIdx.x;
@@ -258,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void outcome_stats_kernel(OutcomeArgs a) 
     const int e0 = seg * a.seg_len;
     const int e1 = min(a.V, e0 + a.seg_len);
     if (tid == 0) s_th = 0;
-    if (tid < L) s_top[tid] = 0;
+    if (tid < L * P) s_ck[tid] = 0;
     int excl = -1;
     if (k < a.gamma) excl = a.tokens[static_cast<int64_t>(r) * a.gamma + k];
     // the draft token's logit, if this segment holds it
@@ -277,56 +276,55 @@ __global__ __launch_bounds__(kThreads) void outcome_stats_kernel(OutcomeArgs a) 
     f.s_th = &s_th;
     RangeSplit<E> sp{e0, e0, e0, 0, e0, e0};
     if (e0 < e1) sp = split_range<E>(row, e0, e1);
+    // candidate slots: [0, L*P) the elements of the workgroup's L best
+    // vectors, in rank order, then the head and the tail elements
+    const int nh = sp.head_end - sp.head_begin;
+    const int nc = L * P + nh + (sp.tail_end - sp.tail_begin);
     for (int e = sp.head_begin + tid; e < sp.head_end; e += kThreads) {
         const float x = E::one(row + e);
         stat_fold<1>(f.s, &x, a.c_hi, a.c_lo);
+        s_ck[L * P + (e - sp.head_begin)] = e != excl ? make_key(x, static_cast<uint32_t>(e)) : 0;
     }
     stream_all_lanes<U>(reinterpret_cast<const char*>(row + sp.body_begin), sp.nvec, f);
     for (int e = sp.tail_begin + tid; e < sp.tail_end; e += kThreads) {
         const float x = E::one(row + e);
         stat_fold<1>(f.s, &x, a.c_hi, a.c_lo);
+        s_ck[L * P + nh + (e - sp.tail_begin)] = e != excl ? make_key(x, static_cast<uint32_t>(e)) : 0;
     }
+    // re-read the wave's L best vectors while the statistics are reduced
+    const bool listed = lane < L && f.lst != 0;
+    const int vbeg = sp.body_begin + static_cast<int>(key_index(f.lst)) * P;
+    uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+    if (listed) raw = load16(row + vbeg);
     if (lane < L) s_lst[wave * L + lane] = f.lst;
     const Stat st = block_reduce_stat(f.s, s_w);  // synchronises the workgroup
 
-    // the workgroup's L best vectors, by rank among the waves' lists
-    if (tid < kWaves * L) {
-        const uint64_t kk = s_lst[tid];
+    // a listed vector among the workgroup's L best (by rank over the waves'
+    // lists; nonzero keys are distinct) scatters its element keys
+    if (listed) {
         int rank = 0;
-        for (int j = 0; j < kWaves * L; ++j) rank += s_lst[j] > kk;
-        if (kk != 0 && rank < L) s_top[rank] = kk;
-    }
-    __syncthreads();
-    // their elements and the head and tail elements, one per thread
-    const int nh = sp.head_end - sp.head_begin;
-    const int nc = L * P + nh + (sp.tail_end - sp.tail_begin);
-    uint64_t ck = 0;
-    float z = kNegInf;
-    int e = -1;
-    if (tid < nc) {
-        if (tid < L * P) {
-            const uint64_t vk = s_top[tid / P];
-            if (vk != 0) e = sp.body_begin + static_cast<int>(key_index(vk)) * P + tid % P;
-        } else {
-            const int j = tid - L * P;
-            e = j < nh ? sp.head_begin + j : sp.tail_begin + (j - nh);
+        for (int j = 0; j < kWaves * L; ++j) rank += s_lst[j] > f.lst;
+        if (rank < L) {
+            float x[P];
+            E::unpack(raw, x);
+#pragma unroll
+            for (int i = 0; i < P; ++i)
+                s_ck[rank * P + i] = vbeg + i != excl ? make_key(x[i], static_cast<uint32_t>(vbeg + i)) : 0;
         }
-        if (e >= 0 && e != excl) {
-            z = E::one(row + e);
-            ck = make_key(z, static_cast<uint32_t>(e));
-        }
-        s_ck[tid] = ck;
     }
     __syncthreads();
     // exact ranks (equal keys, i.e. empty ones, by position)
     OutcomeCand* out = a.cand + static_cast<int64_t>(unit) * KB;
     if (tid < nc) {
+        const uint64_t ck = s_ck[tid];
         int rank = 0;
         for (int j = 0; j < nc; ++j) {
             const uint64_t o = s_ck[j];
             rank += (o > ck) || (o == ck && j < tid);
         }
-        if (rank < KB) out[rank] = ck != 0 ? OutcomeCand{z, e} : OutcomeCand{kNegInf, INT32_MAX};
+        if (rank < KB)
+            out[rank] = ck != 0 ? OutcomeCand{key_value(ck), static_cast<int32_t>(key_index(ck))}
+                                : OutcomeCand{kNegInf, INT32_MAX};
     }
     if (tid == 0) {
         a.part[unit] = st;
@@ -336,143 +334,180 @@ __global__ __launch_bounds__(kThreads) void outcome_stats_kernel(OutcomeArgs a) 
 
 // Per-request merge: row statistics, prefix of accepted-token log2
 // probabilities, candidate scores and the ncache best outcomes.
+//
+// Candidate i of a request sits at ((k * nseg + segment) * kb + position);
+// each segment's list is sorted by (logit desc, token asc) and the segments
+// of a row cover increasing token ranges, so among equal scores the
+// required order (smaller k, then smaller token) is the order of i.  The
+// best outcomes are therefore found by a tournament over the list heads on
+// one wave: each lane owns some lists, one wave-wide maximum of
+// (score desc, i asc) per kept outcome, after which only the winning list
+// advances.
+__device__ inline bool cand_ahead(double s1, int i1, double s2, int i2) {
+    return s1 > s2 || (s1 == s2 && s1 > -INFINITY && i1 < i2);
+}
+
+// One step of a wave-wide maximum over DPP lane moves (lanes outside the
+// move keep their own value).
+template <int CTRL, int ROWS>
+__device__ inline void dpp_max_step(double& s, int& i) {
+    const int lo = __double2loint(s), hi = __double2hiint(s);
+    const int olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xf, false);
+    const int ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xf, false);
+    const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROWS, 0xf, false);
+    const double os = __hiloint2double(ohi, olo);
+    if (cand_ahead(os, oi, s, i)) {
+        s = os;
+        i = oi;
+    }
+}
+
+// The wave's best (score, i); every lane gets it.  Quad swaps, half-row and
+// row mirrors leave each row of 16 lanes with its best, the two row
+// broadcasts carry it to lane 63.
+__device__ inline void wave_best(double& s, int& i) {
+    dpp_max_step<0xb1, 0xf>(s, i);   // quad_perm [1,0,3,2]
+    dpp_max_step<0x4e, 0xf>(s, i);   // quad_perm [2,3,0,1]
+    dpp_max_step<0x141, 0xf>(s, i);  // row_half_mirror
+    dpp_max_step<0x140, 0xf>(s, i);  // row_mirror
+    dpp_max_step<0x142, 0xa>(s, i);  // row_bcast:15 into rows 1 and 3
+    dpp_max_step<0x143, 0xc>(s, i);  // row_bcast:31 into rows 2 and 3
+    const int lo = __builtin_amdgcn_readlane(__double2loint(s), 63);
+    const int hi = __builtin_amdgcn_readlane(__double2hiint(s), 63);
+    i = __builtin_amdgcn_readlane(i, 63);
+    s = __hiloint2double(hi, lo);
+}
+
 __global__ __launch_bounds__(kThreads) void outcome_select_kernel(OutcomeArgs a) {
     extern __shared__ unsigned char s_dyn[];
     __shared__ double s_L[kMaxGamma + 1];
     __shared__ double s_A[kMaxGamma + 1];
     __shared__ double s_waves[kWaves];
     __shared__ int s_bad;
-    __shared__ double s_bv[kWaves];
-    __shared__ int s_bk[kWaves], s_ba[kWaves], s_bj[kWaves];
+    __shared__ int s_firstneg;
+    constexpr int kPre = 2;  // candidates per thread loaded up front
     const int r = blockIdx.x;
-    const int g = a.gamma, rows = g + 1, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int ncand = rows * a.nseg * a.kb;  // candidates of this request
-    const int per_row = a.nseg * a.kb;                              // candidates per row
-    double* c_score = reinterpret_cast<double*>(s_dyn);             // [ncand]
-    int* c_tok = reinterpret_cast<int*>(c_score + ncand);           // [ncand]
-    if (tid == 0) s_bad = 0;
-    __syncthreads();
-    // row statistics (one thread per row, its segments merged in order)
-    for (int k = tid; k < rows; k += kThreads) {
-        const Stat* p = a.part + (static_cast<int64_t>(r) * rows + k) * a.nseg;
-        Stat t = p[0];
+    const int g = a.gamma, rows = g + 1, tid = threadIdx.x, lane = tid & 63;
+    const int kb = a.kb;
+    const int nlists = rows * a.nseg;  // one sorted list per (row, segment)
+    const int ncand = nlists * kb;     // candidates of this request
+    const int per_row = a.nseg * kb;   // candidates per row
+    double* c_score = reinterpret_cast<double*>(s_dyn);  // [ncand]
+    int* c_tok = reinterpret_cast<int*>(c_score + ncand);  // [ncand]
+    int* l_pos = c_tok + ncand;                            // [nlists] next entry
+    const OutcomeCand* cand = a.cand + static_cast<int64_t>(r) * ncand;
+    // every global read of the request is issued before the first wait
+    OutcomeCand pre[kPre];
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) {
+        const int i = tid + j * kThreads;
+        pre[j] = i < ncand ? cand[i] : OutcomeCand{kNegInf, INT32_MAX};
+    }
+    int x_tok = 0;
+    float zx = 0.0f;
+    if (tid < g) {
+        x_tok = a.tokens[static_cast<int64_t>(r) * g + tid];
+        zx = a.zx[static_cast<int64_t>(r) * rows + tid];
+    }
+    Stat t = stat_empty();
+    if (tid < rows) {
+        const Stat* p = a.part + (static_cast<int64_t>(r) * rows + tid) * a.nseg;
+        t = p[0];
         for (int s = 1; s < a.nseg; ++s) t = stat_merge(t, p[s]);
+    }
+    if (tid == 0) {
+        s_bad = 0;
+        s_firstneg = INT32_MAX;
+    }
+    for (int l = tid; l < nlists; l += kThreads) l_pos[l] = 0;
+    __syncthreads();
+    // row statistics (one thread per row; rows <= kThreads)
+    if (tid < rows) {
         const bool ok = isfinite(t.S) && t.S > 0.0 && fabs(static_cast<double>(t.m) / a.T) <= kDomain;
         if (!ok) atomicOr(&s_bad, 1);
-        s_L[k] = static_cast<double>(t.R) + log2(t.S);
-        if (k < g) {
-            const int x = a.tokens[static_cast<int64_t>(r) * g + k];
-            if (x < 0 || x >= a.V) atomicOr(&s_bad, 1);
-        }
+        s_L[tid] = static_cast<double>(t.R) + log2(t.S);
+        if (tid < g && (x_tok < 0 || x_tok >= a.V)) atomicOr(&s_bad, 1);
     }
     __syncthreads();
     // A_k = sum_{i<k} log2 p_i(x_i): exclusive prefix over the rows
     double term = 0.0;
-    if (tid < g) {
-        const float zx = a.zx[static_cast<int64_t>(r) * rows + tid];
-        term = zx == kNegInf ? -INFINITY : static_cast<double>(zx) * a.c_d - s_L[tid];
-    }
+    if (tid < g) term = zx == kNegInf ? -INFINITY : static_cast<double>(zx) * a.c_d - s_L[tid];
     // a -inf term (a masked draft token) makes every later prefix -inf
     const bool neg = term == -INFINITY;
     double total;
     const double excl_sum = block_exclusive_scan(neg ? 0.0 : term, s_waves, &total);
-    __syncthreads();
-    // the first position whose draft token is masked, via the LDS minimum
-    __shared__ int s_firstneg;
-    if (tid == 0) s_firstneg = INT32_MAX;
-    __syncthreads();
     if (neg) atomicMin(&s_firstneg, tid);
     __syncthreads();
     if (tid < rows) s_A[tid] = tid > s_firstneg ? -INFINITY : excl_sum;
     __syncthreads();
     // scores of every candidate (log2 P), -inf for empty slots
-    for (int i = tid; i < ncand; i += kThreads) {
+    const bool bad = s_bad != 0;
+    auto score = [&](int i, const OutcomeCand& c) {
         const int k = i / per_row;
-        const OutcomeCand c = a.cand[static_cast<int64_t>(r) * ncand + i];
         double sc = -INFINITY;
-        if (c.idx != INT32_MAX && c.val != kNegInf && !s_bad)
+        if (c.idx != INT32_MAX && c.val != kNegInf && !bad)
             sc = s_A[k] + (static_cast<double>(c.val) * a.c_d - s_L[k]);
         c_score[i] = sc;
         c_tok[i] = c.idx;
+    };
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) {
+        const int i = tid + j * kThreads;
+        if (i < ncand) score(i, pre[j]);
     }
+    for (int i = tid + kPre * kThreads; i < ncand; i += kThreads) score(i, cand[i]);
     __syncthreads();
-    // ncache rounds of a workgroup-wide maximum (ties: smaller k, then token)
+    if (tid >= 64) return;  // the tournament runs on the first wave alone
+
     int32_t* ok_ = a.out_k + static_cast<int64_t>(r) * a.ncache;
     int32_t* oa_ = a.out_a + static_cast<int64_t>(r) * a.ncache;
     double* op_ = a.out_p + static_cast<int64_t>(r) * a.ncache;
+    // this lane's best list head
+    double bs = -INFINITY;
+    int bi = INT32_MAX, bl = -1;
+    auto rescan = [&]() {
+        bs = -INFINITY;
+        bi = INT32_MAX;
+        bl = -1;
+        for (int l = lane; l < nlists; l += 64) {
+            const int p = l_pos[l];
+            if (p >= kb) continue;
+            const int i = l * kb + p;
+            const double sc = c_score[i];
+            if (cand_ahead(sc, i, bs, bi)) {
+                bs = sc;
+                bi = i;
+                bl = l;
+            }
+        }
+    };
+    rescan();
     double hit = 0.0;
-    for (int c = 0; c < a.ncache; ++c) {
-        double bv = -INFINITY;
-        int bk = INT32_MAX, ba = INT32_MAX, bj = -1;
-        for (int i = tid; i < ncand; i += kThreads) {
-            const double v = c_score[i];
-            const int k = i / per_row, t = c_tok[i];
-            if (v > bv || (v == bv && v > -INFINITY && (k < bk || (k == bk && t < ba)))) {
-                bv = v;
-                bk = k;
-                ba = t;
-                bj = i;
-            }
-        }
-#pragma unroll
-        for (int mask = 32; mask >= 1; mask >>= 1) {
-            const double ov = __shfl_xor(bv, mask, 64);
-            const int ok = __shfl_xor(bk, mask, 64), oa = __shfl_xor(ba, mask, 64);
-            const int oj = __shfl_xor(bj, mask, 64);
-            if (ov > bv || (ov == bv && ov > -INFINITY && (ok < bk || (ok == bk && oa < ba)))) {
-                bv = ov;
-                bk = ok;
-                ba = oa;
-                bj = oj;
-            }
-        }
+    int c = 0;
+    for (; c < a.ncache; ++c) {
+        double ws = bs;
+        int wi = bi;
+        wave_best(ws, wi);
+        if (!(ws > -INFINITY)) break;  // no outcome with positive probability left
+        const double P = exp2(ws);
+        hit += P;
         if (lane == 0) {
-            s_bv[wave] = bv;
-            s_bk[wave] = bk;
-            s_ba[wave] = ba;
-            s_bj[wave] = bj;
+            ok_[c] = wi / per_row;
+            oa_[c] = c_tok[wi];
+            op_[c] = P;
         }
-        __syncthreads();
-        double wv = s_bv[0];
-        int wk = s_bk[0], wa = s_ba[0], wj = s_bj[0];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) {
-            const double ov = s_bv[w];
-            if (ov > wv || (ov == wv && ov > -INFINITY && (s_bk[w] < wk || (s_bk[w] == wk && s_ba[w] < wa)))) {
-                wv = ov;
-                wk = s_bk[w];
-                wa = s_ba[w];
-                wj = s_bj[w];
-            }
+        if (bi == wi) {  // the owner of the winning list advances it
+            l_pos[bl] += 1;
+            rescan();
         }
-        __syncthreads();
-        if (wv > -INFINITY) {
-            const double P = exp2(wv);
-            hit += P;
-            if (tid == 0) {
-                ok_[c] = wk;
-                oa_[c] = wa;
-                op_[c] = P;
-                c_score[wj] = -INFINITY;  // taken
-            }
-        } else if (tid == 0) {
+    }
+    if (lane == 0) {
+        for (; c < a.ncache; ++c) {
             ok_[c] = -1;
             oa_[c] = -1;
             op_[c] = 0.0;
         }
-        __syncthreads();
-    }
-    if (tid == 0) {
-        if (s_bad) {
-            for (int c = 0; c < a.ncache; ++c) {
-                ok_[c] = -1;
-                oa_[c] = -1;
-                op_[c] = 0.0;
-            }
-            a.hit[r] = -1.0;
-        } else {
-            a.hit[r] = hit;
-        }
+        a.hit[r] = bad ? -1.0 : hit;
     }
 }
 
@@ -493,8 +528,8 @@ hipError_t launch_outcome_stats(const OutcomeArgs& a, int dtype, hipStream_t s,
 }
 
 hipError_t launch_outcome_select(const OutcomeArgs& a, hipStream_t s) {
-    const size_t ncand = static_cast<size_t>(a.gamma + 1) * a.nseg * a.kb;
-    const size_t lds = ncand * (sizeof(double) + sizeof(int));
+    const size_t nlists = static_cast<size_t>(a.gamma + 1) * a.nseg;
+    const size_t lds = nlists * a.kb * (sizeof(double) + sizeof(int)) + nlists * sizeof(int);
     hipLaunchKernelGGL(outcome_select_kernel, dim3(a.R), dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
