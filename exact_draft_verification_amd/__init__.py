@@ -22,7 +22,7 @@ __all__ = [
     "SV_DTYPE_F32", "SV_DTYPE_BF16", "SpecVerifyError", "library_path", "load_library",
     "spec_verify_chain", "spec_verify_tree_greedy", "spec_verify_chain_workspace_bytes",
     "spec_verify_chain_pointmass", "spec_verify_chain_pointmass_workspace_bytes",
-    "spec_outcome_topk", "spec_outcome_topk_workspace_bytes",
+    "spec_outcome_topk", "spec_outcome_topk_workspace_bytes", "spec_cache_lookup",
     "spec_verify_tree_greedy_workspace_bytes", "spec_verify_status_string",
 ]
 
@@ -80,6 +80,8 @@ def load_library():
     lib.spec_outcome_topk.restype = I32
     lib.spec_verify_tree_greedy.argtypes = [P, I32, P, P, I32, I32, I32, P, P, P, P, SZ, P, P]
     lib.spec_verify_tree_greedy.restype = I32
+    lib.spec_cache_lookup.argtypes = [P, P, I32, I32, P, P, I32, P, P]
+    lib.spec_cache_lookup.restype = I32
     _lib = lib
     return lib
 
@@ -308,6 +310,32 @@ def spec_outcome_topk(logits, draft_tokens, temperature, ncache, *, out_k=None, 
     if st != 0:
         raise SpecVerifyError(st, "spec_outcome_topk")
     return out_k, out_a, out_p, hit
+
+
+def spec_cache_lookup(accept_len, out_tokens, cache_k, cache_a, *, slot=None, stream=None):
+    """Speculation-cache lookup on the GPU: for each block, the first cache
+    slot whose outcome (k, a) is the verified one (k = accept_len,
+    a = out_tokens[k]), else -1.  accept_len [R], out_tokens [R, gamma+1],
+    cache_k and cache_a [R, ncache], all int32.  Returns slot [R] int32."""
+    torch = _torch()
+    lib = load_library()
+    if out_tokens.dim() != 2 or cache_k.dim() != 2:
+        raise ValueError("out_tokens must be [R, gamma+1] and cache_k [R, ncache]")
+    R, g1 = out_tokens.shape
+    ncache = cache_k.shape[1]
+    dev = out_tokens.device
+    _check(accept_len, "accept_len", (R,), dtype=torch.int32, device=dev)
+    _check(out_tokens, "out_tokens", (R, g1), dtype=torch.int32, device=dev)
+    _check(cache_k, "cache_k", (R, ncache), dtype=torch.int32, device=dev)
+    _check(cache_a, "cache_a", (R, ncache), dtype=torch.int32, device=dev)
+    if slot is None:
+        slot = torch.empty(R, dtype=torch.int32, device=dev)
+    _check(slot, "slot", (R,), dtype=torch.int32, device=dev)
+    st = lib.spec_cache_lookup(_ptr(accept_len), _ptr(out_tokens), R, g1 - 1, _ptr(cache_k),
+                               _ptr(cache_a), ncache, _ptr(slot), _stream_handle(stream, dev))
+    if st != 0:
+        raise SpecVerifyError(st, "spec_cache_lookup")
+    return slot
 
 
 def spec_verify_tree_greedy(target, parents, tokens, *, accept_len=None, accept_node=None,

@@ -350,6 +350,22 @@ extern "C" int32_t spec_outcome_topk(const void* logits, int32_t dtype,
     return SV_OK;
 }
 
+extern "C" int32_t spec_cache_lookup(const int32_t* accept_len, const int32_t* out_tokens,
+                                     int32_t R, int32_t gamma, const int32_t* cache_k,
+                                     const int32_t* cache_a, int32_t ncache, int32_t* slot,
+                                     void* stream) {
+    if (R < 1 || gamma < 1 || gamma > kMaxGamma || ncache < 1 || ncache > kMaxCache)
+        return SV_ERR_SHAPE;
+    if (!accept_len || !out_tokens || !cache_k || !cache_a || !slot) return SV_ERR_NULL;
+    if (!aligned(accept_len, 4) || !aligned(out_tokens, 4) || !aligned(cache_k, 4) ||
+        !aligned(cache_a, 4) || !aligned(slot, 4))
+        return SV_ERR_ALIGN;
+    return launch_cache_lookup(accept_len, out_tokens, R, gamma, cache_k, cache_a, ncache, slot,
+                               static_cast<hipStream_t>(stream)) == hipSuccess
+               ? SV_OK
+               : SV_ERR_HIP;
+}
+
 extern "C" int32_t spec_verify_tree_greedy(const void* target_logits, int32_t dtype,
                                            const int32_t* parents, const int32_t* tokens,
                                            int32_t B, int32_t n, int32_t V, int32_t* accept_len,

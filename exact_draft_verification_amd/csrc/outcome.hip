@@ -511,7 +511,39 @@ __global__ __launch_bounds__(kThreads) void outcome_select_kernel(OutcomeArgs a)
     }
 }
 
+// One thread per request: the verified outcome against the request's cache.
+__global__ __launch_bounds__(kThreads) void cache_lookup_kernel(const int32_t* accept_len,
+                                                                 const int32_t* out_tokens, int R,
+                                                                 int gamma, const int32_t* cache_k,
+                                                                 const int32_t* cache_a, int ncache,
+                                                                 int32_t* slot) {
+    const int r = blockIdx.x * kThreads + threadIdx.x;
+    if (r >= R) return;
+    const int k = accept_len[r];
+    int found = -1;
+    if (k >= 0 && k <= gamma) {
+        const int a = out_tokens[static_cast<int64_t>(r) * (gamma + 1) + k];
+        const int32_t* ck = cache_k + static_cast<int64_t>(r) * ncache;
+        const int32_t* ca = cache_a + static_cast<int64_t>(r) * ncache;
+        for (int c = 0; c < ncache; ++c) {
+            if (ck[c] == k && ca[c] == a) {
+                found = c;
+                break;
+            }
+        }
+    }
+    slot[r] = found;
+}
+
 }  // namespace
+
+hipError_t launch_cache_lookup(const int32_t* accept_len, const int32_t* out_tokens, int R,
+                               int gamma, const int32_t* cache_k, const int32_t* cache_a,
+                               int ncache, int32_t* slot, hipStream_t s) {
+    hipLaunchKernelGGL(cache_lookup_kernel, dim3((R + kThreads - 1) / kThreads), dim3(kThreads),
+                       0, s, accept_len, out_tokens, R, gamma, cache_k, cache_a, ncache, slot);
+    return hipGetLastError();
+}
 
 hipError_t launch_outcome_stats(const OutcomeArgs& a, int dtype, hipStream_t s,
                                 hipEvent_t ev_start, hipEvent_t ev_stop) {

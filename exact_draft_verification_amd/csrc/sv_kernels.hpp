@@ -131,5 +131,8 @@ hipError_t launch_tree_resolve(const TreeArgs& a, hipStream_t s);
 hipError_t launch_outcome_stats(const OutcomeArgs& a, int dtype, hipStream_t s,
                                 hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_outcome_select(const OutcomeArgs& a, hipStream_t s);
+hipError_t launch_cache_lookup(const int32_t* accept_len, const int32_t* out_tokens, int R,
+                               int gamma, const int32_t* cache_k, const int32_t* cache_a,
+                               int ncache, int32_t* slot, hipStream_t s);
 
 }  // namespace sv

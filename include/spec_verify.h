@@ -229,6 +229,25 @@ int32_t spec_outcome_topk(const void *logits, int32_t dtype, const int32_t *draf
                           void *workspace, size_t workspace_bytes, void *stream,
                           void *const *phase_events);
 
+/* Speculation-cache lookup ("JetSpec++", Section 4.2: a block drafted in
+ * advance for the outcome (k, a) becomes the next block when verification
+ * ends in exactly that outcome).  For each of R requests the verified outcome
+ * is k = accept_len[r] and a = out_tokens[r][k]; slot[r] is the index of the
+ * first cache entry with (cache_k, cache_a) = (k, a), or -1 for a miss, for an
+ * invalid block (accept_len = -1) and for k outside [0, gamma].
+ *
+ *  accept_len      [R] int32 and out_tokens [R][gamma+1] int32, as written by
+ *                  spec_verify_chain or spec_verify_chain_pointmass.
+ *  cache_k, cache_a  [R][ncache] int32, as written by spec_outcome_topk for
+ *                  the same block (k = -1 marks an unused slot, which never
+ *                  matches).
+ *  slot            out [R] int32.
+ *  R >= 1, gamma in [1, SV_MAX_GAMMA], ncache in [1, SV_MAX_CACHE]; every
+ *  pointer is a 4-byte aligned device pointer; one kernel on `stream`. */
+int32_t spec_cache_lookup(const int32_t *accept_len, const int32_t *out_tokens, int32_t R,
+                          int32_t gamma, const int32_t *cache_k, const int32_t *cache_a,
+                          int32_t ncache, int32_t *slot, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

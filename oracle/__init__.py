@@ -211,3 +211,27 @@ def tree_greedy(target, parents, tokens, dtype="bf16", threads=None) -> dict:
     if rc != 0:
         raise ValueError("oracle_tree_greedy rejected its arguments")
     return dict(accept_len=acc, accept_node=node, out_tokens=out, amax=amax)
+
+
+def cache_lookup(accept_len, out_tokens, cache_k, cache_a) -> np.ndarray:
+    """The cache slot hit by each verified block ("JetSpec++", Section 4.2:
+    the block drafted for outcome (k, a) is used when verification ends in
+    (k, a)).  The verified outcome is k = accept_len[r], a = out_tokens[r][k];
+    the result is the first slot c with (cache_k, cache_a)[r][c] = (k, a),
+    else -1 (also for an invalid block, accept_len = -1)."""
+    accept_len = np.asarray(accept_len)
+    out_tokens = np.asarray(out_tokens)
+    cache_k = np.asarray(cache_k)
+    cache_a = np.asarray(cache_a)
+    R, g1 = out_tokens.shape
+    slot = np.full(R, -1, dtype=np.int32)
+    for r in range(R):
+        k = int(accept_len[r])
+        if not 0 <= k < g1:
+            continue
+        a = int(out_tokens[r, k])
+        for c in range(cache_k.shape[1]):
+            if cache_k[r, c] == k and cache_a[r, c] == a:
+                slot[r] = c
+                break
+    return slot

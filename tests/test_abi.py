@@ -40,7 +40,8 @@ def test_exports_every_declared_symbol(lib):
     assert {"spec_verify_chain", "spec_verify_tree_greedy", "spec_verify_chain_workspace_bytes",
             "spec_verify_tree_greedy_workspace_bytes", "spec_verify_status_string",
             "spec_verify_chain_pointmass", "spec_verify_chain_pointmass_workspace_bytes",
-            "spec_outcome_topk", "spec_outcome_topk_workspace_bytes"} <= set(names)
+            "spec_outcome_topk", "spec_outcome_topk_workspace_bytes",
+            "spec_cache_lookup"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
@@ -206,6 +207,33 @@ def test_outcome_host_errors(lib):
     assert (k == 0).all() and (hit == 0).all()
     assert sv.spec_outcome_topk_workspace_bytes(32, 16, 151936, 1, 8) > 0
     assert sv.spec_outcome_topk_workspace_bytes(32, 16, 151936, 1, 17) == 0
+
+
+def test_cache_lookup_host_errors(lib):
+    c = header_constants()
+    R, g, nc = 3, 4, 8
+    acc = np.zeros(R, np.int32)
+    out = np.zeros((R, g + 1), np.int32)
+    ck = np.zeros((R, nc), np.int32)
+    ca = np.zeros((R, nc), np.int32)
+    slot = np.full(R, 7, np.int32)
+
+    def call(**o):
+        args = dict(acc=p(acc), out=p(out), R=R, g=g, ck=p(ck), ca=p(ca), nc=nc, slot=p(slot))
+        args.update(o)
+        return lib.spec_cache_lookup(args["acc"], args["out"], args["R"], args["g"], args["ck"],
+                                     args["ca"], args["nc"], args["slot"], None)
+
+    assert call(acc=None) == c["SV_ERR_NULL"]
+    assert call(ca=None) == c["SV_ERR_NULL"]
+    assert call(slot=None) == c["SV_ERR_NULL"]
+    assert call(R=0) == c["SV_ERR_SHAPE"]
+    assert call(g=0) == c["SV_ERR_SHAPE"]
+    assert call(g=c["SV_MAX_GAMMA"] + 1) == c["SV_ERR_SHAPE"]
+    assert call(nc=0) == c["SV_ERR_SHAPE"]
+    assert call(nc=c["SV_MAX_CACHE"] + 1) == c["SV_ERR_SHAPE"]
+    assert call(out=ct.c_void_p(out.ctypes.data + 2)) == c["SV_ERR_ALIGN"]
+    assert (slot == 7).all()  # nothing was written
 
 
 def test_tree_host_errors(lib):

@@ -118,3 +118,38 @@ def test_hit_probability_grows_with_cache_size():
         h = oracle.outcome_topk(z, d, 0.8, ncache=B)["hit"]
         assert (h >= prev - 1e-15).all() and (h <= 1 + 1e-12).all()
         prev = h
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_lookup_hit_rate_is_the_cache_hit_probability(seed):
+    """Sampling the point-mass verification of one block many times and
+    looking each outcome up in the block's cache hits slot c with probability
+    p_c, and some slot with the cache's hit probability (Proposition 1: the
+    verified outcome has law P(k, a)).  Three oracle functions are checked
+    against each other; N = 40000 draws, bounds of 5 standard deviations."""
+    rng = np.random.default_rng(500 + seed)
+    V, g, B, N = 40, 3, 6, 40000
+    z = f32(rng.normal(0, 1.5, (g + 1, V)))
+    z[:, 0] += 2.0  # a likely draft token
+    d = np.zeros(g, np.int32)
+    cache = oracle.outcome_topk(z[None], d[None], 0.8, ncache=B)
+    u = rng.random((N, g + 1), dtype=np.float32)
+    ver = oracle.chain_pointmass(np.broadcast_to(z, (N, g + 1, V)).copy(),
+                                 np.broadcast_to(d, (N, g)).copy(), u, 0.8)
+    slot = oracle.cache_lookup(ver["accept_len"], ver["out_tokens"],
+                               np.broadcast_to(cache["k"], (N, B)), np.broadcast_to(cache["a"], (N, B)))
+    h = cache["hit"][0]
+    assert abs((slot >= 0).mean() - h) < 5 * np.sqrt(h * (1 - h) / N)
+    for c in range(B):
+        pc = cache["p"][0, c]
+        assert abs((slot == c).mean() - pc) < 5 * np.sqrt(pc * (1 - pc) / N) + 1e-12, c
+
+
+def test_lookup_cases():
+    """Definition cases: the first matching slot wins, unused slots (-1) and
+    invalid blocks never match, and a is the token after the k accepted ones."""
+    acc = np.array([2, 0, -1, 3], np.int32)
+    out = np.array([[5, 6, 7, -1], [9, -1, -1, -1], [-1, -1, -1, -1], [1, 2, 3, 4]], np.int32)
+    ck = np.array([[2, 2, -1], [0, 1, -1], [-1, -1, -1], [3, 3, 0]], np.int32)
+    ca = np.array([[6, 7, -1], [9, 9, -1], [-1, -1, -1], [3, 4, 4]], np.int32)
+    assert oracle.cache_lookup(acc, out, ck, ca).tolist() == [1, 0, -1, 1]
