@@ -57,9 +57,10 @@ def _declare(lib):
     lib.oracle_chain_pointmass.argtypes = [P, I, P, P, I, I, I, D, P, P, P, P, P, P, I]
     lib.oracle_chain_pointmass_du.argtypes = [P, I, P, P, I, I, I, D, P, P, P, P, P, P, I]
     lib.oracle_outcome_topk.argtypes = [P, I, P, I, I, I, D, I, P, P, P, P, P]
+    lib.oracle_tree_build.argtypes = [P, I, I, I, I, D, I, I, I, P, P, P, P, P, P, P]
     for f in (lib.oracle_chain, lib.oracle_chain_du, lib.oracle_chain_alpha,
               lib.oracle_tree_greedy, lib.oracle_chain_pointmass, lib.oracle_chain_pointmass_du,
-              lib.oracle_outcome_topk):
+              lib.oracle_outcome_topk, lib.oracle_tree_build):
         f.restype = I
     return lib
 
@@ -212,6 +213,34 @@ def tree_greedy(target, parents, tokens, dtype="bf16", threads=None) -> dict:
         raise ValueError("oracle_tree_greedy rejected its arguments")
     return dict(accept_len=acc, accept_node=node, out_tokens=out, amax=amax)
 
+
+
+def tree_build(logits, T, W, N, budget, child_row=None, dtype="f32") -> dict:
+    """Best-first construction of a draft tree from per-potential-node draft
+    logits [R, M, V] ("JetSpec" reading notes, Algorithm 1 and Eq. 15).
+    Returns parents, tokens, rows [R, budget] int32 (-1 past the end and for
+    the root's parent and token), score [R, budget] float64 (natural log,
+    -inf past the end), n [R] (-1 for an invalid request) and min_gap [R]
+    (the smallest score gap behind an expansion decision)."""
+    lib = _load()
+    logits = _logits(logits, dtype)
+    R, M, V = logits.shape
+    cr = None
+    if child_row is not None:
+        cr = np.ascontiguousarray(child_row, dtype=np.int32)
+        assert cr.shape == (M, W)
+    par = np.empty((R, budget), np.int32)
+    tok = np.empty((R, budget), np.int32)
+    rows = np.empty((R, budget), np.int32)
+    sc = np.empty((R, budget), np.float64)
+    n = np.empty(R, np.int32)
+    gap = np.empty(R, np.float64)
+    rc = lib.oracle_tree_build(_ptr(logits), _DT[dtype], R, M, V, float(T), int(W), int(N),
+                               int(budget), _ptr(cr), _ptr(par), _ptr(tok), _ptr(rows), _ptr(sc),
+                               _ptr(n), _ptr(gap))
+    if rc != 0:
+        raise ValueError(f"oracle_tree_build rejected its arguments (rc={rc})")
+    return dict(parents=par, tokens=tok, rows=rows, score=sc, n=n, min_gap=gap)
 
 def cache_lookup(accept_len, out_tokens, cache_k, cache_a) -> np.ndarray:
     """The cache slot hit by each verified block ("JetSpec++", Section 4.2:

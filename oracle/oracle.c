@@ -807,3 +807,149 @@ int oracle_tree_greedy(const void *target, int dtype, const int32_t *parents,
     free(args);
     return 0;
 }
+
+/* ----------------------------------------------------------------------
+ * Tree construction by best-first search ([JN] Algorithm 1, with the branch
+ * score of Eq. 15).
+ *
+ * Each request has M rows of draft logits, one per potential node: row m is
+ * the draft distribution q_m (softmax at temperature T) of the token that
+ * follows potential node m's path, and row 0 belongs to the root (the
+ * verified prefix).  The pages have the draft head produce these rows in one
+ * pass before the search starts.  C(v), the candidate children of a node
+ * whose row is m, are the W most probable tokens of q_m (ties: the smaller
+ * token id; tokens of probability 0 are not candidates).  The child reached
+ * through the j-th of them has row child_row[m][j] (-1: it has no row and is
+ * never expanded).  With child_row NULL the potential nodes are numbered
+ * breadth first in a complete W-ary tree: child j of row m has row
+ * m*W + 1 + j if that is below M, else none.
+ *
+ * The search: the tree starts as the root alone (node 0, depth 0, score 0)
+ * and the queue holds the root.  While the tree has fewer than `budget` nodes
+ * and the queue is not empty, the node with the highest score leaves the
+ * queue (ties: the smaller node index, i.e. the one added first).  A node at
+ * depth N or without a row is not expanded.  Otherwise each candidate child y
+ * in turn is added to the tree -- next node index, parent v, token y, score
+ * s_v + ln q_m(y), the sum of the draft log probabilities along the path
+ * ([JN] Eq. 15) -- and enters the queue, until the tree holds `budget` nodes.
+ *
+ * Outputs per request ([R][budget]): parents (root -1), tokens (root -1),
+ * node_row (-1 for none), score (natural log; -inf past the end), and
+ * n_nodes [R]; past the end parents, tokens and node_row are -1.  An invalid
+ * request (a NaN or +inf logit, a row without a finite logit, or the |m|/T
+ * domain, in any of its M rows) gets n_nodes = -1 and every node output
+ * -1 / -inf; a child_row entry outside [-1, M) makes every request invalid.
+ * min_gap (nullable, [R]) receives, over the pops that expand a node, the
+ * smallest difference between the popped score and the score of any other
+ * expandable node in the queue, leaving out exact ties between siblings
+ * (equal logits in one row tie exactly in any arithmetic); +inf if there is
+ * none.  A small gap marks an order that rounding elsewhere may swap.
+ */
+int oracle_tree_build(const void *logits, int dtype, int R, int M, int V, double T, int W, int N,
+                      int budget, const int32_t *child_row, int32_t *parents, int32_t *tokens,
+                      int32_t *node_row, double *score, int32_t *n_nodes, double *min_gap)
+{
+    if (!logits || !parents || !tokens || !node_row || !score || !n_nodes)
+        return -1;
+    if (R < 1 || M < 1 || V < 1 || W < 1 || N < 1 || budget < 1 || !(T > 0.0) || !isfinite(T))
+        return -1;
+    if (dtype != ORC_F32 && dtype != ORC_BF16)
+        return -1;
+    int map_ok = 1;
+    if (child_row)
+        for (int64_t i = 0; i < (int64_t)M * W; ++i)
+            map_ok &= (child_row[i] >= -1 && child_row[i] < M);
+    double *m = malloc(sizeof(double) * (size_t)M);
+    double *S = malloc(sizeof(double) * (size_t)M);
+    int *depth = malloc(sizeof(int) * (size_t)budget);
+    char *inq = malloc((size_t)budget);
+    int *ctok = malloc(sizeof(int) * (size_t)W);
+    char *taken = malloc((size_t)V);
+    if (!m || !S || !depth || !inq || !ctok || !taken)
+        return -2;
+    for (int r = 0; r < R; ++r) {
+        const int64_t o = (int64_t)r * budget;
+        int32_t *par = parents + o, *tok = tokens + o, *row = node_row + o;
+        double *sc = score + o;
+        for (int i = 0; i < budget; ++i) {
+            par[i] = tok[i] = row[i] = -1;
+            sc[i] = -INFINITY;
+        }
+        n_nodes[r] = -1;
+        if (min_gap)
+            min_gap[r] = INFINITY;
+        const int64_t base = (int64_t)r * M * V;
+        int bad = !map_ok;
+        for (int j = 0; j < M && !bad; ++j)
+            bad |= row_softmax_stats(logits, dtype, base + (int64_t)j * V, V, T, &m[j], &S[j]);
+        if (bad)
+            continue;
+        int n = 1;
+        row[0] = 0;
+        sc[0] = 0.0;
+        depth[0] = 0;
+        inq[0] = 1;
+        double gap = INFINITY;
+        while (n < budget) {
+            int v = -1;
+            for (int u = 0; u < n; ++u)
+                if (inq[u] && (v < 0 || sc[u] > sc[v]))
+                    v = u;
+            if (v < 0)
+                break;
+            inq[v] = 0;
+            if (depth[v] >= N || row[v] < 0)
+                continue;
+            for (int u = 0; u < n; ++u) {
+                if (!inq[u] || depth[u] >= N || row[u] < 0)
+                    continue;
+                if (par[u] == par[v] && sc[u] == sc[v])
+                    continue;
+                if (sc[v] - sc[u] < gap)
+                    gap = sc[v] - sc[u];
+            }
+            /* C(v): the W most probable tokens of the row, by selection */
+            const int64_t off = base + (int64_t)row[v] * V;
+            memset(taken, 0, (size_t)V);
+            int nc = 0;
+            for (int j = 0; j < W; ++j) {
+                int best = -1;
+                double bz = -INFINITY;
+                for (int y = 0; y < V; ++y) {
+                    const double z = logit_at(logits, dtype, off + y);
+                    if (!taken[y] && z > bz) {
+                        bz = z;
+                        best = y;
+                    }
+                }
+                if (best < 0)
+                    break; /* only probability-0 tokens are left */
+                taken[best] = 1;
+                ctok[nc++] = best;
+            }
+            for (int j = 0; j < nc && n < budget; ++j) {
+                const int u = n++;
+                const int mr = row[v];
+                par[u] = v;
+                tok[u] = ctok[j];
+                if (child_row)
+                    row[u] = child_row[(int64_t)mr * W + j];
+                else
+                    row[u] = ((int64_t)mr * W + 1 + j < M) ? mr * W + 1 + j : -1;
+                depth[u] = depth[v] + 1;
+                sc[u] = sc[v] + logprob_at(logits, dtype, off, ctok[j], T, m[mr], S[mr]);
+                inq[u] = 1;
+            }
+        }
+        n_nodes[r] = n;
+        if (min_gap)
+            min_gap[r] = gap;
+    }
+    free(m);
+    free(S);
+    free(depth);
+    free(inq);
+    free(ctok);
+    free(taken);
+    return 0;
+}
