@@ -23,6 +23,7 @@ __all__ = [
     "spec_verify_chain", "spec_verify_tree_greedy", "spec_verify_chain_workspace_bytes",
     "spec_verify_chain_pointmass", "spec_verify_chain_pointmass_workspace_bytes",
     "spec_outcome_topk", "spec_outcome_topk_workspace_bytes", "spec_cache_lookup",
+    "spec_tree_build", "spec_tree_build_workspace_bytes",
     "spec_verify_tree_greedy_workspace_bytes", "spec_verify_status_string",
 ]
 
@@ -82,6 +83,11 @@ def load_library():
     lib.spec_verify_tree_greedy.restype = I32
     lib.spec_cache_lookup.argtypes = [P, P, I32, I32, P, P, I32, P, P]
     lib.spec_cache_lookup.restype = I32
+    lib.spec_tree_build_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
+    lib.spec_tree_build_workspace_bytes.restype = SZ
+    lib.spec_tree_build.argtypes = [P, I32, P, I32, I32, I32, D, I32, I32, I32, P, P, P, P, P, P,
+                                    SZ, P, P]
+    lib.spec_tree_build.restype = I32
     _lib = lib
     return lib
 
@@ -100,6 +106,11 @@ def spec_verify_chain_pointmass_workspace_bytes(B: int, gamma: int, V: int, dtyp
 
 def spec_outcome_topk_workspace_bytes(R: int, gamma: int, V: int, dtype: int, ncache: int) -> int:
     return int(load_library().spec_outcome_topk_workspace_bytes(R, gamma, V, dtype, ncache))
+
+
+def spec_tree_build_workspace_bytes(R: int, M: int, V: int, dtype: int, W: int, max_depth: int,
+                                    budget: int) -> int:
+    return int(load_library().spec_tree_build_workspace_bytes(R, M, V, dtype, W, max_depth, budget))
 
 
 def spec_verify_tree_greedy_workspace_bytes(B: int, n: int, V: int, dtype: int) -> int:
@@ -310,6 +321,53 @@ def spec_outcome_topk(logits, draft_tokens, temperature, ncache, *, out_k=None, 
     if st != 0:
         raise SpecVerifyError(st, "spec_outcome_topk")
     return out_k, out_a, out_p, hit
+
+
+def spec_tree_build(draft_logits, temperature, width, max_depth, budget, *, child_row=None,
+                    parents=None, tokens=None, node_row=None, score=None, n_nodes=None,
+                    workspace=None, stream=None, phase_events=None):
+    """Best-first draft-tree construction on the GPU.
+
+    draft_logits [R, M, V] (float32 or bfloat16): one row per potential node;
+    child_row optional int32 [M, width].  Returns (parents, tokens, node_row
+    [R, budget] int32, score [R, budget] float64, n_nodes [R] int32)."""
+    torch = _torch()
+    lib = load_library()
+    if draft_logits.dim() != 3:
+        raise ValueError("draft_logits must be [R, M, V]")
+    R, M, V = draft_logits.shape
+    dev = draft_logits.device
+    code = _dtype_code(draft_logits)
+    W, budget = int(width), int(budget)
+    _check(draft_logits, "draft_logits", (R, M, V), device=dev)
+    if child_row is not None:
+        _check(child_row, "child_row", (M, W), dtype=torch.int32, device=dev)
+
+    def out(t, name, shape, dt):
+        if t is None:
+            t = torch.empty(shape, dtype=dt, device=dev)
+        _check(t, name, shape, dtype=dt, device=dev)
+        return t
+
+    parents = out(parents, "parents", (R, budget), torch.int32)
+    tokens = out(tokens, "tokens", (R, budget), torch.int32)
+    node_row = out(node_row, "node_row", (R, budget), torch.int32)
+    score = out(score, "score", (R, budget), torch.float64)
+    n_nodes = out(n_nodes, "n_nodes", (R,), torch.int32)
+    need = spec_tree_build_workspace_bytes(R, M, V, code, W, int(max_depth), budget)
+    if need == 0:
+        raise SpecVerifyError(2, "spec_tree_build")
+    if workspace is None:
+        workspace = _workspace(need, dev, stream)
+    ev = _events(phase_events)
+    st = lib.spec_tree_build(_ptr(draft_logits), code, _ptr(child_row), R, M, V, float(temperature),
+                             W, int(max_depth), budget, _ptr(parents), _ptr(tokens), _ptr(node_row),
+                             _ptr(score), _ptr(n_nodes), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(),
+                             _stream_handle(stream, dev), None if ev is None else ev[0])
+    if st != 0:
+        raise SpecVerifyError(st, "spec_tree_build")
+    return parents, tokens, node_row, score, n_nodes
 
 
 def spec_cache_lookup(accept_len, out_tokens, cache_k, cache_a, *, slot=None, stream=None):

@@ -145,6 +145,35 @@ int32_t outcome_plan(int32_t R, int32_t gamma, int32_t V, int32_t dtype, int32_t
     return SV_OK;
 }
 
+struct TreeBuildPlan {
+    int nseg, seg_len, kb;
+    size_t off_part, off_cand, off_tok, off_lq, off_ok, bytes;
+};
+
+int32_t tree_build_plan(int32_t R, int32_t M, int32_t V, int32_t dtype, int32_t W,
+                        int32_t max_depth, int32_t budget, TreeBuildPlan* p) {
+    if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
+    if (R < 1 || M < 1 || V < 1 || W < 1 || W > kMaxTreeWidth || max_depth < 1 || budget < 1 ||
+        budget > kMaxTreeNodes || static_cast<int64_t>(M) * W > kMaxTreeSlots)
+        return SV_ERR_SHAPE;
+    const int E = elem_bytes(dtype), epv = 16 / E;
+    const int64_t rows_total = static_cast<int64_t>(R) * M;
+    if (static_cast<double>(rows_total) * V * E > 9.0e18) return SV_ERR_SHAPE;
+    p->kb = W <= 4 ? 4 : (W <= 8 ? 8 : 16);
+    // a row's segments are merged one lane each
+    plan_segments(rows_total, V, epv, kOutcomeUnits, 16, kMaxTreeSegs, &p->nseg, &p->seg_len);
+    if (rows_total * p->nseg > INT32_MAX) return SV_ERR_SHAPE;
+    const size_t nr = static_cast<size_t>(rows_total);
+    size_t off = 0;
+    p->off_part = carve(&off, sizeof(Stat), nr * p->nseg);
+    p->off_cand = carve(&off, sizeof(OutcomeCand), nr * p->nseg * p->kb);
+    p->off_tok = carve(&off, sizeof(int32_t), nr * W);
+    p->off_lq = carve(&off, sizeof(float), nr * W);
+    p->off_ok = carve(&off, sizeof(int32_t), nr);
+    p->bytes = off;
+    return SV_OK;
+}
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 hipEvent_t event_at(void* const* ev, int i) {
@@ -347,6 +376,77 @@ extern "C" int32_t spec_outcome_topk(const void* logits, int32_t dtype,
         hipSuccess)
         return SV_ERR_HIP;
     if (launch_outcome_select(a, s) != hipSuccess) return SV_ERR_HIP;
+    return SV_OK;
+}
+
+extern "C" size_t spec_tree_build_workspace_bytes(int32_t R, int32_t M, int32_t V, int32_t dtype,
+                                                  int32_t W, int32_t max_depth, int32_t budget) {
+    TreeBuildPlan p;
+    return tree_build_plan(R, M, V, dtype, W, max_depth, budget, &p) == SV_OK ? p.bytes : 0;
+}
+
+extern "C" int32_t spec_tree_build(const void* draft_logits, int32_t dtype,
+                                   const int32_t* child_row, int32_t R, int32_t M, int32_t V,
+                                   double temperature, int32_t W, int32_t max_depth,
+                                   int32_t budget, int32_t* parents, int32_t* tokens,
+                                   int32_t* node_row, double* score, int32_t* n_nodes,
+                                   void* workspace, size_t workspace_bytes, void* stream,
+                                   void* const* phase_events) {
+    TreeBuildPlan p;
+    int32_t st = tree_build_plan(R, M, V, dtype, W, max_depth, budget, &p);
+    if (st != SV_OK) return st;
+    if (!draft_logits || !parents || !tokens || !node_row || !score || !n_nodes || !workspace)
+        return SV_ERR_NULL;
+    if (!std::isfinite(temperature) || temperature < 1e-6 || temperature > 1e6)
+        return SV_ERR_TEMPERATURE;
+    const size_t E = static_cast<size_t>(elem_bytes(dtype));
+    if (!aligned(draft_logits, E) || (child_row && !aligned(child_row, 4)) ||
+        !aligned(parents, 4) || !aligned(tokens, 4) || !aligned(node_row, 4) ||
+        !aligned(score, 8) || !aligned(n_nodes, 4))
+        return SV_ERR_ALIGN;
+    if (!aligned(workspace, 16) || workspace_bytes < p.bytes) return SV_ERR_WORKSPACE;
+    TreeBuildArgs a;
+    OutcomeArgs& o = a.st;
+    o = OutcomeArgs{};
+    o.logits = draft_logits;
+    o.tokens = nullptr;  // no token is excluded from a row's candidates
+    o.R = R;
+    o.gamma = M - 1;  // M rows per request
+    o.V = V;
+    const double c = 1.4426950408889634074 / temperature;
+    float c_hi = static_cast<float>(c);
+    if (static_cast<double>(c_hi) >= c) c_hi = std::nextafter(c_hi, 0.0f);
+    o.c_hi = c_hi;
+    o.c_lo = static_cast<float>(c - static_cast<double>(c_hi));
+    o.c_d = static_cast<double>(o.c_hi) + static_cast<double>(o.c_lo);
+    o.T = temperature;
+    o.nseg = p.nseg;
+    o.seg_len = p.seg_len;
+    o.ncache = W;
+    o.kb = p.kb;
+    char* ws = static_cast<char*>(workspace);
+    o.part = reinterpret_cast<Stat*>(ws + p.off_part);
+    o.cand = reinterpret_cast<OutcomeCand*>(ws + p.off_cand);
+    o.zx = nullptr;  // written only for rows with a draft token
+    a.child_row = child_row;
+    a.M = M;
+    a.W = W;
+    a.max_depth = max_depth;
+    a.budget = budget;
+    a.rt_tok = reinterpret_cast<int32_t*>(ws + p.off_tok);
+    a.rt_lq = reinterpret_cast<float*>(ws + p.off_lq);
+    a.rt_ok = reinterpret_cast<int32_t*>(ws + p.off_ok);
+    a.parents = parents;
+    a.tokens = tokens;
+    a.node_row = node_row;
+    a.score = score;
+    a.n_nodes = n_nodes;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (launch_outcome_stats(o, dtype, s, event_at(phase_events, 0), event_at(phase_events, 1)) !=
+        hipSuccess)
+        return SV_ERR_HIP;
+    if (launch_tree_rows(a, s) != hipSuccess) return SV_ERR_HIP;
+    if (launch_tree_search(a, s) != hipSuccess) return SV_ERR_HIP;
     return SV_OK;
 }
 

@@ -38,35 +38,6 @@ namespace {
 constexpr double kDomain = 268435456.0;  // |m| / T limit (2^28)
 constexpr float kNegInf = -INFINITY;
 
-// Candidate keys: unsigned 64-bit integers ordered like the candidates
-// (value descending, then index ascending).  The high word maps the float
-// value monotonically (-0 counts as +0, as in a float comparison), the low
-// word is 0xffffffff - index.  Key 0 is below every real key and means none.
-__device__ inline uint32_t value_key(float f) {
-    uint32_t u = __float_as_uint(f);
-    if (u == 0x80000000u) u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ inline float key_value(uint64_t k) {
-    const uint32_t u = static_cast<uint32_t>(k >> 32);
-    return __uint_as_float((u & 0x80000000u) ? (u ^ 0x80000000u) : ~u);
-}
-__device__ inline uint64_t make_key(float v, uint32_t idx) {
-    return (static_cast<uint64_t>(value_key(v)) << 32) | (0xffffffffu - idx);
-}
-__device__ inline uint32_t key_index(uint64_t k) { return 0xffffffffu - static_cast<uint32_t>(k); }
-
-__device__ inline uint64_t readlane64(uint64_t x, int l) {
-    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(x), l);
-    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(x >> 32), l);
-    return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-__device__ inline uint64_t uniform64(uint64_t x) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<int>(x));
-    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<int>(x >> 32));
-    return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
 // Descending bitonic sort of one key per lane over the 64 lanes of a wave.
 __device__ inline uint64_t wave_sort_desc(uint64_t x) {
     const int lane = threadIdx.x & 63;
@@ -259,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void outcome_stats_kernel(OutcomeArgs a) 
     if (tid == 0) s_th = 0;
     if (tid < L * P) s_ck[tid] = 0;
     int excl = -1;
-    if (k < a.gamma) excl = a.tokens[static_cast<int64_t>(r) * a.gamma + k];
+    if (k < a.gamma && a.tokens) excl = a.tokens[static_cast<int64_t>(r) * a.gamma + k];
     // the draft token's logit, if this segment holds it
     float zx = 0.0f;
     const bool have_zx = tid == 0 && excl >= e0 && excl < e1;
@@ -343,41 +314,6 @@ __global__ __launch_bounds__(kThreads) void outcome_stats_kernel(OutcomeArgs a) 
 // one wave: each lane owns some lists, one wave-wide maximum of
 // (score desc, i asc) per kept outcome, after which only the winning list
 // advances.
-__device__ inline bool cand_ahead(double s1, int i1, double s2, int i2) {
-    return s1 > s2 || (s1 == s2 && s1 > -INFINITY && i1 < i2);
-}
-
-// One step of a wave-wide maximum over DPP lane moves (lanes outside the
-// move keep their own value).
-template <int CTRL, int ROWS>
-__device__ inline void dpp_max_step(double& s, int& i) {
-    const int lo = __double2loint(s), hi = __double2hiint(s);
-    const int olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xf, false);
-    const int ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xf, false);
-    const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROWS, 0xf, false);
-    const double os = __hiloint2double(ohi, olo);
-    if (cand_ahead(os, oi, s, i)) {
-        s = os;
-        i = oi;
-    }
-}
-
-// The wave's best (score, i); every lane gets it.  Quad swaps, half-row and
-// row mirrors leave each row of 16 lanes with its best, the two row
-// broadcasts carry it to lane 63.
-__device__ inline void wave_best(double& s, int& i) {
-    dpp_max_step<0xb1, 0xf>(s, i);   // quad_perm [1,0,3,2]
-    dpp_max_step<0x4e, 0xf>(s, i);   // quad_perm [2,3,0,1]
-    dpp_max_step<0x141, 0xf>(s, i);  // row_half_mirror
-    dpp_max_step<0x140, 0xf>(s, i);  // row_mirror
-    dpp_max_step<0x142, 0xa>(s, i);  // row_bcast:15 into rows 1 and 3
-    dpp_max_step<0x143, 0xc>(s, i);  // row_bcast:31 into rows 2 and 3
-    const int lo = __builtin_amdgcn_readlane(__double2loint(s), 63);
-    const int hi = __builtin_amdgcn_readlane(__double2hiint(s), 63);
-    i = __builtin_amdgcn_readlane(i, 63);
-    s = __hiloint2double(hi, lo);
-}
-
 __global__ __launch_bounds__(kThreads) void outcome_select_kernel(OutcomeArgs a) {
     extern __shared__ unsigned char s_dyn[];
     __shared__ double s_L[kMaxGamma + 1];

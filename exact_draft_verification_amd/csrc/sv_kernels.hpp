@@ -98,7 +98,7 @@ constexpr int kMaxCache = 16;  // cache entries per request
 
 struct OutcomeArgs {
     const void* logits;      // [R][gamma+1][V]
-    const int32_t* tokens;   // [R][gamma]
+    const int32_t* tokens;   // [R][gamma]; null: no token is excluded
     int R, gamma, V;
     float c_hi, c_lo;
     double c_d;
@@ -113,6 +113,26 @@ struct OutcomeArgs {
     int32_t* out_a;          // [R][ncache]
     double* out_p;           // [R][ncache]
     double* hit;             // [R]
+};
+
+// Draft-tree construction: per-potential-node draft logits, the W best
+// children of every row, then a best-first search per request.
+constexpr int kMaxTreeWidth = 16;     // children per node
+constexpr int kMaxTreeSlots = 2048;   // M * W (the search stages every row's children)
+constexpr int kMaxTreeSegs = 64;      // segments per row (one lane each when merged)
+
+struct TreeBuildArgs {
+    OutcomeArgs st;          // statistics pass over the rows (no draft tokens)
+    const int32_t* child_row;  // [M][W] or null (complete W-ary numbering)
+    int M, W, max_depth, budget;
+    int32_t* rt_tok;         // [R][M][W] child tokens (-1: none)
+    float* rt_lq;            // [R][M][W] their ln q
+    int32_t* rt_ok;          // [R][M] 1 if the row is valid
+    int32_t* parents;        // [R][budget]
+    int32_t* tokens;         // [R][budget]
+    int32_t* node_row;       // [R][budget]
+    double* score;           // [R][budget]
+    int32_t* n_nodes;        // [R]
 };
 
 // Launchers (return the hipError_t of the launch).
@@ -131,6 +151,8 @@ hipError_t launch_tree_resolve(const TreeArgs& a, hipStream_t s);
 hipError_t launch_outcome_stats(const OutcomeArgs& a, int dtype, hipStream_t s,
                                 hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_outcome_select(const OutcomeArgs& a, hipStream_t s);
+hipError_t launch_tree_rows(const TreeBuildArgs& a, hipStream_t s);
+hipError_t launch_tree_search(const TreeBuildArgs& a, hipStream_t s);
 hipError_t launch_cache_lookup(const int32_t* accept_len, const int32_t* out_tokens, int R,
                                int gamma, const int32_t* cache_k, const int32_t* cache_a,
                                int ncache, int32_t* slot, hipStream_t s);

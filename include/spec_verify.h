@@ -229,6 +229,56 @@ int32_t spec_outcome_topk(const void *logits, int32_t dtype, const int32_t *draf
                           void *workspace, size_t workspace_bytes, void *stream,
                           void *const *phase_events);
 
+/* Children per node, and rows times children, of spec_tree_build. */
+#define SV_MAX_TREE_WIDTH 16
+#define SV_MAX_TREE_SLOTS 2048
+
+/* Bytes of workspace spec_tree_build needs; 0 if the arguments are invalid. */
+size_t spec_tree_build_workspace_bytes(int32_t R, int32_t M, int32_t V, int32_t dtype, int32_t W,
+                                       int32_t max_depth, int32_t budget);
+
+/* Draft-tree construction by best-first search ("JetSpec" reading notes,
+ * Algorithm 1, with the branch score of Eq. 15).  For each of R requests the
+ * draft head has produced one row of logits per potential node: row m is the
+ * draft distribution q_m = softmax(row_m / T) of the token after potential
+ * node m's path, and row 0 belongs to the root (the verified prefix).  The
+ * candidate children of a node whose row is m are the W most probable tokens
+ * of q_m (ties: smaller token id; tokens of probability 0 are not
+ * candidates); the child through the j-th of them has row child_row[m][j]
+ * (-1: none).  The tree starts as the root (node 0, score 0); repeatedly the
+ * queued node of highest score (ties: the one added first) is expanded --
+ * each of its candidate children in order becomes the next node, with parent
+ * the expanded node and score = parent's score + ln q_m(token) -- until the
+ * tree holds `budget` nodes or nothing is left to expand.  Nodes at depth
+ * max_depth and nodes without a row are never expanded.
+ *
+ *  draft_logits  [R][M][V] dtype (f32 or bf16 bits).
+ *  child_row     NULLABLE [M][W] int32, shared by all requests, entries in
+ *                [-1, M); NULL numbers the potential nodes breadth first in a
+ *                complete W-ary tree: child j of row m has row m*W + 1 + j if
+ *                that is below M, else none.
+ *  temperature   T > 0 (finite, in [1e-6, 1e6]); W in [1, SV_MAX_TREE_WIDTH];
+ *                M*W <= SV_MAX_TREE_SLOTS; max_depth >= 1; budget in
+ *                [1, SV_MAX_TREE_NODES] (the root counts).
+ *  parents, tokens, node_row  out [R][budget] int32: node j's parent (root
+ *                -1; 0 <= parents[j] < j), token (root -1) and row (-1: none);
+ *                -1 past the last node.  This is the parent/token layout
+ *                spec_verify_tree_greedy takes.
+ *  score         out [R][budget] double: the node's score (natural log; root
+ *                0; -inf past the last node).
+ *  n_nodes       out [R] int32: the number of nodes, or -1 for an invalid
+ *                request (a NaN or +inf logit, a row without a finite logit,
+ *                or |max finite logit| / T > 2^28 in any of its M rows, or a
+ *                child_row entry outside [-1, M)), whose outputs are then all
+ *                -1 / -inf.
+ *  workspace, stream, phase_events: as for spec_verify_tree_greedy (the two
+ *  events bracket the one pass over the logits). */
+int32_t spec_tree_build(const void *draft_logits, int32_t dtype, const int32_t *child_row,
+                        int32_t R, int32_t M, int32_t V, double temperature, int32_t W,
+                        int32_t max_depth, int32_t budget, int32_t *parents, int32_t *tokens,
+                        int32_t *node_row, double *score, int32_t *n_nodes, void *workspace,
+                        size_t workspace_bytes, void *stream, void *const *phase_events);
+
 /* Speculation-cache lookup ("JetSpec++", Section 4.2: a block drafted in
  * advance for the outcome (k, a) becomes the next block when verification
  * ends in exactly that outcome).  For each of R requests the verified outcome

@@ -291,6 +291,71 @@ def outcome_config_bytes(**overrides) -> int:
     return c["R"] * (c["gamma"] + 1) * c["V"] * e
 
 
+# Draft-tree construction: one row of draft logits per potential node of a
+# complete W-ary tree above depth N, so M = 1 + W + ... + W^(N-1) rows.
+TREEBUILD_CONFIG = dict(R=32, W=4, N=4, budget=64, V=151936, dtype="bf16", T=1.0,
+                        logits=("gumbel", 3.0))
+
+
+def complete_tree_rows(W: int, N: int) -> int:
+    """Rows of the potential nodes above depth N in a complete W-ary tree."""
+    return sum(W ** d for d in range(N))
+
+
+def _treebuild_request(seed_seq, M, V, dtype, logits):
+    rng = np.random.default_rng(seed_seq)
+    kind, scale = logits
+    if kind == "normal":
+        z = rng.standard_normal((M, V), dtype=np.float32) * np.float32(scale)
+    elif kind == "gumbel":
+        z = _gumbel(rng, (M, V)) * np.float32(scale)
+    else:
+        raise ValueError(f"unknown logit distribution {kind!r}")
+    return _store(z, dtype)
+
+
+def treebuild_inputs(R: int, M: int, V: int, dtype: str = "f32", T: float = 1.0,
+                     logits=("normal", 2.0), seed: int = 0, threads: int | None = None) -> dict:
+    """Draft logits [R, M, V] for tree construction: independent rows, one per
+    potential node."""
+    if R < 1 or M < 1 or V < 1:
+        raise ValueError("R, M and V must be >= 1")
+    st = np.uint16 if dtype == "bf16" else np.float32
+    z = np.empty((R, M, V), dtype=st)
+    children = np.random.SeedSequence(seed).spawn(R)
+
+    def work(r):
+        z[r] = _treebuild_request(children[r], M, V, dtype, logits)
+
+    nw = _workers(R, threads)
+    if nw == 1:
+        for r in range(R):
+            work(r)
+    else:
+        with _cf.ThreadPoolExecutor(nw) as ex:
+            list(ex.map(work, range(R)))
+    return dict(kind="treebuild", logits=z, R=R, M=M, V=V, dtype=dtype, T=float(T))
+
+
+def treebuild_config_inputs(seed: int = 0, threads: int | None = None, **overrides) -> dict:
+    """The tree-construction workload: R requests, width W, depth N, budget."""
+    c = dict(TREEBUILD_CONFIG)
+    c.update(overrides)
+    M = complete_tree_rows(c["W"], c["N"])
+    d = treebuild_inputs(c["R"], M, c["V"], c["dtype"], c["T"], c["logits"], seed=seed,
+                         threads=threads)
+    d.update(W=c["W"], N=c["N"], budget=c["budget"])
+    return d
+
+
+def treebuild_config_bytes(**overrides) -> int:
+    """Algorithmic logit bytes of one tree-construction call."""
+    c = dict(TREEBUILD_CONFIG)
+    c.update(overrides)
+    e = 4 if c["dtype"] == "f32" else 2
+    return c["R"] * complete_tree_rows(c["W"], c["N"]) * c["V"] * e
+
+
 def _tree_parents(rng, n, max_depth, max_children):
     parents = np.full(n, -1, dtype=np.int32)
     depth = np.zeros(n, dtype=np.int32)

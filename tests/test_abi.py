@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
             "spec_verify_tree_greedy_workspace_bytes", "spec_verify_status_string",
             "spec_verify_chain_pointmass", "spec_verify_chain_pointmass_workspace_bytes",
             "spec_outcome_topk", "spec_outcome_topk_workspace_bytes",
-            "spec_cache_lookup"} <= set(names)
+            "spec_cache_lookup", "spec_tree_build", "spec_tree_build_workspace_bytes"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
@@ -234,6 +234,47 @@ def test_cache_lookup_host_errors(lib):
     assert call(nc=c["SV_MAX_CACHE"] + 1) == c["SV_ERR_SHAPE"]
     assert call(out=ct.c_void_p(out.ctypes.data + 2)) == c["SV_ERR_ALIGN"]
     assert (slot == 7).all()  # nothing was written
+
+
+def test_tree_build_host_errors(lib):
+    import exact_draft_verification_amd as sv
+
+    c = header_constants()
+    R, M, V, W, N, nb = 2, 5, 64, 2, 2, 7
+    z = np.zeros((R, M, V), np.float32)
+    par = np.zeros((R, nb), np.int32)
+    tok = np.zeros((R, nb), np.int32)
+    row = np.zeros((R, nb), np.int32)
+    sc = np.zeros((R, nb), np.float64)
+    n = np.full(R, 5, np.int32)
+    ws = np.zeros(1 << 16, np.uint8)
+    wsa = ws[(-ws.ctypes.data) % 256:]
+
+    def call(**o):
+        args = dict(z=p(z), dt=0, cr=None, R=R, M=M, V=V, T=1.0, W=W, N=N, nb=nb, par=p(par),
+                    tok=p(tok), row=p(row), sc=p(sc), n=p(n), ws=p(wsa), wsb=16)
+        args.update(o)
+        return lib.spec_tree_build(args["z"], args["dt"], args["cr"], args["R"], args["M"],
+                                   args["V"], args["T"], args["W"], args["N"], args["nb"],
+                                   args["par"], args["tok"], args["row"], args["sc"], args["n"],
+                                   args["ws"], args["wsb"], None, None)
+
+    assert call(z=None) == c["SV_ERR_NULL"]
+    assert call(n=None) == c["SV_ERR_NULL"]
+    assert call(R=0) == c["SV_ERR_SHAPE"]
+    assert call(W=0) == c["SV_ERR_SHAPE"]
+    assert call(W=c["SV_MAX_TREE_WIDTH"] + 1) == c["SV_ERR_SHAPE"]
+    assert call(N=0) == c["SV_ERR_SHAPE"]
+    assert call(nb=0) == c["SV_ERR_SHAPE"]
+    assert call(nb=c["SV_MAX_TREE_NODES"] + 1) == c["SV_ERR_SHAPE"]
+    assert call(M=c["SV_MAX_TREE_SLOTS"] // W + 1) == c["SV_ERR_SHAPE"]
+    assert call(dt=2) == c["SV_ERR_DTYPE"]
+    assert call(T=float("nan")) == c["SV_ERR_TEMPERATURE"]
+    assert call(sc=ct.c_void_p(sc.ctypes.data + 4)) == c["SV_ERR_ALIGN"]
+    assert call(wsb=16) == c["SV_ERR_WORKSPACE"]
+    assert (n == 5).all()
+    assert sv.spec_tree_build_workspace_bytes(32, 85, 151936, 1, 4, 4, 64) > 0
+    assert sv.spec_tree_build_workspace_bytes(32, 85, 151936, 1, 17, 4, 64) == 0
 
 
 def test_tree_host_errors(lib):
