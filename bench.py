@@ -95,6 +95,10 @@ def measured_traffic(kernel_key):
 
 # ---------------------------------------------------------------- workloads --
 
+def synth_rows(W, N):
+    return sum(W ** d for d in range(N))
+
+
 class Workload:
     """Device-resident input copies plus a direct C-ABI call per step."""
 
@@ -109,6 +113,11 @@ class Workload:
             self.bytes = synth.outcome_config_bytes()
             t0 = time.time()
             d = synth.outcome_config_inputs(seed=seed)
+        elif cfg == "treebuild":
+            self.spec = dict(synth.TREEBUILD_CONFIG, kind="treebuild")
+            self.bytes = synth.treebuild_config_bytes()
+            t0 = time.time()
+            d = synth.treebuild_config_inputs(seed=seed)
         elif isinstance(cfg, str) and cfg.startswith("pm"):
             base = int(cfg[2:])
             self.spec = dict(synth.POINTMASS_CONFIGS[base], kind="pointmass")
@@ -155,6 +164,24 @@ class Workload:
                          for lg, tk, k_, a_, p_, h_ in self.sets]
             self.n_events = 2
             self.shape = dict(R=R, gamma=g, V=V, ncache=nc)
+        elif self.kind == "treebuild":
+            R, M, V, W, N, nb = d["R"], d["M"], d["V"], d["W"], d["N"], d["budget"]
+            z0 = logits(d["logits"])
+            self.sets = []
+            for i in range(self.nsets):
+                lg = z0 if i == 0 else z0.clone()
+                outs = [torch.empty((R, nb), dtype=torch.int32, device=dev) for _ in range(3)]
+                sc = torch.empty((R, nb), dtype=torch.float64, device=dev)
+                n = torch.empty(R, dtype=torch.int32, device=dev)
+                self.sets.append((lg, *outs, sc, n))
+            nbytes = sv.spec_tree_build_workspace_bytes(R, M, V, self.code, W, N, nb)
+            self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+            self.args = [(P(lg.data_ptr()), self.code, None, R, M, V, float(d["T"]), W, N, nb,
+                          P(pa.data_ptr()), P(tk.data_ptr()), P(ro.data_ptr()), P(sc.data_ptr()),
+                          P(n.data_ptr()), P(self.ws.data_ptr()), nbytes)
+                         for lg, pa, tk, ro, sc, n in self.sets]
+            self.n_events = 2
+            self.shape = dict(R=R, M=M, V=V, W=W, N=N, budget=nb)
         elif self.kind == "pointmass":
             B, g, V = d["B"], d["gamma"], d["V"]
             t0g = logits(d["target"])
@@ -228,13 +255,16 @@ class Workload:
             st = self.lib.spec_verify_chain_pointmass(*a, stream_handle, ev)
         elif self.kind == "outcome":
             st = self.lib.spec_outcome_topk(*a, stream_handle, ev)
+        elif self.kind == "treebuild":
+            st = self.lib.spec_tree_build(*a, stream_handle, ev)
         else:
             st = self.lib.spec_verify_tree_greedy(*a, stream_handle, ev)
         if st != 0:
             raise RuntimeError(f"library call failed with status {st}")
 
     def outputs(self):
-        return [tuple(t.cpu().clone() for t in s[-2:]) for s in self.sets]
+        keep = 5 if self.kind == "treebuild" else 2  # every output tensor of the call
+        return [tuple(t.cpu().clone() for t in s[-keep:]) for s in self.sets]
 
     def describe(self):
         s = self.spec
@@ -242,6 +272,11 @@ class Workload:
             return (f"outcome scoring + cache of {s['ncache']} R={s['R']} gamma={s['gamma']} "
                     f"V={s['V']} {s['dtype']} T={s['T']} (decoder rows {s['target'][0]}x"
                     f"{s['target'][1]}; draft token = row argmax w.p. {s['p_match']} else uniform)")
+        if self.kind == "treebuild":
+            return (f"draft-tree construction R={s['R']} W={s['W']} N={s['N']} "
+                    f"budget={s['budget']} V={s['V']} {s['dtype']} T={s['T']} (one draft row per "
+                    f"potential node of the complete {s['W']}-ary tree above depth {s['N']}: "
+                    f"{synth_rows(s['W'], s['N'])} rows of {s['logits'][0]}x{s['logits'][1]})")
         if self.kind == "pointmass":
             tgt = f"{s['target'][0]}x{s['target'][1]}"
             extra = f", +{s['boost'][1]:g} on {s['boost'][0]} ids/row" if s.get("boost") else ""
@@ -317,15 +352,31 @@ def measure(w, steps, warmup, torch, hip):
 
 
 def cpu_baseline(w, budget_s):
+    """The oracle on the host cores, on whole rounds of the workload (or, for
+    the single-threaded outcome and tree-construction oracles, on rounds of
+    its first few requests), for about budget_s seconds."""
     import oracle
 
     d = w.host
     threads = min(16, os.cpu_count() or 1)
+    units, used, what = d.get("B", d.get("R")), None, "block(s)"
+    if w.kind in ("outcome", "treebuild"):
+        used = min(4, d["R"])
+        threads, what = 1, f"request(s) of {d['R']}, one thread"
     rounds, t0 = 0, time.time()
     while True:
         if w.kind == "chain":
             oracle.chain(d["target"], d["draft"], d["draft_tokens"], d["uniforms"], d["T"],
                          dtype=d["dtype"], threads=threads)
+        elif w.kind == "pointmass":
+            oracle.chain_pointmass(d["target"], d["draft_tokens"], d["uniforms"], d["T"],
+                                   dtype=d["dtype"], threads=threads)
+        elif w.kind == "outcome":
+            oracle.outcome_topk(d["target"][:used], d["draft_tokens"][:used], d["T"], d["ncache"],
+                                dtype=d["dtype"])
+        elif w.kind == "treebuild":
+            oracle.tree_build(d["logits"][:used], d["T"], d["W"], d["N"], d["budget"],
+                              dtype=d["dtype"])
         else:
             oracle.tree_greedy(d["target"], d["parents"], d["tokens"], dtype=d["dtype"],
                                threads=threads)
@@ -333,12 +384,13 @@ def cpu_baseline(w, budget_s):
         if time.time() - t0 >= budget_s:
             break
     dt = time.time() - t0
-    blocks = d["B"]
-    return {"value": round(w.bytes * rounds / dt / 1e9, 4), "unit": "GB/s",
-            "cores": min(threads, blocks), "kind": "oracle",
+    frac = 1.0 if used is None else used / units
+    n = units if used is None else used
+    return {"value": round(w.bytes * frac * rounds / dt / 1e9, 4), "unit": "GB/s",
+            "cores": min(threads, n), "kind": "oracle",
             "rounds_per_s": round(rounds / dt, 3),
-            "sample": f"{rounds} full rounds of the headline workload in {dt:.1f}s "
-                      f"(fp64 oracle, threads over the {blocks} block(s))"}
+            "sample": f"{rounds} rounds of {n} {what} of the workload in {dt:.1f}s "
+                      f"(fp64 oracle)"}
 
 
 def copy_calibration(nbytes, reps, torch):
@@ -362,7 +414,7 @@ def main():
     ap.add_argument("--config", type=str, default=str(HEADLINE_CFG),
                     help="workload for the headline line (1-5; pm3 / pm5 for the point-mass "
                          "workloads with the shapes of configs 3 and 5; outcome for outcome "
-                         "scoring)")
+                         "scoring; treebuild for draft-tree construction)")
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip the other workloads in the per_config field")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -386,12 +438,14 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     hip = HipEvents()
     default_steps = {1: 2000, 2: 2000, 3: 200, 4: 100, 5: 50, "pm3": 200, "pm5": 50,
-                     "outcome": 200}
+                     "outcome": 200, "treebuild": 100}
     cfg_arg = int(args.config) if args.config.isdigit() else args.config
 
     def run(cfg, steps):
         if cfg == "outcome":
             seed = 8077
+        elif cfg == "treebuild":
+            seed = 9077
         else:
             seed = 1000 * int(cfg[2:]) + 77 if isinstance(cfg, str) else 1000 * cfg + 7
         w = Workload(cfg, seed=seed, torch=torch, sv=sv)
@@ -402,7 +456,8 @@ def main():
         return w, k, r
 
     w, K, r = run(cfg_arg, args.steps)
-    kernel = {"tree": "tree_argmax_kernel", "outcome": "outcome_stats_kernel"}.get(
+    kernel = {"tree": "tree_argmax_kernel", "outcome": "outcome_stats_kernel",
+              "treebuild": "outcome_stats_kernel"}.get(
         w.kind, "chain_stats_kernel") + ("<F32>" if w.spec["dtype"] == "f32" else "<BF16>")
     traffic = measured_traffic(f"{kernel} config{args.config}")
     line = {
@@ -436,7 +491,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_per_config:
         per = {}
-        for cfg in (3, 4, 5, "pm3", "pm5", "outcome"):
+        for cfg in (3, 4, 5, "pm3", "pm5", "outcome", "treebuild"):
             if cfg == cfg_arg:
                 continue
             try:

@@ -147,7 +147,7 @@ int32_t outcome_plan(int32_t R, int32_t gamma, int32_t V, int32_t dtype, int32_t
 
 struct TreeBuildPlan {
     int nseg, seg_len, kb;
-    size_t off_part, off_cand, off_tok, off_lq, off_ok, bytes;
+    size_t off_part, off_cand, bytes;
 };
 
 int32_t tree_build_plan(int32_t R, int32_t M, int32_t V, int32_t dtype, int32_t W,
@@ -160,16 +160,13 @@ int32_t tree_build_plan(int32_t R, int32_t M, int32_t V, int32_t dtype, int32_t 
     const int64_t rows_total = static_cast<int64_t>(R) * M;
     if (static_cast<double>(rows_total) * V * E > 9.0e18) return SV_ERR_SHAPE;
     p->kb = W <= 4 ? 4 : (W <= 8 ? 8 : 16);
-    // a row's segments are merged one lane each
+    // a row's segments are merged by one lane
     plan_segments(rows_total, V, epv, kOutcomeUnits, 16, kMaxTreeSegs, &p->nseg, &p->seg_len);
     if (rows_total * p->nseg > INT32_MAX) return SV_ERR_SHAPE;
     const size_t nr = static_cast<size_t>(rows_total);
     size_t off = 0;
     p->off_part = carve(&off, sizeof(Stat), nr * p->nseg);
     p->off_cand = carve(&off, sizeof(OutcomeCand), nr * p->nseg * p->kb);
-    p->off_tok = carve(&off, sizeof(int32_t), nr * W);
-    p->off_lq = carve(&off, sizeof(float), nr * W);
-    p->off_ok = carve(&off, sizeof(int32_t), nr);
     p->bytes = off;
     return SV_OK;
 }
@@ -433,9 +430,6 @@ extern "C" int32_t spec_tree_build(const void* draft_logits, int32_t dtype,
     a.W = W;
     a.max_depth = max_depth;
     a.budget = budget;
-    a.rt_tok = reinterpret_cast<int32_t*>(ws + p.off_tok);
-    a.rt_lq = reinterpret_cast<float*>(ws + p.off_lq);
-    a.rt_ok = reinterpret_cast<int32_t*>(ws + p.off_ok);
     a.parents = parents;
     a.tokens = tokens;
     a.node_row = node_row;
@@ -445,7 +439,6 @@ extern "C" int32_t spec_tree_build(const void* draft_logits, int32_t dtype,
     if (launch_outcome_stats(o, dtype, s, event_at(phase_events, 0), event_at(phase_events, 1)) !=
         hipSuccess)
         return SV_ERR_HIP;
-    if (launch_tree_rows(a, s) != hipSuccess) return SV_ERR_HIP;
     if (launch_tree_search(a, s) != hipSuccess) return SV_ERR_HIP;
     return SV_OK;
 }

@@ -364,10 +364,9 @@ __device__ inline void dpp_max_step(double& s, int& i) {
     const int ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xf, false);
     const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROWS, 0xf, false);
     const double os = __hiloint2double(ohi, olo);
-    if (cand_ahead(os, oi, s, i)) {
-        s = os;
-        i = oi;
-    }
+    const bool take = (os > s) | ((os == s) & (os > -INFINITY) & (oi < i));  // as cand_ahead
+    s = take ? os : s;
+    i = take ? oi : i;
 }
 
 // The wave's best (score, i); every lane gets it.  Quad swaps, half-row and

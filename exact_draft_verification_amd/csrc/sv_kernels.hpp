@@ -119,15 +119,12 @@ struct OutcomeArgs {
 // children of every row, then a best-first search per request.
 constexpr int kMaxTreeWidth = 16;     // children per node
 constexpr int kMaxTreeSlots = 2048;   // M * W (the search stages every row's children)
-constexpr int kMaxTreeSegs = 64;      // segments per row (one lane each when merged)
+constexpr int kMaxTreeSegs = 64;      // segments per row
 
 struct TreeBuildArgs {
     OutcomeArgs st;          // statistics pass over the rows (no draft tokens)
     const int32_t* child_row;  // [M][W] or null (complete W-ary numbering)
     int M, W, max_depth, budget;
-    int32_t* rt_tok;         // [R][M][W] child tokens (-1: none)
-    float* rt_lq;            // [R][M][W] their ln q
-    int32_t* rt_ok;          // [R][M] 1 if the row is valid
     int32_t* parents;        // [R][budget]
     int32_t* tokens;         // [R][budget]
     int32_t* node_row;       // [R][budget]
@@ -151,7 +148,6 @@ hipError_t launch_tree_resolve(const TreeArgs& a, hipStream_t s);
 hipError_t launch_outcome_stats(const OutcomeArgs& a, int dtype, hipStream_t s,
                                 hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_outcome_select(const OutcomeArgs& a, hipStream_t s);
-hipError_t launch_tree_rows(const TreeBuildArgs& a, hipStream_t s);
 hipError_t launch_tree_search(const TreeBuildArgs& a, hipStream_t s);
 hipError_t launch_cache_lookup(const int32_t* accept_len, const int32_t* out_tokens, int R,
                                int gamma, const int32_t* cache_k, const int32_t* cache_a,

@@ -13,14 +13,12 @@
 // score s_parent + ln q_m(token) -- until the tree holds `budget` nodes;
 // nodes at depth N or without a row are never expanded.
 //
-// Three kernels:
+// Two kernels:
 //  1. outcome_stats_kernel (outcome.hip), without draft tokens: one pass over
 //     every row keeps the softmax statistics and each segment's best logits.
-//  2. tree_rows_kernel: one wave per row merges the segment statistics and,
-//     by a tournament over the segments' sorted lists, takes the row's W best
-//     tokens with their ln q.
-//  3. tree_search_kernel: one wave per request stages every row's children in
-//     LDS and runs the search.  The queue never holds a node that cannot be
+//  2. tree_search_kernel: one workgroup per request merges each row's
+//     segments into the row's W best tokens with their ln q, in LDS (one row
+//     per thread), and then its first wave runs the search.  The queue never holds a node that cannot be
 //     expanded (popping it would change nothing), and it is kept as the union
 //     of the expanded nodes' child lists: children of one node have
 //     consecutive indices and non-increasing scores, so each list is sorted
@@ -35,63 +33,54 @@ namespace {
 constexpr double kDomain = 268435456.0;  // |m| / T limit (2^28)
 constexpr double kLn2 = 0.69314718055994530942;
 
-__global__ __launch_bounds__(kThreads) void tree_rows_kernel(TreeBuildArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);  // r*M + m
-    if (row >= static_cast<int64_t>(a.st.R) * a.M) return;  // the whole wave leaves together
-    const int nseg = a.st.nseg, kb = a.st.kb;
-    Stat t = stat_empty();
-    if (lane < nseg) t = a.st.part[row * nseg + lane];
-    t = wave_reduce_stat(t);
-    const bool ok = isfinite(t.S) && t.S > 0.0 && fabs(static_cast<double>(t.m) / a.st.T) <= kDomain;
-    const double L = static_cast<double>(t.R) + log2(t.S);
-    // lane s walks segment s's candidate list (sorted by value, then token)
-    const OutcomeCand* list = a.st.cand + (row * nseg + lane) * kb;
-    int pos = 0;
-    auto head = [&]() -> uint64_t {
-        if (lane >= nseg || pos >= kb) return 0;
-        const OutcomeCand c = list[pos];
-        if (c.idx == INT32_MAX || c.val == -INFINITY) return 0;  // empty or probability 0
-        return make_key(c.val, static_cast<uint32_t>(c.idx));
-    };
-    uint64_t h = head();
-    int32_t* tok = a.rt_tok + row * a.W;
-    float* lq = a.rt_lq + row * a.W;
-    int j = 0;
-    for (; j < a.W; ++j) {
-        const uint64_t w = wave_max_u64(h);
-        if (w == 0) break;  // fewer than W tokens of positive probability
-        if (lane == 0) {
-            tok[j] = static_cast<int32_t>(key_index(w));
-            lq[j] = static_cast<float>((static_cast<double>(key_value(w)) * a.st.c_d - L) * kLn2);
-        }
-        if (h == w) {
-            ++pos;
-            h = head();
-        }
-    }
-    if (lane == 0) {
-        for (; j < a.W; ++j) {
-            tok[j] = -1;
-            lq[j] = -INFINITY;
-        }
-        a.rt_ok[row] = ok ? 1 : 0;
-    }
+// Wave-wide best of (score desc, node asc), carrying the node's packed row
+// and depth along (same lane moves as wave_best).
+template <int CTRL, int ROWS>
+__device__ inline void dpp_best_step(double& s, int& i, int& rd) {
+    const int lo = __double2loint(s), hi = __double2hiint(s);
+    const int olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xf, false);
+    const int ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xf, false);
+    const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROWS, 0xf, false);
+    const int ord = __builtin_amdgcn_update_dpp(rd, rd, CTRL, ROWS, 0xf, false);
+    const double os = __hiloint2double(ohi, olo);
+    // scores here are finite: plain (score desc, node asc), taken by selects
+    const bool take = (os > s) | ((os == s) & (oi < i));  // no short circuit: no branches
+    s = take ? os : s;
+    i = take ? oi : i;
+    rd = take ? ord : rd;
+}
+__device__ inline void wave_best_rd(double& s, int& i, int& rd) {
+    dpp_best_step<0xb1, 0xf>(s, i, rd);
+    dpp_best_step<0x4e, 0xf>(s, i, rd);
+    dpp_best_step<0x141, 0xf>(s, i, rd);
+    dpp_best_step<0x140, 0xf>(s, i, rd);
+    dpp_best_step<0x142, 0xa>(s, i, rd);
+    dpp_best_step<0x143, 0xc>(s, i, rd);
+    const int lo = __builtin_amdgcn_readlane(__double2loint(s), 63);
+    const int hi = __builtin_amdgcn_readlane(__double2hiint(s), 63);
+    i = __builtin_amdgcn_readlane(i, 63);
+    rd = __builtin_amdgcn_readlane(rd, 63);
+    s = __hiloint2double(hi, lo);
 }
 
-__global__ __launch_bounds__(64) void tree_search_kernel(TreeBuildArgs a) {
+// A node's row (>= 0) and depth in one int (rows < 2^20, depths < 2^10).
+__device__ inline int pack_rd(int row, int depth) { return (row << 10) | depth; }
+
+__global__ __launch_bounds__(kThreads) void tree_search_kernel(TreeBuildArgs a) {
     extern __shared__ unsigned char s_dyn[];
-    const int r = blockIdx.x, lane = threadIdx.x;
+    const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     const int M = a.M, W = a.W, B = a.budget, N = a.max_depth;
     const int slots = M * W;
+    const int nseg = a.st.nseg, kb = a.st.kb;
     double* n_score = reinterpret_cast<double*>(s_dyn);  // [B] node scores
-    float* c_lq = reinterpret_cast<float*>(n_score + B);  // [slots] children per row
-    int* c_tok = reinterpret_cast<int*>(c_lq + slots);    // [slots]
-    int* c_row = c_tok + slots;                            // [slots]
-    int* n_row = c_row + slots;                            // [B]
-    int* n_depth = n_row + B;                              // [B]
-    int* l_head = n_depth + B;                             // [B] list heads
-    int* l_end = l_head + B;                               // [B] list ends
+    double* l_hs = n_score + B;                          // [B] list head scores
+    float* c_lq = reinterpret_cast<float*>(l_hs + B);    // [slots] children per row
+    int* c_tok = reinterpret_cast<int*>(c_lq + slots);   // [slots]
+    int* c_row = c_tok + slots;                          // [slots]
+    int* n_row = c_row + slots;                          // [B]
+    int* l_head = n_row + B;                             // [B] list heads
+    int* l_end = l_head + B;                             // [B] list ends
+    int* l_hrd = l_end + B;                              // [B] head's packed row and depth
     const int64_t rb = static_cast<int64_t>(r) * M;
     const int64_t ob = static_cast<int64_t>(r) * B;
     int32_t* o_par = a.parents + ob;
@@ -99,104 +88,197 @@ __global__ __launch_bounds__(64) void tree_search_kernel(TreeBuildArgs a) {
     int32_t* o_row = a.node_row + ob;
     double* o_sc = a.score + ob;
 
-    // stage every row's children and the child map; check the rows
+    // every row's W children, one row per thread of the workgroup: its
+    // segment statistics merged, and the W best of its segments' sorted
+    // candidate lists
     int bad = 0;
-    for (int i = lane; i < slots; i += 64) {
-        c_tok[i] = a.rt_tok[rb * W + i];
-        c_lq[i] = a.rt_lq[rb * W + i];
-        int cr;
-        if (a.child_row) {
-            cr = a.child_row[i];
-            bad |= (cr < -1 || cr >= M);
-        } else {
-            const int m = i / W;
-            const int64_t c = static_cast<int64_t>(m) * W + 1 + (i - m * W);
-            cr = c < M ? static_cast<int>(c) : -1;
+    for (int m = tid; m < M; m += kThreads) {
+        const Stat* pp = a.st.part + (rb + m) * nseg;
+        const OutcomeCand* cc = a.st.cand + (rb + m) * nseg * kb;
+        if (nseg == 1) {
+            // one sorted list: its first W entries, loaded together
+            OutcomeCand c[kMaxTreeWidth];
+#pragma unroll
+            for (int q = 0; q < kMaxTreeWidth; ++q)
+                if (q < W) c[q] = cc[q];
+            const Stat t = pp[0];
+            bad |= !(isfinite(t.S) && t.S > 0.0 &&
+                     fabs(static_cast<double>(t.m) / a.st.T) <= kDomain);
+            const double L = static_cast<double>(t.R) + log2(t.S);
+#pragma unroll
+            for (int q = 0; q < kMaxTreeWidth; ++q) {
+                if (q < W) {
+                    const bool ok = c[q].idx != INT32_MAX && c[q].val != -INFINITY;  // a prefix
+                    c_tok[m * W + q] = ok ? c[q].idx : -1;
+                    c_lq[m * W + q] =
+                        ok ? static_cast<float>((static_cast<double>(c[q].val) * a.st.c_d - L) * kLn2)
+                           : -INFINITY;
+                }
+            }
+            continue;
         }
-        c_row[i] = cr;
+        Stat t = pp[0];
+        for (int sg = 1; sg < nseg; ++sg) t = stat_merge(t, pp[sg]);
+        bad |= !(isfinite(t.S) && t.S > 0.0 &&
+                 fabs(static_cast<double>(t.m) / a.st.T) <= kDomain);
+        const double L = static_cast<double>(t.R) + log2(t.S);
+        // pass j takes the best key below the one taken by pass j-1 (keys are
+        // distinct); a segment contributes at most W
+        const int depth_k = min(kb, W);
+        uint64_t prev = ~0ull;
+        int j = 0;
+        for (; j < W; ++j) {
+            uint64_t best = 0;
+            for (int sg = 0; sg < nseg; ++sg) {
+                for (int p = 0; p < depth_k; ++p) {
+                    const OutcomeCand c = cc[sg * kb + p];
+                    if (c.idx == INT32_MAX || c.val == -INFINITY) break;  // the rest is empty
+                    const uint64_t k = make_key(c.val, static_cast<uint32_t>(c.idx));
+                    if (k < prev) {  // the segment's best not yet taken
+                        best = k > best ? k : best;
+                        break;
+                    }
+                }
+            }
+            if (best == 0) break;  // fewer than W tokens of positive probability
+            c_tok[m * W + j] = static_cast<int>(key_index(best));
+            c_lq[m * W + j] =
+                static_cast<float>((static_cast<double>(key_value(best)) * a.st.c_d - L) * kLn2);
+            prev = best;
+        }
+        for (; j < W; ++j) {
+            c_tok[m * W + j] = -1;
+            c_lq[m * W + j] = -INFINITY;
+        }
     }
-    for (int m = lane; m < M; m += 64) bad |= (a.rt_ok[rb + m] == 0);
-    if (__ballot(bad) != 0) {
-        for (int i = lane; i < B; i += 64) {
+    // the child map, in chunks whose loads are all issued before use
+    constexpr int kChunk = 8;
+    for (int base = 0; base < slots; base += kThreads * kChunk) {
+        int cr[kChunk];
+#pragma unroll
+        for (int c = 0; c < kChunk; ++c) {
+            const int i = base + c * kThreads + tid;
+            if (i < slots) {
+                if (a.child_row) {
+                    cr[c] = a.child_row[i];
+                } else {
+                    const int m = i / W;
+                    const int64_t ch = static_cast<int64_t>(m) * W + 1 + (i - m * W);
+                    cr[c] = ch < M ? static_cast<int>(ch) : -1;
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kChunk; ++c) {
+            const int i = base + c * kThreads + tid;
+            if (i < slots) {
+                c_row[i] = cr[c];
+                bad |= (cr[c] < -1 || cr[c] >= M);
+            }
+        }
+    }
+    if (__syncthreads_or(bad)) {
+        for (int i = tid; i < B; i += kThreads) {
             o_par[i] = -1;
             o_tok[i] = -1;
             o_row[i] = -1;
             o_sc[i] = -INFINITY;
         }
-        if (lane == 0) a.n_nodes[r] = -1;
+        if (tid == 0) a.n_nodes[r] = -1;
         return;
     }
+    if (tid >= 64) return;  // the search runs on the first wave alone
     if (lane == 0) {
         n_score[0] = 0.0;
         n_row[0] = 0;
-        n_depth[0] = 0;
         o_par[0] = -1;
         o_tok[0] = -1;
         o_row[0] = 0;
         o_sc[0] = 0.0;
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
     int n = 1, nlists = 0;
-    // this lane's best list head: score, node, list
+    // this lane's best list head: score, node, packed row/depth, list
     double bs = -INFINITY;
-    int bn = INT32_MAX, bl = -1;
+    int bn = INT32_MAX, brd = 0, bl = -1;
     auto consider = [&](int l) {
         const int h = l_head[l];
-        if (h < l_end[l] && cand_ahead(n_score[h], h, bs, bn)) {
-            bs = n_score[h];
+        const double hs = l_hs[l];
+        if (h < l_end[l] && cand_ahead(hs, h, bs, bn)) {
+            bs = hs;
             bn = h;
+            brd = l_hrd[l];
             bl = l;
         }
     };
-    // adds the candidate children of node v (all lanes, v uniform)
-    auto expand = [&](int v) {
-        const int rv = n_row[v], dv = n_depth[v];
-        const double sv = n_score[v];
-        int cnt = 0;
-        for (int j = 0; j < W; ++j) cnt += c_tok[rv * W + j] >= 0;  // children form a prefix
-        cnt = min(cnt, B - n);
+    // adds the candidate children of node v (all lanes; arguments uniform)
+    auto expand = [&](int v, int rv, int dv, double sv) {
+        int tk = -1, cr = -1;
+        float q = 0.0f;
+        if (lane < W) {
+            tk = c_tok[rv * W + lane];
+            q = c_lq[rv * W + lane];
+            cr = c_row[rv * W + lane];
+        }
+        const int cnt = min(__popcll(__ballot(tk >= 0)), B - n);  // the children form a prefix
+        const double s = sv + static_cast<double>(q);
         if (lane < cnt) {
-            const int u = n + lane, i = rv * W + lane;
-            const double s = sv + static_cast<double>(c_lq[i]);
+            const int u = n + lane;
             n_score[u] = s;
-            n_row[u] = c_row[i];
-            n_depth[u] = dv + 1;
+            n_row[u] = cr;
             o_par[u] = v;
-            o_tok[u] = c_tok[i];
-            o_row[u] = c_row[i];
+            o_tok[u] = tk;
+            o_row[u] = cr;
             o_sc[u] = s;
         }
-        __syncthreads();
-        if (dv + 1 < N && cnt > 0) {
+        // only children with a row are ever expanded
+        const uint64_t expandable = __ballot(lane < cnt && cr >= 0);
+        if (dv + 1 < N && expandable != 0) {
+            const int f = __builtin_ctzll(expandable);
             const int l = nlists++;
+            const double hs = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(s), f),
+                                               __builtin_amdgcn_readlane(__double2loint(s), f));
+            const int hrd = pack_rd(__builtin_amdgcn_readlane(cr, f), dv + 1);
             if (lane == (l & 63)) {
-                int h = n;
-                while (h < n + cnt && n_row[h] < 0) ++h;  // only nodes with a row are queued
-                l_head[l] = h;
+                l_head[l] = n + f;
                 l_end[l] = n + cnt;
-                consider(l);
+                l_hs[l] = hs;
+                l_hrd[l] = hrd;
+                if (cand_ahead(hs, n + f, bs, bn)) {
+                    bs = hs;
+                    bn = n + f;
+                    brd = hrd;
+                    bl = l;
+                }
             }
         }
         n += cnt;
+        // the workgroup is this one wave: order its LDS writes before later
+        // reads without waiting for the global stores
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     };
-    expand(0);  // the root is the only queued node at first
+    expand(0, 0, 0, 0.0);  // the root is the only queued node at first
     while (n < B) {
         double ws = bs;
-        int wn = bn;
-        wave_best(ws, wn);
+        int wn = bn, wrd = brd;
+        wave_best_rd(ws, wn, wrd);
         if (wn == INT32_MAX) break;  // nothing left to expand
         if (bn == wn) {              // the owner advances the popped list
-            int h = wn + 1;
             const int e = l_end[bl];
+            int h = wn + 1;
             while (h < e && n_row[h] < 0) ++h;
             l_head[bl] = h;
+            if (h < e) {
+                l_hs[bl] = n_score[h];
+                l_hrd[bl] = pack_rd(n_row[h], wrd & 1023);
+            }
             bs = -INFINITY;
             bn = INT32_MAX;
             bl = -1;
             for (int l = lane; l < nlists; l += 64) consider(l);
         }
-        expand(wn);
+        expand(wn, wrd >> 10, wrd & 1023, ws);
     }
     for (int i = n + lane; i < B; i += 64) {
         o_par[i] = -1;
@@ -209,21 +291,14 @@ __global__ __launch_bounds__(64) void tree_search_kernel(TreeBuildArgs a) {
 
 }  // namespace
 
-hipError_t launch_tree_rows(const TreeBuildArgs& a, hipStream_t s) {
-    const int64_t rows = static_cast<int64_t>(a.st.R) * a.M;
-    hipLaunchKernelGGL(tree_rows_kernel, dim3(static_cast<unsigned>((rows + kWaves - 1) / kWaves)),
-                       dim3(kThreads), 0, s, a);
-    return hipGetLastError();
-}
-
 size_t tree_search_lds_bytes(int M, int W, int budget) {
     const size_t slots = static_cast<size_t>(M) * W;
-    return static_cast<size_t>(budget) * (sizeof(double) + 4 * sizeof(int)) +
+    return static_cast<size_t>(budget) * (2 * sizeof(double) + 4 * sizeof(int)) +
            slots * (sizeof(float) + 2 * sizeof(int));
 }
 
 hipError_t launch_tree_search(const TreeBuildArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(tree_search_kernel, dim3(a.st.R), dim3(64),
+    hipLaunchKernelGGL(tree_search_kernel, dim3(a.st.R), dim3(kThreads),
                        tree_search_lds_bytes(a.M, a.W, a.budget), s, a);
     return hipGetLastError();
 }
