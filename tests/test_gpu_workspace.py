@@ -1,5 +1,4 @@
-"""One scratch workspace shared by calls of different sizes and both entry
-points.
+"""One scratch workspace shared by calls of different sizes and entry points.
 
 The library needs no initialised workspace: each call writes every workspace
 byte it later reads.  Regression test for a workspace reused across shapes
@@ -42,3 +41,43 @@ def test_workspace_reused_across_shapes_and_entry_points():
             g = gpu_tree(dict(d, dtype="bf16"), workspace=ws)
             o = oracle.tree_greedy(d["target"], d["parents"], d["tokens"])
             compare_tree(g, o, f"call{i}")
+
+
+def test_workspace_garbage_for_outcomes_and_tree_construction():
+    """The same contract for spec_outcome_topk, spec_verify_chain_pointmass and
+    spec_tree_build: a shared workspace refilled with garbage before every
+    call, shapes changing between calls."""
+    torch, sv = require_gpu()
+    from gpu_util import (compare_outcomes, gpu_outcome, gpu_pointmass, to_dev,
+                          to_dev_logits)
+
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    fills = [0xFF, 0x00, 0x7F, 0xA5]
+    for i, (R, g, V, nc) in enumerate([(3, 4, 3001, 8), (1, 31, 600, 16), (6, 2, 151936, 1)]):
+        print(f"[case] shared workspace outcome call {i}", flush=True)
+        d = synth.pointmass_inputs(R, g, V, "bf16", T=0.9, seed=40 + i)
+        ws.fill_(fills[i % 4])
+        got = gpu_outcome(d, nc, workspace=ws)
+        o = oracle.outcome_topk(d["target"], d["draft_tokens"], d["T"], nc, dtype="bf16",
+                                want_all=True)
+        compare_outcomes(got, o["all_scores"], o, f"outcome-call{i}")
+        ws.fill_(fills[(i + 1) % 4])
+        got = gpu_pointmass(d, workspace=ws)
+        o = oracle.chain_pointmass(d["target"], d["draft_tokens"], d["uniforms"], d["T"],
+                                   dtype="bf16")
+        keep = o["margin"] >= 1e-6
+        assert np.array_equal(got["accept_len"][keep], o["accept_len"][keep])
+        assert np.array_equal(got["out_tokens"][keep], o["out_tokens"][keep])
+    for i, (R, M, V, W, N, nb) in enumerate([(2, 21, 5003, 4, 3, 40), (5, 7, 300, 2, 6, 100),
+                                             (1, 85, 151936, 4, 4, 64)]):
+        print(f"[case] shared workspace tree-construction call {i}", flush=True)
+        d = synth.treebuild_inputs(R, M, V, "bf16", T=1.0, logits=("gumbel", 2.0), seed=50 + i)
+        ws.fill_(fills[(i + 2) % 4])
+        par, tok, row, sc, n = sv.spec_tree_build(to_dev_logits(d["logits"], "bf16"), d["T"], W,
+                                                  N, nb, workspace=ws)
+        torch.cuda.synchronize()
+        o = oracle.tree_build(d["logits"], d["T"], W, N, nb, dtype="bf16")
+        for r in np.nonzero(o["min_gap"] >= 1e-4)[0]:
+            assert np.array_equal(par.cpu().numpy()[r], o["parents"][r])
+            assert np.array_equal(tok.cpu().numpy()[r], o["tokens"][r])
+            assert np.array_equal(row.cpu().numpy()[r], o["rows"][r])
