@@ -14,7 +14,8 @@ namespace sv {
 namespace {
 
 constexpr int kThreadsHost = 256;
-constexpr int64_t kTargetUnits = 8192;  // statistics/argmax workgroups to aim for
+constexpr int64_t kChainUnits = 4096;   // chain statistics workgroups to aim for
+constexpr int64_t kTreeUnits = 8192;    // tree argmax workgroups to aim for
 constexpr int64_t kOutcomeUnits = 1024; // outcome-scoring workgroups to aim for
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -67,7 +68,9 @@ int32_t chain_plan(int32_t B, int32_t gamma, int32_t V, int32_t dtype, bool poin
     if (static_cast<double>(rows_total) * V * E > 9.0e18) return SV_ERR_SHAPE;
     p->rows = static_cast<int>(rows);
     // a block's rows*nseg partials are staged in LDS by the chunk kernel
-    plan_segments(rows_total, V, epv, kTargetUnits, 4,
+    // fewer, longer segments keep the partials every chunk workgroup merges
+    // for its block's decision few
+    plan_segments(rows_total, V, epv, kChainUnits, 4,
                   static_cast<int>(kMaxBlockParts / rows), &p->nseg, &p->seg_len);
     if (rows_total * p->nseg > INT32_MAX) return SV_ERR_SHAPE;
     // final draw: tiles of one 16-byte vector per thread, sums kept per
@@ -103,7 +106,7 @@ int32_t tree_plan(int32_t B, int32_t n, int32_t V, int32_t dtype, TreePlan* p) {
     const int64_t rows_total = static_cast<int64_t>(B) * n;
     if (static_cast<double>(rows_total) * V * E > 9.0e18) return SV_ERR_SHAPE;
     // a request's n*nseg partials are staged in LDS by the resolve kernel
-    plan_segments(rows_total, V, epv, kTargetUnits, 4, kMaxBlockParts / n, &p->nseg,
+    plan_segments(rows_total, V, epv, kTreeUnits, 4, kMaxBlockParts / n, &p->nseg,
                   &p->seg_len);
     if (rows_total * p->nseg > INT32_MAX) return SV_ERR_SHAPE;
     size_t off = 0;
