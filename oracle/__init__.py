@@ -58,9 +58,10 @@ def _declare(lib):
     lib.oracle_chain_pointmass_du.argtypes = [P, I, P, P, I, I, I, D, P, P, P, P, P, P, I]
     lib.oracle_outcome_topk.argtypes = [P, I, P, I, I, I, D, I, P, P, P, P, P]
     lib.oracle_tree_build.argtypes = [P, I, I, I, I, D, I, I, I, P, P, P, P, P, P, P]
+    lib.oracle_tree_stochastic.argtypes = [P, P, I, P, P, P, I, I, I, D, P, P, P, P, P]
     for f in (lib.oracle_chain, lib.oracle_chain_du, lib.oracle_chain_alpha,
               lib.oracle_tree_greedy, lib.oracle_chain_pointmass, lib.oracle_chain_pointmass_du,
-              lib.oracle_outcome_topk, lib.oracle_tree_build):
+              lib.oracle_outcome_topk, lib.oracle_tree_build, lib.oracle_tree_stochastic):
         f.restype = I
     return lib
 
@@ -214,6 +215,34 @@ def tree_greedy(target, parents, tokens, dtype="bf16", threads=None) -> dict:
     return dict(accept_len=acc, accept_node=node, out_tokens=out, amax=amax)
 
 
+
+
+def tree_stochastic(target, draft, parents, tokens, uniforms, T, dtype="bf16",
+                    want_dist=False) -> dict:
+    """Stochastic tree verification: one Bernoulli test per node with
+    probability min(1, p/q) from its parent's rows, the deepest node whose
+    whole path passed wins, and the correction is drawn from p after it with
+    u[:, 0].  Returns accept_len, accept_node [B], out_tokens [B, n], margin
+    [B] and, if asked, final_dist [B, V]."""
+    lib = _load()
+    target = _logits(target, dtype)
+    draft = _logits(draft, dtype)
+    B, n, V = target.shape
+    assert draft.shape == (B, n, V)
+    par = np.ascontiguousarray(parents, dtype=np.int32)
+    tok = np.ascontiguousarray(tokens, dtype=np.int32)
+    u = np.ascontiguousarray(uniforms, dtype=np.float32)
+    acc = np.empty(B, np.int32)
+    node = np.empty(B, np.int32)
+    out = np.empty((B, n), np.int32)
+    margin = np.empty(B, np.float64)
+    dist = np.empty((B, V), np.float64) if want_dist else None
+    rc = lib.oracle_tree_stochastic(_ptr(target), _ptr(draft), _DT[dtype], _ptr(par), _ptr(tok),
+                                    _ptr(u), B, n, V, float(T), _ptr(acc), _ptr(node), _ptr(out),
+                                    _ptr(dist), _ptr(margin))
+    if rc != 0:
+        raise ValueError(f"oracle_tree_stochastic rejected its arguments (rc={rc})")
+    return dict(accept_len=acc, accept_node=node, out_tokens=out, margin=margin, final_dist=dist)
 
 def tree_build(logits, T, W, N, budget, child_row=None, dtype="f32") -> dict:
     """Best-first construction of a draft tree from per-potential-node draft

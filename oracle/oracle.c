@@ -953,3 +953,154 @@ int oracle_tree_build(const void *logits, int dtype, int R, int M, int V, double
     free(taken);
     return 0;
 }
+
+/* ----------------------------------------------------------------------
+ * Stochastic tree verification ([JN] section "Tree verification", Eq. 16-17
+ * and Fig. 5).
+ *
+ * Request b holds a candidate tree of n nodes: parents[b][0] = -1 (node 0 is
+ * the root, the verified prefix), 0 <= parents[b][j] < j, tokens[b][j] the
+ * token of node j (node 0's is not used).  Target row j and draft row j are
+ * the target's and the draft's next-token logits after node j's path; p_j
+ * and q_j are their softmax at temperature T.
+ *  - Every node j >= 1 takes one Bernoulli test (Eq. 16) with probability
+ *    alpha_j = min(1, p_par(y_j) / q_par(y_j)), par = parents[j], y_j its
+ *    token: accepted iff u[b][j] < alpha_j (a node shared by several
+ *    branches is tested once).  As in the chain rule, alpha = 0 when
+ *    p_par(y) = 0 and alpha = 1 when q_par(y) = 0 < p_par(y).
+ *  - A branch keeps its longest prefix of accepted tokens (Eq. 17): node j
+ *    counts as accepted iff its parent does and its own test passes; the
+ *    root counts as accepted.
+ *  - The best branch ends at the deepest accepted node v* (the lowest index
+ *    among equally deep ones); its tokens are committed.
+ *  - The correction token is drawn from p_{v*}, the target distribution
+ *    after the accepted path (as Fig. 5 shows), by inverse CDF in ascending
+ *    token id with u[b][0]: the smallest v with sum_{t<=v} p(t) > u * W
+ *    (W the total), else the last v of positive probability.  The pages give
+ *    no residual rule for a branch rejected below v*, so none is applied.
+ * Outputs as for greedy tree verification: accept_len[b] = depth of v*,
+ * accept_node[b] = v*, out_tokens[b][0..n) the path root -> v* (root
+ * excluded), the drawn token, then -1.  final_dist (nullable, [B][V])
+ * receives p_{v*}; margin (nullable, [B]) the smallest |u_j - alpha_j| over
+ * the nodes whose parent is accepted, and the draw's distance to the nearest
+ * CDF breakpoint relative to W.  An invalid request (a malformed parent
+ * array, a token outside [0, V), a NaN or +inf logit or a row without a
+ * finite logit in any target or draft row, or the |m|/T domain) gets
+ * accept_len = accept_node = -1 and all tokens -1.
+ */
+int oracle_tree_stochastic(const void *target, const void *draft, int dtype,
+                           const int32_t *parents, const int32_t *tokens, const float *uniforms,
+                           int B, int n, int V, double T, int32_t *accept_len,
+                           int32_t *accept_node, int32_t *out_tokens, double *final_dist,
+                           double *margin)
+{
+    if (!target || !draft || !parents || !tokens || !uniforms || !accept_len || !accept_node ||
+        !out_tokens)
+        return -1;
+    if (B < 1 || n < 1 || V < 1 || !(T > 0.0) || !isfinite(T))
+        return -1;
+    if (dtype != ORC_F32 && dtype != ORC_BF16)
+        return -1;
+    double *mp = malloc(sizeof(double) * (size_t)n), *Sp = malloc(sizeof(double) * (size_t)n);
+    double *mq = malloc(sizeof(double) * (size_t)n), *Sq = malloc(sizeof(double) * (size_t)n);
+    int *acc = malloc(sizeof(int) * (size_t)n), *depth = malloc(sizeof(int) * (size_t)n);
+    double *w = malloc(sizeof(double) * (size_t)V);
+    if (!mp || !Sp || !mq || !Sq || !acc || !depth || !w)
+        return -2;
+    for (int b = 0; b < B; ++b) {
+        const int32_t *par = parents + (int64_t)b * n, *tok = tokens + (int64_t)b * n;
+        const float *u = uniforms + (int64_t)b * n;
+        int32_t *out = out_tokens + (int64_t)b * n;
+        const int64_t base = (int64_t)b * n * V;
+        for (int j = 0; j < n; ++j)
+            out[j] = -1;
+        accept_len[b] = accept_node[b] = -1;
+        if (margin)
+            margin[b] = 0.0;
+        if (final_dist)
+            for (int v = 0; v < V; ++v)
+                final_dist[(int64_t)b * V + v] = 0.0;
+        int bad = par[0] != -1;
+        for (int j = 1; j < n && !bad; ++j)
+            bad |= (par[j] < 0 || par[j] >= j || tok[j] < 0 || tok[j] >= V);
+        for (int j = 0; j < n && !bad; ++j) {
+            bad |= row_softmax_stats(target, dtype, base + (int64_t)j * V, V, T, &mp[j], &Sp[j]);
+            if (!bad)
+                bad |= row_softmax_stats(draft, dtype, base + (int64_t)j * V, V, T, &mq[j], &Sq[j]);
+        }
+        if (bad)
+            continue;
+        /* per-node tests, in index order (parents precede children) */
+        double mg = INFINITY;
+        acc[0] = 1;
+        depth[0] = 0;
+        for (int j = 1; j < n; ++j) {
+            const int p = par[j];
+            const double lp = logprob_at(target, dtype, base + (int64_t)p * V, tok[j], T, mp[p], Sp[p]);
+            const double lq = logprob_at(draft, dtype, base + (int64_t)p * V, tok[j], T, mq[p], Sq[p]);
+            double alpha;
+            if (lp == -INFINITY)
+                alpha = 0.0;
+            else if (lq == -INFINITY)
+                alpha = 1.0;
+            else
+                alpha = fmin(1.0, exp(lp - lq));
+            const double uj = (double)u[j];
+            acc[j] = acc[p] && uj < alpha;
+            depth[j] = depth[p] + 1;
+            if (acc[p])
+                mg = fmin(mg, fabs(uj - alpha));
+        }
+        int best = 0;
+        for (int j = 1; j < n; ++j)
+            if (acc[j] && depth[j] > depth[best])
+                best = j;
+        /* the correction from p at the deepest accepted node */
+        const int64_t prow = base + (int64_t)best * V;
+        double W = 0.0;
+        for (int v = 0; v < V; ++v) {
+            w[v] = prob_at(target, dtype, prow, v, T, mp[best], Sp[best]);
+            W += w[v];
+        }
+        const double t = (double)u[0] * W;
+        double C = 0.0, Cprev = 0.0;
+        int drawn = -1;
+        for (int v = 0; v < V; ++v) {
+            Cprev = C;
+            C += w[v];
+            if (C > t) {
+                drawn = v;
+                break;
+            }
+        }
+        double mf;
+        if (drawn < 0) {
+            for (int v = V - 1; v >= 0; --v)
+                if (w[v] > 0.0) {
+                    drawn = v;
+                    break;
+                }
+            mf = 0.0;
+        } else {
+            mf = fmin(t - Cprev, C - t) / W;
+        }
+        for (int j = best; j != 0; j = par[j])
+            out[depth[j] - 1] = tok[j];
+        out[depth[best]] = drawn;
+        accept_len[b] = depth[best];
+        accept_node[b] = best;
+        if (margin)
+            margin[b] = fmin(mg, mf);
+        if (final_dist)
+            for (int v = 0; v < V; ++v)
+                final_dist[(int64_t)b * V + v] = w[v] / W;
+    }
+    free(mp);
+    free(Sp);
+    free(mq);
+    free(Sq);
+    free(acc);
+    free(depth);
+    free(w);
+    return 0;
+}
