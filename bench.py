@@ -113,6 +113,11 @@ class Workload:
             self.bytes = synth.outcome_config_bytes()
             t0 = time.time()
             d = synth.outcome_config_inputs(seed=seed)
+        elif cfg == "stree":
+            self.spec = dict(synth.STREE_CONFIG, kind="stree")
+            self.bytes = synth.stree_config_bytes()
+            t0 = time.time()
+            d = synth.stree_config_inputs(seed=seed)
         elif cfg == "treebuild":
             self.spec = dict(synth.TREEBUILD_CONFIG, kind="treebuild")
             self.bytes = synth.treebuild_config_bytes()
@@ -164,6 +169,29 @@ class Workload:
                          for lg, tk, k_, a_, p_, h_ in self.sets]
             self.n_events = 2
             self.shape = dict(R=R, gamma=g, V=V, ncache=nc)
+        elif self.kind == "stree":
+            B, n, V = d["B"], d["n"], d["V"]
+            t0g, d0g = logits(d["target"]), logits(d["draft"])
+            par = torch.from_numpy(d["parents"]).to(dev)
+            tok = torch.from_numpy(d["tokens"]).to(dev)
+            uni = torch.from_numpy(d["uniforms"]).to(dev)
+            self.sets = []
+            for i in range(self.nsets):
+                tg = t0g if i == 0 else t0g.clone()
+                dr = d0g if i == 0 else d0g.clone()
+                acc = torch.empty(B, dtype=torch.int32, device=dev)
+                node = torch.empty(B, dtype=torch.int32, device=dev)
+                out = torch.empty((B, n), dtype=torch.int32, device=dev)
+                self.sets.append((tg, dr, acc, node, out))
+            nbytes = sv.spec_verify_tree_stochastic_workspace_bytes(B, n, V, self.code)
+            self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+            self.args = [(P(tg.data_ptr()), P(dr.data_ptr()), self.code, P(par.data_ptr()),
+                          P(tok.data_ptr()), P(uni.data_ptr()), B, n, V, float(d["T"]),
+                          P(ac.data_ptr()), P(no.data_ptr()), P(ou.data_ptr()), None,
+                          P(self.ws.data_ptr()), nbytes)
+                         for tg, dr, ac, no, ou in self.sets]
+            self.n_events = 3
+            self.shape = dict(B=B, n=n, V=V)
         elif self.kind == "treebuild":
             R, M, V, W, N, nb = d["R"], d["M"], d["V"], d["W"], d["N"], d["budget"]
             z0 = logits(d["logits"])
@@ -257,13 +285,15 @@ class Workload:
             st = self.lib.spec_outcome_topk(*a, stream_handle, ev)
         elif self.kind == "treebuild":
             st = self.lib.spec_tree_build(*a, stream_handle, ev)
+        elif self.kind == "stree":
+            st = self.lib.spec_verify_tree_stochastic(*a, stream_handle, ev)
         else:
             st = self.lib.spec_verify_tree_greedy(*a, stream_handle, ev)
         if st != 0:
             raise RuntimeError(f"library call failed with status {st}")
 
     def outputs(self):
-        keep = 5 if self.kind == "treebuild" else 2  # every output tensor of the call
+        keep = {"treebuild": 5, "stree": 3}.get(self.kind, 2)  # every output tensor of the call
         return [tuple(t.cpu().clone() for t in s[-keep:]) for s in self.sets]
 
     def describe(self):
@@ -272,6 +302,12 @@ class Workload:
             return (f"outcome scoring + cache of {s['ncache']} R={s['R']} gamma={s['gamma']} "
                     f"V={s['V']} {s['dtype']} T={s['T']} (decoder rows {s['target'][0]}x"
                     f"{s['target'][1]}; draft token = row argmax w.p. {s['p_match']} else uniform)")
+        if self.kind == "stree":
+            return (f"stochastic tree verify B={s['B']} n={s['n']} V={s['V']} {s['dtype']} "
+                    f"T={s['T']} (target {s['target'][0]}x{s['target'][1]}, draft = target + "
+                    f"N(0,{s['noise']}^2) per node, depth<={s['max_depth']}, "
+                    f"branching<={s['max_children']}, node tokens ~ q at the parent, "
+                    f"seeded uniforms)")
         if self.kind == "treebuild":
             return (f"draft-tree construction R={s['R']} W={s['W']} N={s['N']} "
                     f"budget={s['budget']} V={s['V']} {s['dtype']} T={s['T']} (one draft row per "
@@ -359,10 +395,10 @@ def cpu_baseline(w, budget_s):
 
     d = w.host
     threads = min(16, os.cpu_count() or 1)
-    units, used, what = d.get("B", d.get("R")), None, "block(s)"
-    if w.kind in ("outcome", "treebuild"):
-        used = min(4, d["R"])
-        threads, what = 1, f"request(s) of {d['R']}, one thread"
+    units, used = d.get("B", d.get("R")), None
+    if w.kind in ("outcome", "treebuild", "stree"):
+        used = min(4, units)
+        threads = 1
     rounds, t0 = 0, time.time()
     while True:
         if w.kind == "chain":
@@ -377,6 +413,10 @@ def cpu_baseline(w, budget_s):
         elif w.kind == "treebuild":
             oracle.tree_build(d["logits"][:used], d["T"], d["W"], d["N"], d["budget"],
                               dtype=d["dtype"])
+        elif w.kind == "stree":
+            oracle.tree_stochastic(d["target"][:used], d["draft"][:used], d["parents"][:used],
+                                   d["tokens"][:used], d["uniforms"][:used], d["T"],
+                                   dtype=d["dtype"])
         else:
             oracle.tree_greedy(d["target"], d["parents"], d["tokens"], dtype=d["dtype"],
                                threads=threads)
@@ -386,11 +426,15 @@ def cpu_baseline(w, budget_s):
     dt = time.time() - t0
     frac = 1.0 if used is None else used / units
     n = units if used is None else used
+    if used is None:
+        sample = (f"{rounds} full rounds of the workload ({units} block(s), "
+                  f"{min(threads, units)} thread(s)) in {dt:.1f}s (fp64 oracle)")
+    else:
+        sample = (f"{rounds} rounds of the first {used} of the workload's {units} requests "
+                  f"on one thread in {dt:.1f}s (fp64 oracle), scaled to bytes per second")
     return {"value": round(w.bytes * frac * rounds / dt / 1e9, 4), "unit": "GB/s",
             "cores": min(threads, n), "kind": "oracle",
-            "rounds_per_s": round(rounds / dt, 3),
-            "sample": f"{rounds} rounds of {n} {what} of the workload in {dt:.1f}s "
-                      f"(fp64 oracle)"}
+            "rounds_per_s": round(rounds / dt, 3), "sample": sample}
 
 
 def copy_calibration(nbytes, reps, torch):
@@ -414,7 +458,8 @@ def main():
     ap.add_argument("--config", type=str, default=str(HEADLINE_CFG),
                     help="workload for the headline line (1-5; pm3 / pm5 for the point-mass "
                          "workloads with the shapes of configs 3 and 5; outcome for outcome "
-                         "scoring; treebuild for draft-tree construction)")
+                         "scoring; treebuild for draft-tree construction; stree for stochastic "
+                         "tree verification)")
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip the other workloads in the per_config field")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -438,7 +483,7 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     hip = HipEvents()
     default_steps = {1: 2000, 2: 2000, 3: 200, 4: 100, 5: 50, "pm3": 200, "pm5": 50,
-                     "outcome": 200, "treebuild": 100}
+                     "outcome": 200, "treebuild": 100, "stree": 30}
     cfg_arg = int(args.config) if args.config.isdigit() else args.config
 
     def run(cfg, steps):
@@ -446,6 +491,8 @@ def main():
             seed = 8077
         elif cfg == "treebuild":
             seed = 9077
+        elif cfg == "stree":
+            seed = 9177
         else:
             seed = 1000 * int(cfg[2:]) + 77 if isinstance(cfg, str) else 1000 * cfg + 7
         w = Workload(cfg, seed=seed, torch=torch, sv=sv)
@@ -491,7 +538,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_per_config:
         per = {}
-        for cfg in (3, 4, 5, "pm3", "pm5", "outcome", "treebuild"):
+        for cfg in (3, 4, 5, "pm3", "pm5", "outcome", "treebuild", "stree"):
             if cfg == cfg_arg:
                 continue
             try:

@@ -23,7 +23,8 @@ __all__ = [
     "spec_verify_chain", "spec_verify_tree_greedy", "spec_verify_chain_workspace_bytes",
     "spec_verify_chain_pointmass", "spec_verify_chain_pointmass_workspace_bytes",
     "spec_outcome_topk", "spec_outcome_topk_workspace_bytes", "spec_cache_lookup",
-    "spec_tree_build", "spec_tree_build_workspace_bytes",
+    "spec_tree_build", "spec_tree_build_workspace_bytes", "spec_verify_tree_stochastic",
+    "spec_verify_tree_stochastic_workspace_bytes",
     "spec_verify_tree_greedy_workspace_bytes", "spec_verify_status_string",
 ]
 
@@ -81,6 +82,11 @@ def load_library():
     lib.spec_outcome_topk.restype = I32
     lib.spec_verify_tree_greedy.argtypes = [P, I32, P, P, I32, I32, I32, P, P, P, P, SZ, P, P]
     lib.spec_verify_tree_greedy.restype = I32
+    lib.spec_verify_tree_stochastic_workspace_bytes.argtypes = [I32, I32, I32, I32]
+    lib.spec_verify_tree_stochastic_workspace_bytes.restype = SZ
+    lib.spec_verify_tree_stochastic.argtypes = [P, P, I32, P, P, P, I32, I32, I32, D, P, P, P, P,
+                                                P, SZ, P, P]
+    lib.spec_verify_tree_stochastic.restype = I32
     lib.spec_cache_lookup.argtypes = [P, P, I32, I32, P, P, I32, P, P]
     lib.spec_cache_lookup.restype = I32
     lib.spec_tree_build_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
@@ -111,6 +117,10 @@ def spec_outcome_topk_workspace_bytes(R: int, gamma: int, V: int, dtype: int, nc
 def spec_tree_build_workspace_bytes(R: int, M: int, V: int, dtype: int, W: int, max_depth: int,
                                     budget: int) -> int:
     return int(load_library().spec_tree_build_workspace_bytes(R, M, V, dtype, W, max_depth, budget))
+
+
+def spec_verify_tree_stochastic_workspace_bytes(B: int, n: int, V: int, dtype: int) -> int:
+    return int(load_library().spec_verify_tree_stochastic_workspace_bytes(B, n, V, dtype))
 
 
 def spec_verify_tree_greedy_workspace_bytes(B: int, n: int, V: int, dtype: int) -> int:
@@ -321,6 +331,58 @@ def spec_outcome_topk(logits, draft_tokens, temperature, ncache, *, out_k=None, 
     if st != 0:
         raise SpecVerifyError(st, "spec_outcome_topk")
     return out_k, out_a, out_p, hit
+
+
+def spec_verify_tree_stochastic(target_logits, draft_logits, parents, tokens, uniforms,
+                                temperature, *, want_dist=False, accept_len=None,
+                                accept_node=None, out_tokens=None, final_dist=None,
+                                workspace=None, stream=None, phase_events=None):
+    """Stochastic tree verification on the GPU.
+
+    target_logits, draft_logits [B, n, V] (float32 or bfloat16), parents and
+    tokens int32 [B, n], uniforms float32 [B, n] (column 0 drives the draw).
+    Returns (accept_len [B], accept_node [B], out_tokens [B, n], final_dist
+    [B, V] or None)."""
+    torch = _torch()
+    lib = load_library()
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, n, V]")
+    B, n, V = target_logits.shape
+    dev = target_logits.device
+    code = _dtype_code(target_logits)
+    _check(target_logits, "target_logits", (B, n, V), device=dev)
+    _check(draft_logits, "draft_logits", (B, n, V), dtype=target_logits.dtype, device=dev)
+    _check(parents, "parents", (B, n), dtype=torch.int32, device=dev)
+    _check(tokens, "tokens", (B, n), dtype=torch.int32, device=dev)
+    _check(uniforms, "uniforms", (B, n), dtype=torch.float32, device=dev)
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if accept_node is None:
+        accept_node = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, n), dtype=torch.int32, device=dev)
+    if want_dist and final_dist is None:
+        final_dist = torch.empty((B, V), dtype=torch.float32, device=dev)
+    _check(accept_len, "accept_len", (B,), dtype=torch.int32, device=dev)
+    _check(accept_node, "accept_node", (B,), dtype=torch.int32, device=dev)
+    _check(out_tokens, "out_tokens", (B, n), dtype=torch.int32, device=dev)
+    if final_dist is not None:
+        _check(final_dist, "final_dist", (B, V), dtype=torch.float32, device=dev)
+    need = spec_verify_tree_stochastic_workspace_bytes(B, n, V, code)
+    if need == 0:
+        raise SpecVerifyError(2, "spec_verify_tree_stochastic")
+    if workspace is None:
+        workspace = _workspace(need, dev, stream)
+    ev = _events(phase_events)
+    st = lib.spec_verify_tree_stochastic(
+        _ptr(target_logits), _ptr(draft_logits), code, _ptr(parents), _ptr(tokens),
+        _ptr(uniforms), B, n, V, float(temperature), _ptr(accept_len), _ptr(accept_node),
+        _ptr(out_tokens), _ptr(final_dist), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream_handle(stream, dev),
+        None if ev is None else ev[0])
+    if st != 0:
+        raise SpecVerifyError(st, "spec_verify_tree_stochastic")
+    return accept_len, accept_node, out_tokens, final_dist
 
 
 def spec_tree_build(draft_logits, temperature, width, max_depth, budget, *, child_row=None,

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspecverify.so")
-SOURCES = ["api.hip", "chain.hip", "tree.hip", "outcome.hip", "treebuild.hip"]
+SOURCES = ["api.hip", "chain.hip", "tree.hip", "outcome.hip", "treebuild.hip", "treestoch.hip"]
 ARCH = os.environ.get("SPEC_VERIFY_ARCH", "gfx950")
 
 # All device code is compiled without packed-fp32 instructions (the compiler

@@ -56,20 +56,17 @@ size_t carve(size_t* off, size_t size, size_t n) {
 
 // Plan of a chain call: rows per block are 2*gamma+1 (target and draft
 // logits) for the ratio test, gamma+1 (target only) for a point-mass draft.
-int32_t chain_plan(int32_t B, int32_t gamma, int32_t V, int32_t dtype, bool pointmass,
-                   ChainPlan* p) {
-    if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
-    if (B < 1 || gamma < 1 || V < 1 || gamma > kMaxGamma) return SV_ERR_SHAPE;
+// Statistics segments, final-draw chunks and workspace for B blocks of `rows`
+// logit rows each (chains; stochastic trees, whose blocks are requests).
+int32_t block_plan(int32_t B, int64_t rows, int32_t V, int32_t dtype, ChainPlan* p) {
     const int E = elem_bytes(dtype), epv = 16 / E;
-    const int64_t rows = (pointmass ? 1 : 2) * static_cast<int64_t>(gamma) + 1;
     const int64_t rows_total = static_cast<int64_t>(B) * rows;
     // every element index and byte offset must fit comfortably in int64, and
     // grid sizes in int32
     if (static_cast<double>(rows_total) * V * E > 9.0e18) return SV_ERR_SHAPE;
     p->rows = static_cast<int>(rows);
-    // a block's rows*nseg partials are staged in LDS by the chunk kernel
-    // fewer, longer segments keep the partials every chunk workgroup merges
-    // for its block's decision few
+    // a block's rows*nseg partials are staged in LDS by the kernel that takes
+    // its decision; fewer, longer segments keep them few
     plan_segments(rows_total, V, epv, kChainUnits, 4,
                   static_cast<int>(kMaxBlockParts / rows), &p->nseg, &p->seg_len);
     if (rows_total * p->nseg > INT32_MAX) return SV_ERR_SHAPE;
@@ -92,6 +89,20 @@ int32_t chain_plan(int32_t B, int32_t gamma, int32_t V, int32_t dtype, bool poin
     p->off_fin = carve(&off, sizeof(FinalState), nb);
     p->bytes = off;
     return SV_OK;
+}
+
+int32_t chain_plan(int32_t B, int32_t gamma, int32_t V, int32_t dtype, bool pointmass,
+                   ChainPlan* p) {
+    if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
+    if (B < 1 || gamma < 1 || V < 1 || gamma > kMaxGamma) return SV_ERR_SHAPE;
+    return block_plan(B, (pointmass ? 1 : 2) * static_cast<int64_t>(gamma) + 1, V, dtype, p);
+}
+
+// Stochastic tree verification: n target rows and n draft rows per request.
+int32_t tree_stoch_plan(int32_t B, int32_t n, int32_t V, int32_t dtype, ChainPlan* p) {
+    if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
+    if (B < 1 || n < 1 || V < 1 || n > kMaxTreeNodes) return SV_ERR_SHAPE;
+    return block_plan(B, 2 * static_cast<int64_t>(n), V, dtype, p);
 }
 
 struct TreePlan {
@@ -258,6 +269,8 @@ int32_t chain_call(const void* target_logits, const void* draft_logits, bool poi
     a.V = V;
     a.pointmass = pointmass ? 1 : 0;
     a.rows = p.rows;
+    a.draft_rows = gamma;
+    a.given = 0;
     // log2(e)/T as c_hi + c_lo with c_hi the largest float strictly below c,
     // so c_lo > 0: a -inf logit then scales to -inf in both parts and never
     // meets +inf (which would give NaN) when the two products are added.
@@ -443,6 +456,85 @@ extern "C" int32_t spec_tree_build(const void* draft_logits, int32_t dtype,
         hipSuccess)
         return SV_ERR_HIP;
     if (launch_tree_search(a, s) != hipSuccess) return SV_ERR_HIP;
+    return SV_OK;
+}
+
+extern "C" size_t spec_verify_tree_stochastic_workspace_bytes(int32_t B, int32_t n, int32_t V,
+                                                              int32_t dtype) {
+    ChainPlan p;
+    return tree_stoch_plan(B, n, V, dtype, &p) == SV_OK ? p.bytes : 0;
+}
+
+extern "C" int32_t spec_verify_tree_stochastic(
+    const void* target_logits, const void* draft_logits, int32_t dtype, const int32_t* parents,
+    const int32_t* tokens, const float* uniforms, int32_t B, int32_t n, int32_t V,
+    double temperature, int32_t* accept_len, int32_t* accept_node, int32_t* out_tokens,
+    float* final_dist, void* workspace, size_t workspace_bytes, void* stream,
+    void* const* phase_events) {
+    ChainPlan p;
+    const int32_t st = tree_stoch_plan(B, n, V, dtype, &p);
+    if (st != SV_OK) return st;
+    if (!target_logits || !draft_logits || !parents || !tokens || !uniforms || !accept_len ||
+        !accept_node || !out_tokens || !workspace)
+        return SV_ERR_NULL;
+    if (!std::isfinite(temperature) || temperature < 1e-6 || temperature > 1e6)
+        return SV_ERR_TEMPERATURE;
+    const size_t E = static_cast<size_t>(elem_bytes(dtype));
+    if (!aligned(target_logits, E) || !aligned(draft_logits, E) || !aligned(parents, 4) ||
+        !aligned(tokens, 4) || !aligned(uniforms, 4) || !aligned(accept_len, 4) ||
+        !aligned(accept_node, 4) || !aligned(out_tokens, 4) ||
+        (final_dist && !aligned(final_dist, 4)))
+        return SV_ERR_ALIGN;
+    if (!aligned(workspace, 16) || workspace_bytes < p.bytes) return SV_ERR_WORKSPACE;
+    TreeStochArgs t;
+    ChainArgs& a = t.ch;
+    a = ChainArgs{};
+    a.target = target_logits;
+    a.draft = draft_logits;
+    a.tokens = nullptr;  // the statistics pass gathers nothing; the decision does
+    a.uniforms = uniforms;
+    a.B = B;
+    a.gamma = n - 1;     // n target rows per request
+    a.V = V;
+    a.pointmass = 1;     // the draw is from p itself, no residual
+    a.rows = p.rows;     // 2n
+    a.draft_rows = n;
+    a.given = 1;
+    const double c = 1.4426950408889634074 / temperature;
+    float c_hi = static_cast<float>(c);
+    if (static_cast<double>(c_hi) >= c) c_hi = std::nextafter(c_hi, 0.0f);
+    a.c_hi = c_hi;
+    a.c_lo = static_cast<float>(c - static_cast<double>(c_hi));
+    a.c_d = static_cast<double>(a.c_hi) + static_cast<double>(a.c_lo);
+    a.T = temperature;
+    a.nseg = p.nseg;
+    a.seg_len = p.seg_len;
+    a.nchunk = p.nchunk;
+    a.chunk_tiles = p.chunk_tiles;
+    a.nquart = p.nquart;
+    char* ws = static_cast<char*>(workspace);
+    a.part = reinterpret_cast<Stat*>(ws + p.off_part);
+    a.zx = nullptr;
+    a.dec = reinterpret_cast<ChainDecision*>(ws + p.off_dec);
+    a.qsum = reinterpret_cast<double*>(ws + p.off_qsum);
+    a.fin = reinterpret_cast<FinalState*>(ws + p.off_fin);
+    a.accept_len = accept_len;
+    a.out_tokens = out_tokens;
+    a.final_dist = final_dist;
+    t.parents = parents;
+    t.node_tokens = tokens;
+    t.n = n;
+    t.dtype = dtype;
+    t.accept_node = accept_node;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (launch_chain_stats(a, dtype, s, event_at(phase_events, 0), event_at(phase_events, 1)) !=
+        hipSuccess)
+        return SV_ERR_HIP;
+    if (launch_tree_stoch_decide(t, s) != hipSuccess) return SV_ERR_HIP;
+    if (launch_chain_chunks(a, dtype, s) != hipSuccess) return SV_ERR_HIP;
+    if (launch_chain_select(a, dtype, s) != hipSuccess) return SV_ERR_HIP;
+    if (record(phase_events, 2, s) != SV_OK) return SV_ERR_HIP;
+    if (final_dist && launch_chain_dist(a, dtype, s) != hipSuccess) return SV_ERR_HIP;
     return SV_OK;
 }
 

@@ -49,7 +49,7 @@ __device__ inline const typename E::storage* chain_row(const ChainArgs& a, int b
         return static_cast<const S*>(a.target) + (static_cast<int64_t>(b) * (a.gamma + 1) + rho) *
                                                      static_cast<int64_t>(a.V);
     return static_cast<const S*>(a.draft) +
-           (static_cast<int64_t>(b) * a.gamma + (rho - a.gamma - 1)) * static_cast<int64_t>(a.V);
+           (static_cast<int64_t>(b) * a.draft_rows + (rho - a.gamma - 1)) * static_cast<int64_t>(a.V);
 }
 
 template <class E>
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
     // i < gamma (target) and gamma+1+i (draft) belong to draft position i.
     float zx = 0.0f;
     bool have_zx = false;
-    if (tid == 0) {
+    if (tid == 0 && a.tokens) {  // (tree rows have no per-row draft token)
         const int i = rho < a.gamma ? rho : (rho > a.gamma ? rho - a.gamma - 1 : -1);
         if (i >= 0) {
             const int x = a.tokens[static_cast<int64_t>(b) * a.gamma + i];
@@ -435,8 +435,13 @@ __global__ __launch_bounds__(kThreads) void chain_chunks_kernel(ChainArgs a) {
     const int b = blockIdx.x / a.nchunk;
     const int c = blockIdx.x % a.nchunk;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const ChainDecision d = chain_decide<E>(a, b, s_part);
-    if (c == 0 && tid == 0) a.dec[b] = d;
+    ChainDecision d;
+    if (a.given) {
+        d = load_decision(a, b);
+    } else {
+        d = chain_decide<E>(a, b, s_part);
+        if (c == 0 && tid == 0) a.dec[b] = d;
+    }
     if (d.k < 0) return;  // invalid block: the select kernel writes -1s
     const FinalRows<E> rows = final_rows<E>(a, b, d.k);
     const DrawRow r = draw_row(a, d);
@@ -486,9 +491,10 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
 #pragma unroll
     for (int j = 0; j < kRun; ++j) run_v[j] = q0 + j < q1 ? qs[q0 + j] : 0.0;
     const ChainDecision d = load_decision(a, b);
-    const double u = static_cast<double>(a.uniforms[static_cast<int64_t>(b) * (g + 1) + g]);
+    const double u =
+        static_cast<double>(a.uniforms[static_cast<int64_t>(b) * (g + 1) + (a.given ? 0 : g)]);
     if (d.k < 0) {
-        write_outputs<E>(a, b, -1, -1);
+        if (!a.given) write_outputs<E>(a, b, -1, -1);  // (a given decision wrote its own)
         return;
     }
     const FinalRows<E> rows = final_rows<E>(a, b, d.k);
@@ -622,7 +628,11 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
         token = pl ? __shfl(lastpos, 63 - __clzll(static_cast<long long>(pl)), 64)
                    : min(qstar * kQuart, a.V - 1);
     }
-    write_outputs<E>(a, b, d.k, token);
+    if (a.given) {
+        if (lane == 0) a.out_tokens[static_cast<int64_t>(b) * (g + 1) + d.pad] = token;
+    } else {
+        write_outputs<E>(a, b, d.k, token);
+    }
     if (lane == 0 && a.final_dist) a.fin[b] = FinalState{W, fallback, 0};
 }
 
@@ -669,7 +679,7 @@ hipError_t launch_chain_stats(const ChainArgs& a, int dtype, hipStream_t s, hipE
 
 hipError_t launch_chain_chunks(const ChainArgs& a, int dtype, hipStream_t s) {
     const dim3 grid(a.B * a.nchunk);
-    const size_t lds = sizeof(Stat) * static_cast<size_t>(a.rows) * a.nseg;
+    const size_t lds = a.given ? 0 : sizeof(Stat) * static_cast<size_t>(a.rows) * a.nseg;
     auto go = [&](auto kernel) {
         hipLaunchKernelGGL(kernel, grid, dim3(kThreads), lds, s, a);
         return hipGetLastError();

@@ -404,4 +404,48 @@ __device__ inline uint64_t wave_max_u64(uint64_t x) {
     return readlane64(x, 63);
 }
 
+
+// ---------------------------------------------------------------------------
+// Tree paths by pointer jumping (greedy and stochastic tree verification).
+// On entry, for every node j < n: s_anc[j] its parent (root: 0), s_dep[j] = 1
+// (root: 0), s_ok[j] whether the edge into j passes its test (root: 1), and
+// *s_key = -1.  After ceil(log2 n) rounds s_anc[j] is the root, s_dep[j] the
+// depth and s_ok[j] whether every edge on the path passed; *s_key then holds
+// (depth << 11) | (2047 - index) of the deepest such node, the lowest index
+// among equally deep ones.  All threads of the workgroup call it (n <= 1024,
+// at most kMaxTreeNodes / kThreads nodes per thread).
+__device__ inline void deepest_accepted(int n, int* s_anc, int* s_dep, unsigned char* s_ok,
+                                        int* s_key) {
+    constexpr int kPer = kMaxTreeNodes / kThreads;
+    const int tid = threadIdx.x;
+    for (int span = 1; span < n; span <<= 1) {
+        int nanc[kPer], ndep[kPer];
+        unsigned char nok[kPer];
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int j = tid + m * kThreads;
+            if (j < n) {
+                const int up = s_anc[j];
+                nok[m] = s_ok[j] & s_ok[up];
+                ndep[m] = s_dep[j] + s_dep[up];
+                nanc[m] = s_anc[up];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int j = tid + m * kThreads;
+            if (j < n) {
+                s_ok[j] = nok[m];
+                s_dep[j] = ndep[m];
+                s_anc[j] = nanc[m];
+            }
+        }
+        __syncthreads();
+    }
+    for (int j = tid; j < n; j += kThreads)
+        if (s_ok[j]) atomicMax(s_key, (s_dep[j] << 11) | (2047 - j));
+    __syncthreads();
+}
+
 }  // namespace sv

@@ -32,7 +32,7 @@ struct ChainDecision {
     float Rp;      // integer reference R of target row k
     double dL;     // (R_p + log2 S_p) - (R_q + log2 S_q) at row k (ratio test, k < gamma), else 0
     int32_t excl;  // point mass, k < gamma: the rejected draft token (weight 0 in the draw); else -1
-    int32_t pad;
+    int32_t pad;   // tree verification: accept length (where the drawn token goes); else 0
 };
 
 // Normaliser of the final draw of one block, kept for the final_dist pass.
@@ -50,6 +50,11 @@ struct ChainArgs {
     int B, gamma, V;
     int pointmass;     // 1: the draft proposes each token with certainty (no draft logits)
     int rows;          // logit rows per block: 2*gamma+1 (target and draft), or gamma+1
+    int draft_rows;    // draft rows per block (the draft array's block stride): gamma, or
+                       // gamma+1 for tree rows
+    int given;         // 1: dec[b] was written by an earlier kernel (tree verification);
+                       // the draw takes uniforms[b][0] and writes only its token, at
+                       // out_tokens[b][dec.pad]
     float c_hi, c_lo;  // log2(e)/T as a float pair
     double c_d;        // c_hi + c_lo exactly
     double T;
@@ -132,6 +137,17 @@ struct TreeBuildArgs {
     int32_t* n_nodes;        // [R]
 };
 
+// Stochastic tree verification: the chain statistics over n target and n
+// draft rows per request, a per-request decision, then the chain draw.
+struct TreeStochArgs {
+    ChainArgs ch;               // gamma = n-1, rows = 2n, draft_rows = n, given = 1
+    const int32_t* parents;     // [B][n]
+    const int32_t* node_tokens; // [B][n]
+    int n;
+    int dtype;                  // 0 f32, 1 bf16
+    int32_t* accept_node;       // [B]
+};
+
 // Launchers (return the hipError_t of the launch).
 // The streaming launchers take an optional pair of events (both null, or
 // both valid): when given, the launch itself records them at the kernel's
@@ -149,6 +165,7 @@ hipError_t launch_outcome_stats(const OutcomeArgs& a, int dtype, hipStream_t s,
                                 hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_outcome_select(const OutcomeArgs& a, hipStream_t s);
 hipError_t launch_tree_search(const TreeBuildArgs& a, hipStream_t s);
+hipError_t launch_tree_stoch_decide(const TreeStochArgs& t, hipStream_t s);
 hipError_t launch_cache_lookup(const int32_t* accept_len, const int32_t* out_tokens, int R,
                                int gamma, const int32_t* cache_k, const int32_t* cache_a,
                                int ncache, int32_t* slot, hipStream_t s);

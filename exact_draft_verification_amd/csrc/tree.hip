@@ -113,7 +113,6 @@ __device__ void tree_resolve(const TreeArgs& a, int b, ArgmaxPart* s_part) {
     __shared__ int s_amax[kMaxTreeNodes];
     __shared__ unsigned char s_ok[kMaxTreeNodes];
     __shared__ int s_bad, s_key;
-    constexpr int kPer = kMaxTreeNodes / kThreads;
     constexpr int kStage = kMaxBlockParts / kThreads;
     const int n = a.n, tid = threadIdx.x;
     const int32_t* par = a.parents + static_cast<int64_t>(b) * n;
@@ -183,35 +182,7 @@ __device__ void tree_resolve(const TreeArgs& a, int b, ArgmaxPart* s_part) {
         }
     }
     __syncthreads();
-    for (int span = 1; span < n; span <<= 1) {
-        int nanc[kPer], ndep[kPer];
-        unsigned char nok[kPer];
-#pragma unroll
-        for (int m = 0; m < kPer; ++m) {
-            const int j = tid + m * kThreads;
-            if (j < n) {
-                const int up = s_anc[j];
-                nok[m] = s_ok[j] & s_ok[up];
-                ndep[m] = s_dep[j] + s_dep[up];
-                nanc[m] = s_anc[up];
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int m = 0; m < kPer; ++m) {
-            const int j = tid + m * kThreads;
-            if (j < n) {
-                s_ok[j] = nok[m];
-                s_dep[j] = ndep[m];
-                s_anc[j] = nanc[m];
-            }
-        }
-        __syncthreads();
-    }
-    // deepest accepted node, lowest index on ties: maximise (depth, -index)
-    for (int j = tid; j < n; j += kThreads)
-        if (s_ok[j]) atomicMax(&s_key, (s_dep[j] << 11) | (2047 - j));
-    __syncthreads();
+    deepest_accepted(n, s_anc, s_dep, s_ok, &s_key);
     const int key = s_key;
     const int depth = key >> 11;
     const int vstar = 2047 - (key & 2047);

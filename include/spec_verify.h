@@ -191,6 +191,49 @@ int32_t spec_verify_tree_greedy(const void *target_logits, int32_t dtype,
                                 int32_t *out_tokens, void *workspace, size_t workspace_bytes,
                                 void *stream, void *const *phase_events);
 
+/* Bytes of workspace spec_verify_tree_stochastic needs; 0 if the sizes or
+ * dtype are invalid. */
+size_t spec_verify_tree_stochastic_workspace_bytes(int32_t B, int32_t n, int32_t V, int32_t dtype);
+
+/* Stochastic tree verification ("JetSpec" reading notes, section "Tree
+ * verification": Eq. 16 and 17, Fig. 5).  For each of B requests, a
+ * candidate tree of n nodes with target and draft logits per node; p_j and
+ * q_j are the temperature softmax of target row j and draft row j, the
+ * distributions of the token after node j's path.
+ *  - Every node j >= 1 takes one Bernoulli test: accepted iff
+ *    u[b][j] < min(1, p_par(y_j) / q_par(y_j)) with par = parents[j] and y_j
+ *    = tokens[j] (a token of probability 0 under p is rejected; one of
+ *    probability 0 under q but not under p is accepted).
+ *  - A node counts as accepted iff every node on its path passed; v* is the
+ *    deepest accepted node (lowest index among equally deep ones), the root
+ *    if none.
+ *  - The correction token is drawn from p_{v*} with u[b][0], by inverse CDF
+ *    in ascending token id: the smallest v whose inclusive prefix sum
+ *    exceeds u * (the total).  The pages give no residual rule for branches
+ *    rejected below v*, and none is applied.
+ *
+ *  target_logits, draft_logits  [B][n][V] dtype.
+ *  parents, tokens  [B][n] int32, as for spec_verify_tree_greedy.
+ *  uniforms      [B][n] float32 in [0, 1): u[b][0] drives the draw, u[b][j]
+ *                node j's test.
+ *  accept_len, accept_node, out_tokens  as for spec_verify_tree_greedy (the
+ *                drawn token follows the path).
+ *  final_dist    NULLABLE [B][V] float32: p_{v*} (zeros for an invalid
+ *                request).
+ *  An invalid request (a malformed parent array, a token outside [0, V), a
+ *  NaN or +inf logit or a row without a finite logit in any target or draft
+ *  row, or |max finite logit| / T > 2^28) gets accept_len = accept_node = -1
+ *  and all tokens -1.
+ *  workspace, stream, phase_events: as for spec_verify_chain (events [0] and
+ *  [1] bracket the statistics pass over all 2n rows, [2] follows the draw). */
+int32_t spec_verify_tree_stochastic(const void *target_logits, const void *draft_logits,
+                                    int32_t dtype, const int32_t *parents, const int32_t *tokens,
+                                    const float *uniforms, int32_t B, int32_t n, int32_t V,
+                                    double temperature, int32_t *accept_len, int32_t *accept_node,
+                                    int32_t *out_tokens, float *final_dist, void *workspace,
+                                    size_t workspace_bytes, void *stream,
+                                    void *const *phase_events);
+
 /* Cache entries per request of spec_outcome_topk. */
 #define SV_MAX_CACHE 16
 

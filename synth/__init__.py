@@ -449,6 +449,80 @@ def tree_inputs(B: int, n: int, V: int, sigma: float = 2.0, max_depth: int = 16,
                 dtype="bf16")
 
 
+# Stochastic tree verification: config 4's trees with draft logits per node
+# and node tokens drawn from the draft at their parent.
+STREE_CONFIG = dict(B=64, n=64, V=151936, dtype="bf16", T=1.0, target=("normal", 2.0),
+                    noise=1.0, max_depth=16, max_children=4)
+
+
+def _stree_request(seed_seq, n, V, dtype, T, target, noise, max_depth, max_children):
+    rng = np.random.default_rng(seed_seq)
+    parents = _tree_parents(rng, n, max_depth, max_children)
+    kind, scale = target
+    if kind == "normal":
+        t = rng.standard_normal((n, V), dtype=np.float32) * np.float32(scale)
+    elif kind == "gumbel":
+        t = _gumbel(rng, (n, V)) * np.float32(scale)
+    else:
+        raise ValueError(f"unknown target distribution {kind!r}")
+    d = t + rng.standard_normal((n, V), dtype=np.float32) * np.float32(noise)
+    t_st, d_st = _store(t, dtype), _store(d, dtype)
+    # node j's token ~ q at its parent (Gumbel-max over the stored draft row)
+    dq = _as_f32(d_st, dtype).astype(np.float64) / T
+    tokens = np.zeros(n, dtype=np.int32)
+    for j in range(1, n):
+        tokens[j] = int(np.argmax(dq[parents[j]] + _gumbel(rng, V)))
+    u = rng.random(n, dtype=np.float32)
+    return t_st, d_st, parents, tokens, u
+
+
+def stree_inputs(B: int, n: int, V: int, dtype: str = "bf16", T: float = 1.0,
+                 target=("normal", 2.0), noise: float = 1.0, max_depth: int = 16,
+                 max_children: int = 4, seed: int = 0, threads: int | None = None) -> dict:
+    """Inputs for one stochastic tree-verification call: ``target`` and
+    ``draft`` [B, n, V] (row j = logits after node j's path), ``parents`` and
+    ``tokens`` int32 [B, n] (node tokens drawn from the draft at their
+    parent), ``uniforms`` float32 [B, n]."""
+    if B < 1 or n < 1 or V < 1:
+        raise ValueError("B, n and V must be >= 1")
+    st = np.uint16 if dtype == "bf16" else np.float32
+    tgt = np.empty((B, n, V), dtype=st)
+    drf = np.empty((B, n, V), dtype=st)
+    par = np.empty((B, n), dtype=np.int32)
+    tok = np.empty((B, n), dtype=np.int32)
+    uni = np.empty((B, n), dtype=np.float32)
+    children = np.random.SeedSequence(seed).spawn(B)
+
+    def work(b):
+        tgt[b], drf[b], par[b], tok[b], uni[b] = _stree_request(
+            children[b], n, V, dtype, T, target, noise, max_depth, max_children)
+
+    nw = _workers(B, threads)
+    if nw == 1:
+        for b in range(B):
+            work(b)
+    else:
+        with _cf.ThreadPoolExecutor(nw) as ex:
+            list(ex.map(work, range(B)))
+    return dict(kind="stree", target=tgt, draft=drf, parents=par, tokens=tok, uniforms=uni, B=B,
+                n=n, V=V, dtype=dtype, T=float(T))
+
+
+def stree_config_inputs(seed: int = 0, threads: int | None = None, **overrides) -> dict:
+    c = dict(STREE_CONFIG)
+    c.update(overrides)
+    return stree_inputs(c["B"], c["n"], c["V"], c["dtype"], c["T"], c["target"], c["noise"],
+                        c["max_depth"], c["max_children"], seed=seed, threads=threads)
+
+
+def stree_config_bytes(**overrides) -> int:
+    """Algorithmic logit bytes of one stochastic tree call (target and draft)."""
+    c = dict(STREE_CONFIG)
+    c.update(overrides)
+    e = 4 if c["dtype"] == "f32" else 2
+    return 2 * c["B"] * c["n"] * c["V"] * e
+
+
 def config_inputs(cfg: int, seed: int = 0, threads: int | None = None, **overrides) -> dict:
     """Inputs for one of the five workloads, with optional shape overrides."""
     c = dict(CONFIGS[cfg])

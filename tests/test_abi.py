@@ -41,7 +41,8 @@ def test_exports_every_declared_symbol(lib):
             "spec_verify_tree_greedy_workspace_bytes", "spec_verify_status_string",
             "spec_verify_chain_pointmass", "spec_verify_chain_pointmass_workspace_bytes",
             "spec_outcome_topk", "spec_outcome_topk_workspace_bytes",
-            "spec_cache_lookup", "spec_tree_build", "spec_tree_build_workspace_bytes"} <= set(names)
+            "spec_cache_lookup", "spec_tree_build", "spec_tree_build_workspace_bytes",
+            "spec_verify_tree_stochastic", "spec_verify_tree_stochastic_workspace_bytes"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
@@ -275,6 +276,46 @@ def test_tree_build_host_errors(lib):
     assert (n == 5).all()
     assert sv.spec_tree_build_workspace_bytes(32, 85, 151936, 1, 4, 4, 64) > 0
     assert sv.spec_tree_build_workspace_bytes(32, 85, 151936, 1, 17, 4, 64) == 0
+
+
+def test_tree_stochastic_host_errors(lib):
+    import exact_draft_verification_amd as sv
+
+    c = header_constants()
+    B, n, V = 2, 5, 64
+    t = np.zeros((B, n, V), np.uint16)
+    par = np.zeros((B, n), np.int32)
+    tok = np.zeros((B, n), np.int32)
+    u = np.zeros((B, n), np.float32)
+    acc = np.full(B, 9, np.int32)
+    node = np.zeros(B, np.int32)
+    out = np.zeros((B, n), np.int32)
+    ws = np.zeros(1 << 16, np.uint8)
+    wsa = ws[(-ws.ctypes.data) % 256:]
+
+    def call(**o):
+        args = dict(t=p(t), d=p(t), dt=1, par=p(par), tok=p(tok), u=p(u), B=B, n=n, V=V, T=1.0,
+                    acc=p(acc), node=p(node), out=p(out), ws=p(wsa), wsb=16)
+        args.update(o)
+        return lib.spec_verify_tree_stochastic(args["t"], args["d"], args["dt"], args["par"],
+                                               args["tok"], args["u"], args["B"], args["n"],
+                                               args["V"], args["T"], args["acc"], args["node"],
+                                               args["out"], None, args["ws"], args["wsb"], None,
+                                               None)
+
+    assert call(d=None) == c["SV_ERR_NULL"]
+    assert call(u=None) == c["SV_ERR_NULL"]
+    assert call(node=None) == c["SV_ERR_NULL"]
+    assert call(B=0) == c["SV_ERR_SHAPE"]
+    assert call(n=0) == c["SV_ERR_SHAPE"]
+    assert call(n=c["SV_MAX_TREE_NODES"] + 1) == c["SV_ERR_SHAPE"]
+    assert call(dt=5) == c["SV_ERR_DTYPE"]
+    assert call(T=-1.0) == c["SV_ERR_TEMPERATURE"]
+    assert call(d=ct.c_void_p(t.ctypes.data + 1)) == c["SV_ERR_ALIGN"]
+    assert call(wsb=16) == c["SV_ERR_WORKSPACE"]
+    assert (acc == 9).all()
+    assert sv.spec_verify_tree_stochastic_workspace_bytes(64, 64, 151936, 1) > 0
+    assert sv.spec_verify_tree_stochastic_workspace_bytes(64, 1025, 151936, 1) == 0
 
 
 def test_tree_host_errors(lib):

@@ -81,3 +81,27 @@ def test_workspace_garbage_for_outcomes_and_tree_construction():
             assert np.array_equal(par.cpu().numpy()[r], o["parents"][r])
             assert np.array_equal(tok.cpu().numpy()[r], o["tokens"][r])
             assert np.array_equal(row.cpu().numpy()[r], o["rows"][r])
+
+
+def test_workspace_garbage_for_stochastic_trees():
+    torch, sv = require_gpu()
+    from gpu_util import to_dev, to_dev_logits
+
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    for i, (B, n, V, dt) in enumerate([(3, 17, 5003, "bf16"), (1, 1024, 200, "f32"),
+                                       (5, 9, 151936, "bf16")]):
+        print(f"[case] shared workspace stochastic-tree call {i}", flush=True)
+        d = synth.stree_inputs(B, n, V, dt, T=0.8, seed=70 + i)
+        ws.fill_([0xFF, 0x00, 0xA5][i])
+        acc, node, out, dist = sv.spec_verify_tree_stochastic(
+            to_dev_logits(d["target"], dt), to_dev_logits(d["draft"], dt),
+            to_dev(d["parents"], np.int32), to_dev(d["tokens"], np.int32),
+            to_dev(d["uniforms"], np.float32), d["T"], want_dist=True, workspace=ws)
+        torch.cuda.synchronize()
+        o = oracle.tree_stochastic(d["target"], d["draft"], d["parents"], d["tokens"],
+                                   d["uniforms"], d["T"], dtype=dt, want_dist=True)
+        keep = o["margin"] >= 1e-6
+        assert np.array_equal(acc.cpu().numpy()[keep], o["accept_len"][keep])
+        assert np.array_equal(out.cpu().numpy()[keep], o["out_tokens"][keep])
+        same = node.cpu().numpy() == o["accept_node"]
+        assert np.abs(dist.cpu().numpy()[same] - o["final_dist"][same]).max() <= 1e-5
