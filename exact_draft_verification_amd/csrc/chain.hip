@@ -12,28 +12,39 @@
 // from the bonus row p_gamma if every test passed ("A fully accepted block
 // yields more than one committed token"; "JetSpec++", Appendix F.1).
 //
+// Point-mass mode ("JetSpec++", Appendix F.3 and Proposition 1): no draft
+// logits; position i passes iff u_i < p_i(x_i), and after a rejection at k
+// the draw is from p_k without x_k.
+//
 // Kernels, in stream order (data crosses workgroups only at kernel
 // boundaries, so no workgroup ever waits on another):
 //  1. chain_stats: one workgroup per (block, row, segment) streams its share
-//     of the 2*gamma+1 rows once, folds it into (m, R, S) statistics and
-//     writes them as one partial; the workgroup whose segment holds a row's
-//     draft token also records that token's logit.
+//     of the block's rows once, folds it into (m, R, S) statistics and writes
+//     them as one partial; the workgroup whose segment holds a row's draft
+//     token also records that token's logit.
 //  2. chain_chunks: one workgroup per (block, chunk of the vocabulary) merges
 //     the block's partials (staged in LDS), evaluates every ratio of the block
-//     in fp64, finds the first rejection k, and sums the draw weights of its
-//     chunk of the final row (residual row k, or the bonus row).
-//  3. chain_select: one workgroup per block scans the chunk sums, finds the
-//     chunk holding u_gamma * W and resolves the token inside it with one
-//     workgroup-wide prefix sum in token order.
+//     in fp64, finds the first rejection k, and writes the draw-weight sum of
+//     every quarter (64 16-byte vectors) of its chunk of the final row
+//     (residual row k, p_k without x_k, or the bonus row).
+//  3. chain_select: one wave per block scans the quarter sums, finds the
+//     quarter holding u_gamma * W and resolves the token inside it with a
+//     second wave scan in token order.
 //  4. chain_dist (only when final_dist is requested): writes the normalised
 //     draw distribution.
+// Stochastic tree verification (treestoch.hip) reuses 1-4: its statistics
+// pass covers n target and n draft rows per request (draft_rows = n, no
+// per-row draft token), and with `given` set the chunk kernel reads the
+// decision an earlier kernel wrote (row v*, a plain p draw) and the select
+// kernel writes only the drawn token, after the accepted path.
 //
 // Numerics.  Ratios are evaluated in the log2 domain in fp64 from the row
 // statistics, so they are accurate to about 1e-8 whatever the dynamic range.
 // The residual weight is formed as p(v) * (1 - 2^-D(v)) with
-// D(v) = log2 p(v) - log2 q(v) computed in fp64 from the logit difference, so
-// neither the subtraction p - q nor a constant offset between the target and
-// draft logits costs precision; weights are fp32, sums and prefix sums fp64.
+// D(v) = log2 p(v) - log2 q(v) taken from the exact logit difference (float
+// pairs for bf16, fp64 for fp32), so neither the subtraction p - q nor a
+// constant offset between the target and draft logits costs precision;
+// weights are fp32, sums and prefix sums fp64.
 #include "sv_device.hpp"
 
 namespace sv {

@@ -148,3 +148,39 @@ def test_pointmass_inputs():
     rate = (d["draft_tokens"] == amax).mean()
     assert 0.76 < rate < 0.84
     assert synth.pointmass_config_bytes(3) == 64 * 17 * 151936 * 2
+
+
+def test_treebuild_inputs():
+    d = synth.treebuild_inputs(3, 21, 500, "bf16", logits=("gumbel", 2.0), seed=4)
+    assert d["logits"].shape == (3, 21, 500) and d["logits"].dtype == np.uint16
+    e = synth.treebuild_inputs(3, 21, 500, "bf16", logits=("gumbel", 2.0), seed=4, threads=1)
+    assert np.array_equal(d["logits"], e["logits"])  # per-request streams: thread count free
+    assert synth.complete_tree_rows(4, 4) == 85 and synth.complete_tree_rows(1, 5) == 5
+    c = synth.TREEBUILD_CONFIG
+    assert synth.treebuild_config_bytes() == (c["R"] * synth.complete_tree_rows(c["W"], c["N"])
+                                             * c["V"] * 2)
+
+
+def test_stree_inputs_structure_and_token_law():
+    """Parents precede children within the caps; each node's token follows
+    q at its parent (Gumbel-max): over many requests, the token equals the
+    parent draft row's argmax about as often as the softmax predicts."""
+    d = synth.stree_inputs(40, 12, 30, "f32", T=1.0, target=("normal", 1.0), noise=0.5,
+                           max_depth=4, max_children=3, seed=5)
+    par, tok = d["parents"], d["tokens"]
+    assert (par[:, 0] == -1).all()
+    hit, want = 0, 0.0
+    for b in range(40):
+        depth = np.zeros(12, int)
+        for j in range(1, 12):
+            assert 0 <= par[b, j] < j
+            depth[j] = depth[par[b, j]] + 1
+            q = np.exp(d["draft"][b, par[b, j]].astype(np.float64))
+            q /= q.sum()
+            want += q.max()
+            hit += tok[b, j] == int(np.argmax(d["draft"][b, par[b, j]]))
+        assert depth.max() <= 4 and np.bincount(par[b, 1:], minlength=12).max() <= 3
+    n = 40 * 11
+    assert abs(hit - want) < 5 * np.sqrt(want * (1 - want / n))
+    assert ((d["uniforms"] >= 0) & (d["uniforms"] < 1)).all()
+    assert synth.stree_config_bytes() == 2 * 64 * 64 * 151936 * 2
