@@ -396,16 +396,11 @@ __device__ inline float lane_weights(const float* zp, const float* zq, const Dra
                    : lane_weights_t<E, false>(zp, zq, r, e, w);
 }
 
-__device__ inline double wave_sum(double v) {
-#pragma unroll
-    for (int mask = 32; mask >= 1; mask >>= 1) v += wave_xor(v, mask);
-    return v;
-}
 
 // Exclusive prefix sum over the lanes of a wave, plus the wave total.
 __device__ inline double wave_exclusive_scan(double v, double* total) {
     const double incl = wave_inclusive_scan(v);
-    *total = __shfl(incl, 63, 64);
+    *total = readlane_f64(incl, 63);
     return incl - v;
 }
 

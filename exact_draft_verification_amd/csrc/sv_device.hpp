@@ -222,16 +222,65 @@ __device__ inline T wave_xor(T v, int mask) {
     return __shfl_xor(v, mask, 64);
 }
 
+// DPP lane moves (the move is one VALU operand modifier, no LDS round trip).
+// Lanes the move leaves out (rows outside ROWS, or a source past the row's
+// edge when BOUND is set) receive `old`.
+template <int CTRL, int ROWS, bool BOUND>
+__device__ inline double dpp_f64(double x, double old) {
+    const int lo = __builtin_amdgcn_update_dpp(__double2loint(old), __double2loint(x), CTRL, ROWS,
+                                               0xf, BOUND);
+    const int hi = __builtin_amdgcn_update_dpp(__double2hiint(old), __double2hiint(x), CTRL, ROWS,
+                                               0xf, BOUND);
+    return __hiloint2double(hi, lo);
+}
+template <int CTRL, int ROWS, bool BOUND>
+__device__ inline float dpp_f32(float x, float old) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(x), CTRL,
+                                                      ROWS, 0xf, BOUND));
+}
+__device__ inline double readlane_f64(double x, int l) {
+    const int lo = __builtin_amdgcn_readlane(__double2loint(x), l);
+    const int hi = __builtin_amdgcn_readlane(__double2hiint(x), l);
+    return __hiloint2double(hi, lo);
+}
+
+// One combining step of a wave-wide reduction: quad swaps, then half-row and
+// row mirrors leave every lane with its row's total; the row broadcasts
+// (row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3) carry the
+// totals up to lane 63.
+template <int CTRL, int ROWS>
+__device__ inline Stat dpp_stat(const Stat& s) {
+    Stat o;
+    o.m = dpp_f32<CTRL, ROWS, false>(s.m, -INFINITY);  // (the empty statistic elsewhere)
+    o.R = dpp_f32<CTRL, ROWS, false>(s.R, -FLT_MAX);
+    o.S = dpp_f64<CTRL, ROWS, false>(s.S, 0.0);
+    return o;
+}
+
+// The merge of the wave's statistics; every lane gets it.
 __device__ inline Stat wave_reduce_stat(Stat s) {
-#pragma unroll
-    for (int mask = 32; mask >= 1; mask >>= 1) {
-        Stat o;
-        o.m = wave_xor(s.m, mask);
-        o.R = wave_xor(s.R, mask);
-        o.S = wave_xor(s.S, mask);
-        s = stat_merge(s, o);
-    }
-    return s;
+    s = stat_merge(s, dpp_stat<0xb1, 0xf>(s));   // quad_perm [1,0,3,2]
+    s = stat_merge(s, dpp_stat<0x4e, 0xf>(s));   // quad_perm [2,3,0,1]
+    s = stat_merge(s, dpp_stat<0x141, 0xf>(s));  // row_half_mirror
+    s = stat_merge(s, dpp_stat<0x140, 0xf>(s));  // row_mirror
+    s = stat_merge(s, dpp_stat<0x142, 0xa>(s));  // row_bcast:15
+    s = stat_merge(s, dpp_stat<0x143, 0xc>(s));  // row_bcast:31
+    Stat r;
+    r.m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s.m), 63));
+    r.R = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s.R), 63));
+    r.S = readlane_f64(s.S, 63);
+    return r;
+}
+
+// The sum of the wave's values; every lane gets it.
+__device__ inline double wave_sum(double v) {
+    v += dpp_f64<0xb1, 0xf, false>(v, 0.0);
+    v += dpp_f64<0x4e, 0xf, false>(v, 0.0);
+    v += dpp_f64<0x141, 0xf, false>(v, 0.0);
+    v += dpp_f64<0x140, 0xf, false>(v, 0.0);
+    v += dpp_f64<0x142, 0xa, false>(v, 0.0);
+    v += dpp_f64<0x143, 0xc, false>(v, 0.0);
+    return readlane_f64(v, 63);
 }
 
 // Workgroup-wide merge of one Stat per thread; every thread gets the result.
@@ -249,14 +298,16 @@ __device__ inline Stat block_reduce_stat(Stat st, Stat* lds_waves) {
     return r;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave (Hillis-Steele).
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele within
+// each row of 16 lanes (row_shr by 1, 2, 4, 8, zero past the row's start),
+// then the row broadcasts add the earlier rows' totals.
 __device__ inline double wave_inclusive_scan(double v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        double o = __shfl_up(v, d, 64);
-        if (lane >= d) v += o;
-    }
+    v += dpp_f64<0x111, 0xf, true>(v, 0.0);  // row_shr:1
+    v += dpp_f64<0x112, 0xf, true>(v, 0.0);  // row_shr:2
+    v += dpp_f64<0x114, 0xf, true>(v, 0.0);  // row_shr:4
+    v += dpp_f64<0x118, 0xf, true>(v, 0.0);  // row_shr:8
+    v += dpp_f64<0x142, 0xa, false>(v, 0.0); // row_bcast:15 into rows 1 and 3
+    v += dpp_f64<0x143, 0xc, false>(v, 0.0); // row_bcast:31 into rows 2 and 3
     return v;
 }
 
