@@ -546,8 +546,9 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
     // the quarter inside the crossing lane's run: lane j takes the run's
     // j-th quarter (runs of up to 64 quarters; longer runs are walked by
     // their own lane), one more wave scan finds the crossing
-    const int sq0 = __shfl(q0, src, 64), sq1 = __shfl(q1, src, 64);
-    const double sbase = __shfl(excl, src, 64);
+    // (src, jj and the like are wave-uniform: broadcasts are lane reads)
+    const int sq0 = __builtin_amdgcn_readlane(q0, src), sq1 = __builtin_amdgcn_readlane(q1, src);
+    const double sbase = readlane_f64(excl, src);
     int qstar;
     double base;
     if (sq1 - sq0 <= 64) {
@@ -560,7 +561,7 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
             x = 0.0;
 #pragma unroll
             for (int j = 0; j < kRun; ++j) {
-                const double v = __shfl(run_v[j], src, 64);
+                const double v = readlane_f64(run_v[j], src);
                 if (lane == j) x = v;
             }
         } else {
@@ -578,7 +579,7 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
             jj = pq ? 63 - __clzll(static_cast<long long>(pq)) : 0;
         }
         qstar = sq0 + jj;
-        base = sbase + __shfl(xe, jj, 64);
+        base = sbase + readlane_f64(xe, jj);
     } else {
         int qfound = q0;
         double b0 = excl;
@@ -604,8 +605,8 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
                 b0 = run_last;
             }
         }
-        qstar = __shfl(qfound, src, 64);
-        base = __shfl(b0, src, 64);
+        qstar = __builtin_amdgcn_readlane(qfound, src);
+        base = readlane_f64(b0, src);
     }
     // tokens of the chosen quarter, kPerVec per lane in token order
     const int e0 = qstar * kQuart + lane * E::kPerVec;
@@ -628,10 +629,10 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
     const unsigned long long fl = __ballot(found != INT32_MAX);
     int token;
     if (fl) {
-        token = __shfl(found, __ffsll(static_cast<long long>(fl)) - 1, 64);
+        token = __builtin_amdgcn_readlane(found, __ffsll(static_cast<long long>(fl)) - 1);
     } else {
         const unsigned long long pl = __ballot(lastpos >= 0);
-        token = pl ? __shfl(lastpos, 63 - __clzll(static_cast<long long>(pl)), 64)
+        token = pl ? __builtin_amdgcn_readlane(lastpos, 63 - __clzll(static_cast<long long>(pl)))
                    : min(qstar * kQuart, a.V - 1);
     }
     if (a.given) {
