@@ -28,7 +28,7 @@ def run_case(d, ncache, label):
     return g, o
 
 
-SHAPES = [(3, 1, 2), (5, 2, 7), (4, 31, 1000), (2, 3, 5003), (1, 16, 151937), (6, 4, 4096),
+SHAPES = [(2, 3, 1), (3, 1, 2), (5, 2, 7), (4, 31, 1000), (2, 3, 5003), (1, 16, 151937), (6, 4, 4096),
           (2, 100, 64)]
 
 

@@ -55,7 +55,7 @@ def run_case(d, label, want_dist=True):
     return g, o
 
 
-SHAPES = [(1, 1, 7), (3, 2, 100), (5, 17, 1000), (2, 64, 5003), (4, 33, 151937), (2, 1024, 300),
+SHAPES = [(1, 1, 7), (2, 5, 1), (3, 2, 100), (5, 17, 1000), (2, 64, 5003), (4, 33, 151937), (2, 1024, 300),
           (16, 8, 4096)]
 
 

@@ -87,6 +87,17 @@ def test_shapes(case, dtype):
     run_case(d, W, N, budget, f"tb-{case}-{dtype}")
 
 
+@pytest.mark.parametrize("V,W", [(1, 4), (3, 8), (5, 16)])
+def test_vocabulary_smaller_than_width(V, W):
+    """Fewer tokens than W: every row offers only its V tokens (a single one
+    when V = 1), so the tree is narrower than W everywhere."""
+    N, budget = 3, 50
+    M = synth.complete_tree_rows(W, N) if synth.complete_tree_rows(W, N) * W <= 2048 else 2048 // W
+    d = synth.treebuild_inputs(3, M, V, "bf16", T=1.0, logits=("normal", 1.0), seed=V + W)
+    g, o = run_case(d, W, N, budget, f"tb-V{V}-W{W}")
+    assert (g["n"] == o["n"]).all()
+
+
 def test_workload_full_size():
     d = synth.treebuild_config_inputs(seed=9001, R=4)
     run_case(d, d["W"], d["N"], d["budget"], "tb-workload-R4")
