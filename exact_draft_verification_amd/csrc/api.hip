@@ -17,6 +17,7 @@ constexpr int kThreadsHost = 256;
 constexpr int64_t kChainUnits = 4096;   // chain statistics workgroups to aim for
 constexpr int64_t kTreeUnits = 8192;    // tree argmax workgroups to aim for
 constexpr int64_t kOutcomeUnits = 1024; // outcome-scoring workgroups to aim for
+constexpr int64_t kChunkUnits = 1024;   // final-draw chunk workgroups to aim for
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -71,13 +72,16 @@ int32_t block_plan(int32_t B, int64_t rows, int32_t V, int32_t dtype, ChainPlan*
                   static_cast<int>(kMaxBlockParts / rows), &p->nseg, &p->seg_len);
     if (rows_total * p->nseg > INT32_MAX) return SV_ERR_SHAPE;
     // final draw: tiles of one 16-byte vector per thread, sums kept per
-    // quarter tile (64 vectors); a chunk workgroup takes 1 or 4 tiles: few
-    // tiles in all (a small batch) favour many short workgroups, many tiles
-    // favour fewer, longer ones that repeat the block's decision less
+    // quarter tile (64 vectors); a chunk workgroup takes the block's decision
+    // once and then streams a run of tiles, so a large batch gets a few long
+    // chunks per block (about kChunkUnits workgroups in all) and a small one
+    // many single-tile chunks
     const int64_t tile = static_cast<int64_t>(kThreadsHost) * epv;
-    const int64_t tiles_total = static_cast<int64_t>(B) * ceil_div(V, tile);
-    p->chunk_tiles = tiles_total <= 2048 ? 1 : 4;
-    p->nchunk = static_cast<int>(ceil_div(ceil_div(V, tile), p->chunk_tiles));
+    const int64_t ntile = ceil_div(V, tile);
+    int64_t nchunk = ceil_div(kChunkUnits, B);
+    if (nchunk > ntile) nchunk = ntile;
+    p->chunk_tiles = static_cast<int>(ceil_div(ntile, nchunk));
+    p->nchunk = static_cast<int>(ceil_div(ntile, p->chunk_tiles));
     p->nquart = static_cast<int>(ceil_div(V, 64 * static_cast<int64_t>(epv)));
     if (static_cast<int64_t>(B) * p->nchunk > INT32_MAX) return SV_ERR_SHAPE;
     const size_t nb = static_cast<size_t>(B), nr = static_cast<size_t>(rows_total);

@@ -381,9 +381,20 @@ __device__ inline float lane_weights_t(const float* zp, const float* zq, const D
 #pragma unroll
     for (int i = 0; i < E::kPerVec; ++i) {
         w[i] = draw_weight<E, RESID>(zp[i], zq[i], r);
-        // only a point-mass draw excludes a token; the residual never does
-        if constexpr (!RESID) w[i] = e + i == r.excl ? 0.0f : w[i];
         s += w[i];
+    }
+    if constexpr (!RESID) {
+        // only a point-mass draw excludes a token (the residual never does):
+        // the one lane that holds it zeroes its weight and sums again, in
+        // the same order
+        if (static_cast<unsigned>(r.excl - e) < static_cast<unsigned>(E::kPerVec)) {
+            s = 0.0f;
+#pragma unroll
+            for (int i = 0; i < E::kPerVec; ++i) {
+                w[i] = e + i == r.excl ? 0.0f : w[i];
+                s += w[i];
+            }
+        }
     }
     return s;
 }
@@ -432,42 +443,114 @@ __device__ inline ChainDecision load_decision(const ChainArgs& a, int b) {
     return d;
 }
 
-// Chunk workgroup: the block's decision, then TILES consecutive tiles of the
-// final row, every load issued before any weight is computed.
-template <class E, int TILES>
+// Raw 16-byte vectors of one group of G tiles of the final row(s), tiles
+// [t, t + G): this thread's vector of each tile.  Every load is issued
+// unconditionally (so the group's count of loads in flight is fixed): a tile
+// at or past t1 re-reads tile t1 - 1, and a vector not wholly inside the row
+// re-reads the row's last whole vector; group_sums discards both.  Needs
+// 16-byte aligned rows of at least one whole vector.
+template <class E, int G, bool RESID>
+__device__ inline void issue_group(const FinalRows<E>& rows, int t, int t1, int vlast, uint4* p,
+                                   uint4* q) {
+    constexpr int kTile = kThreads * E::kPerVec;
+#pragma unroll
+    for (int m = 0; m < G; ++m) {
+        const int e = min(min(t + m, t1 - 1) * kTile + static_cast<int>(threadIdx.x) * E::kPerVec, vlast);
+        p[m] = load16_stream(rows.p + e);
+        if constexpr (RESID) q[m] = load16_stream(rows.q + e);
+    }
+}
+
+// Quarter sums of the group of tiles [t, min(t + G, t1)) from its raw
+// vectors; a vector that straddles the row's end is read token by token,
+// one past it is all -inf (weight 0).
+template <class E, int G, bool RESID>
+__device__ inline void group_sums(const FinalRows<E>& rows, const DrawRow& r, int t, int t1, int V,
+                                  const uint4* p, const uint4* q, double* qs, int nquart) {
+    constexpr int kTile = kThreads * E::kPerVec;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int m = 0; m < G; ++m) {
+        const int j = t + m;
+        if (j >= t1) break;  // (uniform)
+        const int e = j * kTile + static_cast<int>(threadIdx.x) * E::kPerVec;
+        float zp[E::kPerVec], zq[E::kPerVec], w[E::kPerVec];
+        if (e + E::kPerVec <= V) {
+            E::unpack(p[m], zp);
+            if constexpr (RESID) {
+                E::unpack(q[m], zq);
+            } else {
+#pragma unroll
+                for (int i = 0; i < E::kPerVec; ++i) zq[i] = 0.0f;
+            }
+        } else {
+            load_tokens<E>(rows, RESID, e, V, zp, zq);
+        }
+        const double sw = wave_sum(static_cast<double>(lane_weights_t<E, RESID>(zp, zq, r, e, w)));
+        const int qi = j * kWaves + wave;
+        if (lane == 0 && qi < nquart) qs[qi] = sw;
+    }
+}
+
+// The chunk's tiles [t0, t1) in groups of G, software-pipelined: the next
+// group's loads are in flight while the current group's weights are formed.
+template <class E, int G, bool RESID>
+__device__ inline void stream_tiles(const FinalRows<E>& rows, const DrawRow& r, int t0, int t1,
+                                    int V, double* qs, int nquart) {
+    const int vlast = (V / E::kPerVec - 1) * E::kPerVec;  // the row's last whole vector
+    const int ngroup = (t1 - t0 + G - 1) / G;
+    uint4 cp[G], cq[G];
+    issue_group<E, G, RESID>(rows, t0, t1, vlast, cp, cq);
+    for (int gi = 0; gi + 1 < ngroup; ++gi) {
+        uint4 np[G], nq[G];
+        issue_group<E, G, RESID>(rows, t0 + (gi + 1) * G, t1, vlast, np, nq);
+        group_sums<E, G, RESID>(rows, r, t0 + gi * G, t1, V, cp, cq, qs, nquart);
+#pragma unroll
+        for (int m = 0; m < G; ++m) {
+            cp[m] = np[m];
+            if constexpr (RESID) cq[m] = nq[m];
+        }
+    }
+    group_sums<E, G, RESID>(rows, r, t0 + (ngroup - 1) * G, t1, V, cp, cq, qs, nquart);
+}
+
+// Chunk workgroup: the block's decision, then the chunk's tiles of the final
+// row, a run of chunk_tiles consecutive tiles streamed in groups of G.
+template <class E, int G>
 __global__ __launch_bounds__(kThreads) void chain_chunks_kernel(ChainArgs a) {
     extern __shared__ Stat s_part[];  // [2*gamma+1][nseg]
     constexpr int kTile = kThreads * E::kPerVec;
     const int b = blockIdx.x / a.nchunk;
     const int c = blockIdx.x % a.nchunk;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     ChainDecision d;
     if (a.given) {
         d = load_decision(a, b);
     } else {
         d = chain_decide<E>(a, b, s_part);
-        if (c == 0 && tid == 0) a.dec[b] = d;
+        if (c == 0 && threadIdx.x == 0) a.dec[b] = d;
     }
     if (d.k < 0) return;  // invalid block: the select kernel writes -1s
     const FinalRows<E> rows = final_rows<E>(a, b, d.k);
     const DrawRow r = draw_row(a, d);
     const int ntile = (a.V + kTile - 1) / kTile;
-    // a tile past the row's end reads as -inf (weight 0) without a load
-    float zp[TILES][E::kPerVec], zq[TILES][E::kPerVec];
-#pragma unroll
-    for (int m = 0; m < TILES; ++m) {
-        const int j = c * TILES + m;
-        load_tokens<E>(rows, r.resid, j * kTile + tid * E::kPerVec, a.V, zp[m], zq[m]);
-    }
+    const int t0 = c * a.chunk_tiles, t1 = min(ntile, t0 + a.chunk_tiles);
     double* qs = a.qsum + static_cast<int64_t>(b) * a.nquart;
-#pragma unroll
-    for (int m = 0; m < TILES; ++m) {
-        const int j = c * TILES + m;
-        float w[E::kPerVec];
-        const int e = j * kTile + tid * E::kPerVec;
-        const double sw = wave_sum(static_cast<double>(lane_weights<E>(zp[m], zq[m], r, e, w)));
+    if (rows.vec_ok && a.V >= E::kPerVec) {
+        if (r.resid)
+            stream_tiles<E, G, true>(rows, r, t0, t1, a.V, qs, a.nquart);
+        else
+            stream_tiles<E, G, false>(rows, r, t0, t1, a.V, qs, a.nquart);
+        return;
+    }
+    // rows not 16-byte aligned (or shorter than a vector): token by token
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int j = t0; j < t1; ++j) {
+        float zp[E::kPerVec], zq[E::kPerVec], w[E::kPerVec];
+        const int e = j * kTile + static_cast<int>(threadIdx.x) * E::kPerVec;
+        load_tokens<E>(rows, r.resid, e, a.V, zp, zq);
+        const double sw = wave_sum(static_cast<double>(lane_weights<E>(zp, zq, r, e, w)));
         const int qi = j * kWaves + wave;
-        if (lane == 0 && j < ntile && qi < a.nquart) qs[qi] = sw;
+        if (lane == 0 && qi < a.nquart) qs[qi] = sw;
     }
 }
 

@@ -272,14 +272,26 @@ __device__ inline Stat wave_reduce_stat(Stat s) {
     return r;
 }
 
-// The sum of the wave's values; every lane gets it.
+// A DPP move whose lanes outside ROWS are left undefined (no old value to
+// initialise), for reductions that read only lanes the pattern defines.
+template <int CTRL, int ROWS>
+__device__ inline double dpp_f64_any(double x) {
+    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(x), CTRL, ROWS, 0xf, false);
+    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(x), CTRL, ROWS, 0xf, false);
+    return __hiloint2double(hi, lo);
+}
+
+// The sum of the wave's values; every lane gets it.  Only lane 63's partial
+// is read: after the row steps every lane holds its row's sum, the two
+// broadcasts leave row 3 with rows 0-3 (rows 0-2 hold values nobody reads,
+// so the lanes the broadcasts skip need no defined old value).
 __device__ inline double wave_sum(double v) {
-    v += dpp_f64<0xb1, 0xf, false>(v, 0.0);
-    v += dpp_f64<0x4e, 0xf, false>(v, 0.0);
-    v += dpp_f64<0x141, 0xf, false>(v, 0.0);
-    v += dpp_f64<0x140, 0xf, false>(v, 0.0);
-    v += dpp_f64<0x142, 0xa, false>(v, 0.0);
-    v += dpp_f64<0x143, 0xc, false>(v, 0.0);
+    v += dpp_f64_any<0xb1, 0xf>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f64_any<0x4e, 0xf>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f64_any<0x141, 0xf>(v);  // row_half_mirror
+    v += dpp_f64_any<0x140, 0xf>(v);  // row_mirror
+    v += dpp_f64_any<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_f64_any<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
     return readlane_f64(v, 63);
 }
 

@@ -44,6 +44,21 @@ def test_shapes_and_ragged_tails(shape, dtype):
         run_case(d, f"shape{shape}-{dtype}-s{seed}")
 
 
+# Batches large enough that each final-draw workgroup streams a run of
+# several tiles (about 1024 chunk workgroups in all): runs of 2 to 17 tiles,
+# a ragged last tile, and vocabularies whose rows are not 16-byte aligned
+# (mixed aligned and unaligned rows in one launch).
+LONG_SHAPES = [(256, 2, 40000, "bf16"), (512, 1, 65541, "bf16"), (300, 2, 20000, "f32"),
+               (300, 2, 20003, "f32"), (200, 3, 30000, "bf16")]
+
+
+@pytest.mark.parametrize("shape", LONG_SHAPES, ids=[f"B{b}g{g}V{v}{t}" for b, g, v, t in LONG_SHAPES])
+def test_long_chunk_runs(shape):
+    B, g, V, dtype = shape
+    d = synth.chain_inputs(B, g, V, dtype, T=0.8, target=("normal", 2.0), noise=0.6, seed=4100 + g)
+    run_case(d, f"long{shape}")
+
+
 @pytest.mark.parametrize("cfg,seeds", [(1, range(40)), (2, range(6)), (3, range(2)), (5, range(1))])
 def test_configs_full_size(cfg, seeds):
     for s in seeds:

@@ -41,6 +41,19 @@ def test_shapes_and_ragged_tails(shape, dtype):
         run_case(d, f"pm-shape{shape}-{dtype}-s{seed}")
 
 
+# Large batches: each final-draw workgroup streams a run of several tiles
+# (runs of 2 to 17 tiles, ragged last tile, unaligned rows).
+LONG_SHAPES = [(256, 3, 40000, "bf16"), (512, 1, 65541, "bf16"), (300, 2, 20003, "f32")]
+
+
+@pytest.mark.parametrize("shape", LONG_SHAPES, ids=[f"B{b}g{g}V{v}{t}" for b, g, v, t in LONG_SHAPES])
+def test_long_chunk_runs(shape):
+    B, g, V, dtype = shape
+    d = synth.pointmass_inputs(B, g, V, dtype, T=0.8, target=("normal", 2.0), p_match=0.7,
+                               seed=4200 + g)
+    run_case(d, f"pm-long{shape}")
+
+
 @pytest.mark.parametrize("cfg", [3, 5])
 def test_config_shapes_full_size(cfg):
     d = synth.pointmass_config_inputs(cfg, seed=7000 + cfg)
