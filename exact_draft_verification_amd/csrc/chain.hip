@@ -582,6 +582,10 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
     const ChainDecision d = load_decision(a, b);
     const double u =
         static_cast<double>(a.uniforms[static_cast<int64_t>(b) * (g + 1) + (a.given ? 0 : g)]);
+    // the block's draft tokens for its output row, requested now (one per
+    // lane; a block of 64 or more positions loads them when writing)
+    const bool lane_out = !a.given && g < 64;
+    const int xtok = lane_out && lane < g ? a.tokens[static_cast<int64_t>(b) * g + lane] : -1;
     if (d.k < 0) {
         if (!a.given) write_outputs<E>(a, b, -1, -1);  // (a given decision wrote its own)
         return;
@@ -720,6 +724,12 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
     }
     if (a.given) {
         if (lane == 0) a.out_tokens[static_cast<int64_t>(b) * (g + 1) + d.pad] = token;
+    } else if (lane_out) {
+        // x_0 .. x_{k-1}, the drawn token, -1 padding: one entry per lane
+        if (lane <= g)
+            a.out_tokens[static_cast<int64_t>(b) * (g + 1) + lane] =
+                lane < d.k ? xtok : (lane == d.k ? token : -1);
+        if (lane == 0) a.accept_len[b] = d.k;
     } else {
         write_outputs<E>(a, b, d.k, token);
     }

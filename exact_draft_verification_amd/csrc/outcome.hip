@@ -38,18 +38,68 @@ namespace {
 constexpr double kDomain = 268435456.0;  // |m| / T limit (2^28)
 constexpr float kNegInf = -INFINITY;
 
+// 64-bit cross-lane moves.  dpp64: a DPP pattern (lanes whose source lies
+// outside the wave are left undefined).  xor_lanes<J>: the key of lane (lane ^ J);
+// within a row it is one or two DPP moves (x ^ 7 is the half-row mirror,
+// x ^ 15 the row mirror, x ^ 3 a quad permute), across rows a swizzle (16)
+// or a permute through LDS (32).
+template <int CTRL>
+__device__ inline uint64_t dpp64(uint64_t x) {
+    const uint32_t lo = __builtin_amdgcn_mov_dpp(static_cast<uint32_t>(x), CTRL, 0xf, 0xf, false);
+    const uint32_t hi = __builtin_amdgcn_mov_dpp(static_cast<uint32_t>(x >> 32), CTRL, 0xf, 0xf, false);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+template <int J>
+__device__ inline uint64_t xor_lanes(uint64_t x) {
+    if constexpr (J == 1) {
+        return dpp64<0xb1>(x);  // quad_perm [1,0,3,2]
+    } else if constexpr (J == 2) {
+        return dpp64<0x4e>(x);  // quad_perm [2,3,0,1]
+    } else if constexpr (J == 4) {
+        return dpp64<0x1b>(dpp64<0x141>(x));  // half-row mirror, then quad_perm [3,2,1,0]
+    } else if constexpr (J == 8) {
+        return dpp64<0x141>(dpp64<0x140>(x));  // row mirror, then half-row mirror
+    } else if constexpr (J == 16) {
+        const uint32_t lo = __builtin_amdgcn_ds_swizzle(static_cast<int>(static_cast<uint32_t>(x)), 0x401f);
+        const uint32_t hi = __builtin_amdgcn_ds_swizzle(static_cast<int>(static_cast<uint32_t>(x >> 32)), 0x401f);
+        return (static_cast<uint64_t>(hi) << 32) | lo;
+    } else {
+        return __shfl_xor(x, J, 64);
+    }
+}
+
+// One compare-exchange step of a bitonic sort (partner lane ^ J, stage K).
+template <int J, int K>
+__device__ inline uint64_t bitonic_step(uint64_t x, int lane) {
+    const uint64_t o = xor_lanes<J>(x);
+    const bool keep_max = ((lane & J) == 0) == ((lane & K) == 0);
+    return keep_max ? (o > x ? o : x) : (o < x ? o : x);
+}
+
 // Descending bitonic sort of one key per lane over the 64 lanes of a wave.
 __device__ inline uint64_t wave_sort_desc(uint64_t x) {
     const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const uint64_t o = __shfl_xor(x, j, 64);
-            const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
-            x = keep_max ? (o > x ? o : x) : (o < x ? o : x);
-        }
-    }
+    x = bitonic_step<1, 2>(x, lane);
+    x = bitonic_step<2, 4>(x, lane);
+    x = bitonic_step<1, 4>(x, lane);
+    x = bitonic_step<4, 8>(x, lane);
+    x = bitonic_step<2, 8>(x, lane);
+    x = bitonic_step<1, 8>(x, lane);
+    x = bitonic_step<8, 16>(x, lane);
+    x = bitonic_step<4, 16>(x, lane);
+    x = bitonic_step<2, 16>(x, lane);
+    x = bitonic_step<1, 16>(x, lane);
+    x = bitonic_step<16, 32>(x, lane);
+    x = bitonic_step<8, 32>(x, lane);
+    x = bitonic_step<4, 32>(x, lane);
+    x = bitonic_step<2, 32>(x, lane);
+    x = bitonic_step<1, 32>(x, lane);
+    x = bitonic_step<32, 64>(x, lane);
+    x = bitonic_step<16, 64>(x, lane);
+    x = bitonic_step<8, 64>(x, lane);
+    x = bitonic_step<4, 64>(x, lane);
+    x = bitonic_step<2, 64>(x, lane);
+    x = bitonic_step<1, 64>(x, lane);
     return x;
 }
 
@@ -88,7 +138,7 @@ struct TopVectorFolder {
     __device__ inline void insert(uint64_t ck) {
         const int lane = threadIdx.x & 63;
         const int pos = __popcll(__ballot(lst > ck));
-        const uint64_t up = __shfl_up(lst, 1u, 64);
+        const uint64_t up = dpp64<0x138>(lst);  // wave_shr:1 (lane 0's value is not used)
         lst = lane < pos ? lst : (lane == pos ? ck : up);
         publish();
     }

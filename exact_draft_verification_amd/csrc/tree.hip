@@ -108,31 +108,48 @@ __device__ inline void range_argmax(const typename E::storage* row, int e0, int 
 // Path resolution for request b (one workgroup).
 __device__ void tree_resolve(const TreeArgs& a, int b, ArgmaxPart* s_part) {
     __shared__ int s_par[kMaxTreeNodes];
+    __shared__ int s_tok[kMaxTreeNodes];
     __shared__ int s_anc[kMaxTreeNodes];
     __shared__ int s_dep[kMaxTreeNodes];
     __shared__ int s_amax[kMaxTreeNodes];
     __shared__ unsigned char s_ok[kMaxTreeNodes];
     __shared__ int s_bad, s_key;
     constexpr int kStage = kMaxBlockParts / kThreads;
+    constexpr int kNodes = kMaxTreeNodes / kThreads;
     const int n = a.n, tid = threadIdx.x;
     const int32_t* par = a.parents + static_cast<int64_t>(b) * n;
     const int32_t* tok = a.tokens + static_cast<int64_t>(b) * n;
     int32_t* out = a.out_tokens + static_cast<int64_t>(b) * n;
     {
-        // stage the request's n*nseg row partials: every load issued before
-        // any LDS store (indices past the end re-read the last partial and
-        // are not stored)
+        // stage the request's n*nseg row partials and every node's parent
+        // and token: all loads issued before any LDS store (partial indices
+        // past the end re-read the last partial and are not stored)
         static_assert(sizeof(ArgmaxPart) == 16, "ArgmaxPart is staged as one 16-byte vector");
         const int np = n * a.nseg;
         const uint4* src = reinterpret_cast<const uint4*>(a.part + static_cast<int64_t>(b) * np);
         uint4* dst = reinterpret_cast<uint4*>(s_part);
         uint4 t[kStage];
+        int pv[kNodes], tv[kNodes];
 #pragma unroll
         for (int m = 0; m < kStage; ++m)
             t[m] = m * kThreads < np ? src[min(tid + m * kThreads, np - 1)] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
+        for (int q = 0; q < kNodes; ++q) {
+            const int j = tid + q * kThreads;
+            pv[q] = j < n ? par[j] : 0;
+            tv[q] = j < n ? tok[j] : 0;
+        }
+#pragma unroll
         for (int m = 0; m < kStage; ++m)
             if (tid + m * kThreads < np) dst[tid + m * kThreads] = t[m];
+#pragma unroll
+        for (int q = 0; q < kNodes; ++q) {
+            const int j = tid + q * kThreads;
+            if (j < n) {
+                s_par[j] = pv[q];
+                s_tok[j] = tv[q];
+            }
+        }
     }
     if (tid == 0) {
         s_bad = 0;
@@ -150,13 +167,12 @@ __device__ void tree_resolve(const TreeArgs& a, int b, ArgmaxPart* s_part) {
         // a valid row has no NaN, no +inf and at least one finite logit
         if (bad || !(best.v > -INFINITY) || best.v == INFINITY) s_bad = 1;
         s_amax[j] = best.idx;
-        const int pj = par[j];
+        const int pj = s_par[j];
         if (j == 0) {
             if (pj != -1) s_bad = 1;
-        } else if (pj < 0 || pj >= j || tok[j] < 0 || tok[j] >= a.V) {
+        } else if (pj < 0 || pj >= j || s_tok[j] < 0 || s_tok[j] >= a.V) {
             s_bad = 1;
         }
-        s_par[j] = pj;
     }
     __syncthreads();
     if (s_bad) {
@@ -178,7 +194,7 @@ __device__ void tree_resolve(const TreeArgs& a, int b, ArgmaxPart* s_part) {
         } else {
             s_anc[j] = s_par[j];
             s_dep[j] = 1;
-            s_ok[j] = tok[j] == s_amax[s_par[j]];
+            s_ok[j] = s_tok[j] == s_amax[s_par[j]];
         }
     }
     __syncthreads();
@@ -190,7 +206,7 @@ __device__ void tree_resolve(const TreeArgs& a, int b, ArgmaxPart* s_part) {
     if (tid == 0) {
         int v = vstar;
         for (int d = depth; d >= 1; --d) {
-            out[d - 1] = tok[v];
+            out[d - 1] = s_tok[v];
             v = s_par[v];
         }
         out[depth] = s_amax[vstar];

@@ -33,34 +33,42 @@ namespace {
 constexpr double kDomain = 268435456.0;  // |m| / T limit (2^28)
 constexpr double kLn2 = 0.69314718055994530942;
 
-// Wave-wide best of (score desc, node asc), carrying the node's packed row
-// and depth along (same lane moves as wave_best).
-template <int CTRL, int ROWS>
-__device__ inline void dpp_best_step(double& s, int& i, int& rd) {
-    const int lo = __double2loint(s), hi = __double2hiint(s);
-    const int olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xf, false);
-    const int ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xf, false);
-    const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROWS, 0xf, false);
-    const int ord = __builtin_amdgcn_update_dpp(rd, rd, CTRL, ROWS, 0xf, false);
-    const double os = __hiloint2double(ohi, olo);
-    // scores here are finite: plain (score desc, node asc), taken by selects
-    const bool take = (os > s) | ((os == s) & (oi < i));  // no short circuit: no branches
-    s = take ? os : s;
-    i = take ? oi : i;
-    rd = take ? ord : rd;
+// Order-preserving image of a score (finite or -inf) as an unsigned key:
+// a larger score gives a larger key, and -0 counts as +0.
+__device__ inline uint64_t score_key(double s) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(s + 0.0));
+    return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
+
+template <int CTRL, int ROWS>
+__device__ inline void dpp_min_step(int& x) {
+    x = min(x, __builtin_amdgcn_update_dpp(x, x, CTRL, ROWS, 0xf, false));
+}
+
+// Wave-wide best of (score desc, node asc) over the lanes' (s, i), carrying
+// the node's packed row and depth along; every lane gets the winner.  The
+// maximum is taken over the scores' integer keys; equal best scores on
+// several lanes (rare) are settled by a minimum over their nodes.
 __device__ inline void wave_best_rd(double& s, int& i, int& rd) {
-    dpp_best_step<0xb1, 0xf>(s, i, rd);
-    dpp_best_step<0x4e, 0xf>(s, i, rd);
-    dpp_best_step<0x141, 0xf>(s, i, rd);
-    dpp_best_step<0x140, 0xf>(s, i, rd);
-    dpp_best_step<0x142, 0xa>(s, i, rd);
-    dpp_best_step<0x143, 0xc>(s, i, rd);
-    const int lo = __builtin_amdgcn_readlane(__double2loint(s), 63);
-    const int hi = __builtin_amdgcn_readlane(__double2hiint(s), 63);
-    i = __builtin_amdgcn_readlane(i, 63);
-    rd = __builtin_amdgcn_readlane(rd, 63);
-    s = __hiloint2double(hi, lo);
+    const uint64_t k = score_key(s);
+    const uint64_t km = wave_max_u64(k);
+    const bool at_max = k == km;
+    const uint64_t tied = __ballot(at_max);
+    int src = __builtin_ctzll(tied);
+    if (__popcll(tied) > 1) {
+        int c = at_max ? i : INT32_MAX;
+        dpp_min_step<0xb1, 0xf>(c);
+        dpp_min_step<0x4e, 0xf>(c);
+        dpp_min_step<0x141, 0xf>(c);
+        dpp_min_step<0x140, 0xf>(c);
+        dpp_min_step<0x142, 0xa>(c);
+        dpp_min_step<0x143, 0xc>(c);
+        const int cm = __builtin_amdgcn_readlane(c, 63);
+        src = __builtin_ctzll(__ballot(at_max & (i == cm)));
+    }
+    s = readlane_f64(s, src);
+    i = __builtin_amdgcn_readlane(i, src);
+    rd = __builtin_amdgcn_readlane(rd, src);
 }
 
 // A node's row (>= 0) and depth in one int (rows < 2^20, depths < 2^10).

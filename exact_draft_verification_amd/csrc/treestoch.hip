@@ -31,17 +31,23 @@ __global__ __launch_bounds__(kThreads) void tree_stoch_decide_kernel(TreeStochAr
     __shared__ double s_L[2 * kMaxTreeNodes];
     __shared__ float s_Rp[kMaxTreeNodes];
     __shared__ int s_par[kMaxTreeNodes];
+    __shared__ int s_tok[kMaxTreeNodes];
     __shared__ int s_bad, s_key;
     constexpr int kStage = kMaxBlockParts / kThreads;
+    constexpr int kNodes = kMaxTreeNodes / kThreads;
     const ChainArgs& a = t.ch;
     const int b = blockIdx.x, tid = threadIdx.x, n = t.n, rows = 2 * n;
     const int32_t* par = t.parents + static_cast<int64_t>(b) * n;
     const int32_t* tok = t.node_tokens + static_cast<int64_t>(b) * n;
     const float* uu = a.uniforms + static_cast<int64_t>(b) * n;
     int32_t* out = a.out_tokens + static_cast<int64_t>(b) * n;
+    // node j = tid + q*kThreads: parent, token and uniform, in registers
+    int pv[kNodes], tv[kNodes];
+    float uv[kNodes];
     {
-        // stage the request's 2n*nseg row partials: every load issued before
-        // any LDS store (indices past the end re-read the last one, unstored)
+        // stage the request's 2n*nseg row partials, and load every node's
+        // inputs: all loads issued before any LDS store (partial indices past
+        // the end re-read the last one, unstored)
         const int np = rows * a.nseg;
         const uint4* src = reinterpret_cast<const uint4*>(a.part + static_cast<int64_t>(b) * np);
         uint4* dst = reinterpret_cast<uint4*>(s_dyn);
@@ -50,8 +56,23 @@ __global__ __launch_bounds__(kThreads) void tree_stoch_decide_kernel(TreeStochAr
         for (int m = 0; m < kStage; ++m)
             v[m] = m * kThreads < np ? src[min(tid + m * kThreads, np - 1)] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
+        for (int q = 0; q < kNodes; ++q) {
+            const int j = tid + q * kThreads;
+            pv[q] = j < n ? par[j] : 0;
+            tv[q] = j < n ? tok[j] : 0;
+            uv[q] = j < n ? uu[j] : 0.0f;
+        }
+#pragma unroll
         for (int m = 0; m < kStage; ++m)
             if (tid + m * kThreads < np) dst[tid + m * kThreads] = v[m];
+#pragma unroll
+        for (int q = 0; q < kNodes; ++q) {
+            const int j = tid + q * kThreads;
+            if (j < n) {
+                s_par[j] = pv[q];
+                s_tok[j] = tv[q];
+            }
+        }
     }
     if (tid == 0) {
         s_bad = 0;
@@ -69,14 +90,15 @@ __global__ __launch_bounds__(kThreads) void tree_stoch_decide_kernel(TreeStochAr
         s_L[r] = static_cast<double>(st.R) + log2(st.S);
         if (r < n) s_Rp[r] = st.R;
     }
-    for (int j = tid; j < n; j += kThreads) {
-        const int pj = par[j];
+#pragma unroll
+    for (int q = 0; q < kNodes; ++q) {
+        const int j = tid + q * kThreads, pj = pv[q];
+        if (j >= n) break;
         if (j == 0) {
             if (pj != -1) atomicOr(&s_bad, 1);
-        } else if (pj < 0 || pj >= j || tok[j] < 0 || tok[j] >= a.V) {
+        } else if (pj < 0 || pj >= j || tv[q] < 0 || tv[q] >= a.V) {
             atomicOr(&s_bad, 1);
         }
-        s_par[j] = pj;
     }
     __syncthreads();  // (the partials are dead from here: their LDS is reused)
     if (s_bad) {
@@ -92,39 +114,51 @@ __global__ __launch_bounds__(kThreads) void tree_stoch_decide_kernel(TreeStochAr
     int* s_dep = s_anc + kMaxTreeNodes;
     unsigned char* s_ok = reinterpret_cast<unsigned char*>(s_dep + kMaxTreeNodes);
     using S16 = uint16_t;
-    for (int j = tid; j < n; j += kThreads) {
+    // the token logits after each node's parent path, target and draft: all
+    // gathers issued before any is used
+    float zp[kNodes], zq[kNodes];
+#pragma unroll
+    for (int q = 0; q < kNodes; ++q) {
+        const int j = tid + q * kThreads;
+        zp[q] = 0.0f;
+        zq[q] = 0.0f;
+        if (j >= 1 && j < n) {
+            const int64_t off = (static_cast<int64_t>(b) * n + pv[q]) * a.V + tv[q];
+            if (t.dtype == 0) {
+                zp[q] = static_cast<const float*>(a.target)[off];
+                zq[q] = static_cast<const float*>(a.draft)[off];
+            } else {
+                zp[q] = __uint_as_float(static_cast<uint32_t>(static_cast<const S16*>(a.target)[off]) << 16);
+                zq[q] = __uint_as_float(static_cast<uint32_t>(static_cast<const S16*>(a.draft)[off]) << 16);
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < kNodes; ++q) {
+        const int j = tid + q * kThreads;
+        if (j >= n) break;
         if (j == 0) {
             s_anc[0] = 0;
             s_dep[0] = 0;
             s_ok[0] = 1;
             continue;
         }
-        const int p = s_par[j], y = tok[j];
-        // the token's logits after the parent's path, target and draft
-        const int64_t off = (static_cast<int64_t>(b) * n + p) * a.V + y;
-        float zp, zq;
-        if (t.dtype == 0) {
-            zp = static_cast<const float*>(a.target)[off];
-            zq = static_cast<const float*>(a.draft)[off];
-        } else {
-            zp = __uint_as_float(static_cast<uint32_t>(static_cast<const S16*>(a.target)[off]) << 16);
-            zq = __uint_as_float(static_cast<uint32_t>(static_cast<const S16*>(a.draft)[off]) << 16);
-        }
+        const int p = pv[q];
         // alpha = min(1, p/q) in the log2 domain, both rows' normalisers in
         // fp64; p = 0 rejects, q = 0 < p accepts
         double alpha;
-        if (zp == -INFINITY) {
+        if (zp[q] == -INFINITY) {
             alpha = 0.0;
-        } else if (zq == -INFINITY) {
+        } else if (zq[q] == -INFINITY) {
             alpha = 1.0;
         } else {
-            const double d = (static_cast<double>(zp) * a.c_d - s_L[p]) -
-                             (static_cast<double>(zq) * a.c_d - s_L[n + p]);
+            const double d = (static_cast<double>(zp[q]) * a.c_d - s_L[p]) -
+                             (static_cast<double>(zq[q]) * a.c_d - s_L[n + p]);
             alpha = d >= 0.0 ? 1.0 : exp2(d);
         }
         s_anc[j] = p;
         s_dep[j] = 1;
-        s_ok[j] = static_cast<double>(uu[j]) < alpha;
+        s_ok[j] = static_cast<double>(uv[q]) < alpha;
     }
     __syncthreads();
     deepest_accepted(n, s_anc, s_dep, s_ok, &s_key);
@@ -135,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void tree_stoch_decide_kernel(TreeStochAr
     if (tid == 0) {
         int v = vstar;
         for (int d = depth; d >= 1; --d) {
-            out[d - 1] = tok[v];
+            out[d - 1] = s_tok[v];
             v = s_par[v];
         }
         a.accept_len[b] = depth;
