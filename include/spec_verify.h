@@ -2,7 +2,8 @@
  * spec_verify.h -- C ABI of the MI355X (gfx950) speculative-verification
  * library libspecverify.so.
  *
- * Two operations, both over the vocabulary, both stated on the pages:
+ * The operations, all over the vocabulary and all stated on the pages (each
+ * declaration below cites its passages):
  *
  *  spec_verify_chain: speculative sampling of one drafted block per batch
  *    entry.  For draft position i the target distribution p_i and the draft
@@ -19,12 +20,26 @@
  *    from the target's bonus row p_gamma (section "A fully accepted block
  *    yields more than one committed token"; "JetSpec++", Appendix F.1).
  *
+ *  spec_verify_chain_pointmass: the same with a draft that proposes each
+ *    token with certainty (no draft logits read).
+ *
  *  spec_verify_tree_greedy: greedy (T = 0) verification of a draft tree given
  *    as a parent array: a node is accepted iff its parent is accepted and its
  *    token equals the target argmax after the parent's path; the deepest
  *    accepted node is kept and the target argmax after it is emitted as the
  *    extra token ("JetSpec reading notes", section "Tree verification",
  *    Fig. 5 and the greedy note; Algorithm 1 for the parent array).
+ *
+ *  spec_verify_tree_stochastic: one Bernoulli test per tree node against its
+ *    parent's target and draft rows, the deepest branch accepted throughout,
+ *    and the correction drawn from the target after it.
+ *
+ *  spec_outcome_topk and spec_cache_lookup: the most probable verification
+ *    outcomes of a block (a speculation cache) and the lookup of the outcome
+ *    that verification produced.
+ *
+ *  spec_tree_build: draft-tree construction by best-first search over the
+ *    draft's per-node logits.
  *
  * Every random draw is an explicit input: the caller passes one uniform per
  * test and one for the final draw, so results are a pure function of the
