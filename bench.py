@@ -365,7 +365,18 @@ def measure(w, steps, warmup, torch, hip):
         for x, y in zip(a, b):
             if not torch.equal(x, y):
                 raise RuntimeError("timed replay disagrees with eager results")
+    # the same K steps replayed and timed 5 more times: the spread of the
+    # measurement (reported beside the one bracketed run above)
+    reps = []
+    for _ in range(5):
+        torch.cuda.synchronize()
+        start.record()
+        g.replay()
+        end.record()
+        torch.cuda.synchronize()
+        reps.append(start.elapsed_time(end) * 1e3 / steps)
     del g
+    reps.sort()
 
     # dominant-kernel duration from events recorded around it by the library
     n_ev = min(steps, 400)
@@ -381,7 +392,9 @@ def measure(w, steps, warmup, torch, hip):
     k1_ms = sum(k1) / len(k1)
     res = dict(ms_per_step=ms / steps, gbps=w.bytes * steps / (ms * 1e-3) / 1e9,
                rounds_per_s=steps / (ms * 1e-3), dominant_ms=k1_ms,
-               dominant_gbps=w.bytes / (k1_ms * 1e-3) / 1e9)
+               dominant_gbps=w.bytes / (k1_ms * 1e-3) / 1e9,
+               repeats=dict(n=len(reps), median_us_per_step=round(reps[len(reps) // 2], 3),
+                            min_us_per_step=round(reps[0], 3), max_us_per_step=round(reps[-1], 3)))
     if k2 is not None:
         res["final_kernel_ms"] = sum(k2) / len(k2)
     return res
@@ -524,6 +537,7 @@ def main():
                    "bytes_per_step": w.bytes, "input_sets": w.nsets, "timing": "hip graph replay"},
         "pct_peak": round(100.0 * r["gbps"] / PEAK_GBPS, 2),
         "rounds_per_s": round(r["rounds_per_s"], 1),
+        "repeats": r["repeats"],
         "roofline": {"bound": "hbm", "kernel": kernel,
                      "achieved": round(r["dominant_gbps"], 2), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(r["dominant_gbps"] / PEAK_GBPS, 4),
@@ -549,7 +563,8 @@ def main():
                     "rounds_per_s": round(rc["rounds_per_s"], 1),
                     "us_per_step": round(rc["ms_per_step"] * 1e3, 3),
                     "dominant_kernel_us": round(rc["dominant_ms"] * 1e3, 3),
-                    "dominant_kernel_gbps": round(rc["dominant_gbps"], 2)}
+                    "dominant_kernel_gbps": round(rc["dominant_gbps"], 2),
+                    "repeats": rc["repeats"]}
                 del wc
                 torch.cuda.empty_cache()
             except Exception as e:  # keep the headline line even if one extra workload fails
