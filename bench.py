@@ -447,7 +447,21 @@ def cpu_baseline(w, budget_s):
                   f"on one thread in {dt:.1f}s (fp64 oracle), scaled to bytes per second")
     return {"value": round(w.bytes * frac * rounds / dt / 1e9, 4), "unit": "GB/s",
             "cores": min(threads, n), "kind": "oracle",
-            "rounds_per_s": round(rounds / dt, 3), "sample": sample}
+            "rounds_per_s": round(rounds / dt, 3), "sample": sample, "host": host_cpu()}
+
+
+def host_cpu():
+    """The host's logical CPU count and model name (as /proc/cpuinfo gives it)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"logical_cpus": os.cpu_count(), "model": model}
 
 
 def copy_calibration(nbytes, reps, torch):
