@@ -47,6 +47,20 @@ def test_outcome_workload_full_size():
     run_case(d, 8, "oc-workload-R4")
 
 
+def test_outcome_workload_bench_launch_sampled():
+    """The whole workload as bench.py times it (all 32 requests, so the same
+    segments and grid), checked against the oracle on a sample of requests."""
+    d = synth.outcome_config_inputs(seed=8002)
+    pick = [0, 13, 31]
+    print(f"[case] oc-bench-launch R={d['target'].shape[0]} sample {pick}", flush=True)
+    g = gpu_outcome(d, d["ncache"])
+    o = oracle.outcome_topk(d["target"][pick], d["draft_tokens"][pick], d["T"], d["ncache"],
+                            dtype=d["dtype"], want_all=True)
+    swaps = compare_outcomes({k: v[pick] for k, v in g.items()}, o["all_scores"], o,
+                             "oc-bench-launch")
+    print(f"[case] oc-bench-launch: near-tie swaps {swaps}", flush=True)
+
+
 def test_peaked_and_tied_rows():
     """bf16 logits with many equal values at the top of each row exercise the
     lowest-token-first order among equal probabilities."""

@@ -38,6 +38,13 @@ def run_case(d, label, want_dist=True):
     g = gpu_stree(d, want_dist=want_dist)
     o = oracle.tree_stochastic(d["target"], d["draft"], d["parents"], d["tokens"], d["uniforms"],
                                d["T"], dtype=d["dtype"], want_dist=want_dist)
+    compare_stree(g, o, label, want_dist)
+    return g, o
+
+
+def compare_stree(g, o, label, want_dist):
+    """Exact outputs outside the boundary band, -1 for invalid requests,
+    final_dist to 1e-5 where the draw's row is the same."""
     bad = o["accept_len"] < 0  # invalid requests: -1 everywhere on both sides
     assert (g["accept_len"][bad] == -1).all() and (g["accept_node"][bad] == -1).all()
     assert (g["out_tokens"][bad] == -1).all()
@@ -52,7 +59,6 @@ def run_case(d, label, want_dist=True):
         assert (g["final_dist"][bad] == 0).all()
     print(f"[case] {label}: compared {int(keep.sum())}, in band {int((~keep & ~bad).sum())}, "
           f"invalid {int(bad.sum())}", flush=True)
-    return g, o
 
 
 SHAPES = [(1, 1, 7), (2, 5, 1), (3, 2, 100), (5, 17, 1000), (2, 64, 5003), (4, 33, 151937), (2, 1024, 300),
@@ -76,6 +82,20 @@ def test_temperatures(T):
 def test_workload_full_size_sample():
     d = synth.stree_config_inputs(seed=9100, B=4)
     run_case(d, "st-workload-B4")
+
+
+def test_workload_bench_launch_sampled():
+    """The whole workload as bench.py times it (64 requests: the same chunk
+    runs and grids, no final_dist), checked against the oracle on a sample of
+    requests."""
+    d = synth.stree_config_inputs(seed=9101)
+    pick = [0, 21, 63]
+    print(f"[case] st-bench-launch B={d['target'].shape[0]} sample {pick}", flush=True)
+    g = gpu_stree(d, want_dist=False)
+    o = oracle.tree_stochastic(d["target"][pick], d["draft"][pick], d["parents"][pick],
+                               d["tokens"][pick], d["uniforms"][pick], d["T"], dtype=d["dtype"])
+    compare_stree({k: (None if v is None else v[pick]) for k, v in g.items()}, o,
+                  "st-bench-launch", want_dist=False)
 
 
 def test_one_hot_targets_equal_greedy_verification():

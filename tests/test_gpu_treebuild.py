@@ -48,6 +48,13 @@ def run_case(d, W, N, budget, label, child_row=None, max_near=None):
           flush=True)
     g = gpu_tree_build(d, W, N, budget, child_row)
     o = oracle.tree_build(d["logits"], d["T"], W, N, budget, child_row=child_row, dtype=d["dtype"])
+    return g, compare_trees(g, o, budget, N, label, max_near)
+
+
+def compare_trees(g, o, budget, N, label, max_near=None):
+    """Request by request: exact parents, tokens, rows and n (scores to 1e-4)
+    unless the oracle's expansion order has a near-tie (min_gap < GAP)."""
+    R = o["n"].shape[0]
     near = 0
     for r in range(R):
         if o["n"][r] < 0:
@@ -67,7 +74,7 @@ def run_case(d, W, N, budget, label, child_row=None, max_near=None):
     if max_near is None:
         max_near = max(1, R // 4)
     assert near <= max_near, f"{label}: too many near-ties ({near})"
-    return g, o
+    return o
 
 
 CASES = [  # R, W, N, V, budget
@@ -101,6 +108,17 @@ def test_vocabulary_smaller_than_width(V, W):
 def test_workload_full_size():
     d = synth.treebuild_config_inputs(seed=9001, R=4)
     run_case(d, d["W"], d["N"], d["budget"], "tb-workload-R4")
+
+
+def test_workload_bench_launch_sampled():
+    """The whole workload as bench.py times it (all 32 requests: the same
+    segments and grid), checked against the oracle on a sample of requests."""
+    d = synth.treebuild_config_inputs(seed=9002)
+    pick = [0, 17, 31]
+    print(f"[case] tb-bench-launch R={d['logits'].shape[0]} sample {pick}", flush=True)
+    g = gpu_tree_build(d, d["W"], d["N"], d["budget"])
+    o = oracle.tree_build(d["logits"][pick], d["T"], d["W"], d["N"], d["budget"], dtype=d["dtype"])
+    compare_trees({k: v[pick] for k, v in g.items()}, o, d["budget"], d["N"], "tb-bench-launch")
 
 
 def test_explicit_and_sparse_child_maps():
