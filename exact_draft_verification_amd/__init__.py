@@ -30,6 +30,7 @@ __all__ = [
 
 SV_DTYPE_F32 = 0
 SV_DTYPE_BF16 = 1
+SV_MAX_VOCAB = 1 << 29  # largest vocabulary size V any entry point accepts
 
 _HERE = _os.path.dirname(_os.path.abspath(__file__))
 _LIB_PATH = _os.path.join(_HERE, "libspecverify.so")

@@ -98,14 +98,14 @@ int32_t block_plan(int32_t B, int64_t rows, int32_t V, int32_t dtype, ChainPlan*
 int32_t chain_plan(int32_t B, int32_t gamma, int32_t V, int32_t dtype, bool pointmass,
                    ChainPlan* p) {
     if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
-    if (B < 1 || gamma < 1 || V < 1 || gamma > kMaxGamma) return SV_ERR_SHAPE;
+    if (B < 1 || gamma < 1 || V < 1 || V > kMaxVocab || gamma > kMaxGamma) return SV_ERR_SHAPE;
     return block_plan(B, (pointmass ? 1 : 2) * static_cast<int64_t>(gamma) + 1, V, dtype, p);
 }
 
 // Stochastic tree verification: n target rows and n draft rows per request.
 int32_t tree_stoch_plan(int32_t B, int32_t n, int32_t V, int32_t dtype, ChainPlan* p) {
     if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
-    if (B < 1 || n < 1 || V < 1 || n > kMaxTreeNodes) return SV_ERR_SHAPE;
+    if (B < 1 || n < 1 || V < 1 || V > kMaxVocab || n > kMaxTreeNodes) return SV_ERR_SHAPE;
     return block_plan(B, 2 * static_cast<int64_t>(n), V, dtype, p);
 }
 
@@ -116,7 +116,7 @@ struct TreePlan {
 
 int32_t tree_plan(int32_t B, int32_t n, int32_t V, int32_t dtype, TreePlan* p) {
     if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
-    if (B < 1 || n < 1 || V < 1 || n > kMaxTreeNodes) return SV_ERR_SHAPE;
+    if (B < 1 || n < 1 || V < 1 || V > kMaxVocab || n > kMaxTreeNodes) return SV_ERR_SHAPE;
     const int E = elem_bytes(dtype), epv = 16 / E;
     const int64_t rows_total = static_cast<int64_t>(B) * n;
     if (static_cast<double>(rows_total) * V * E > 9.0e18) return SV_ERR_SHAPE;
@@ -138,7 +138,8 @@ struct OutcomePlan {
 int32_t outcome_plan(int32_t R, int32_t gamma, int32_t V, int32_t dtype, int32_t ncache,
                      OutcomePlan* p) {
     if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
-    if (R < 1 || gamma < 1 || V < 1 || gamma > kMaxGamma || ncache < 1 || ncache > kMaxCache)
+    if (R < 1 || gamma < 1 || V < 1 || V > kMaxVocab || gamma > kMaxGamma || ncache < 1 ||
+        ncache > kMaxCache)
         return SV_ERR_SHAPE;
     const int E = elem_bytes(dtype), epv = 16 / E;
     const int64_t rows = static_cast<int64_t>(gamma) + 1;
@@ -171,8 +172,9 @@ struct TreeBuildPlan {
 int32_t tree_build_plan(int32_t R, int32_t M, int32_t V, int32_t dtype, int32_t W,
                         int32_t max_depth, int32_t budget, TreeBuildPlan* p) {
     if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
-    if (R < 1 || M < 1 || V < 1 || W < 1 || W > kMaxTreeWidth || max_depth < 1 || budget < 1 ||
-        budget > kMaxTreeNodes || static_cast<int64_t>(M) * W > kMaxTreeSlots)
+    if (R < 1 || M < 1 || V < 1 || V > kMaxVocab || W < 1 || W > kMaxTreeWidth ||
+        max_depth < 1 || budget < 1 || budget > kMaxTreeNodes ||
+        static_cast<int64_t>(M) * W > kMaxTreeSlots)
         return SV_ERR_SHAPE;
     const int E = elem_bytes(dtype), epv = 16 / E;
     const int64_t rows_total = static_cast<int64_t>(R) * M;

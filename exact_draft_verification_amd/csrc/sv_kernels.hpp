@@ -16,6 +16,8 @@ namespace sv {
 
 constexpr int kMaxGamma = 255;        // draft positions per chain block
 constexpr int kMaxTreeNodes = 1024;   // nodes per tree, root included
+constexpr int kMaxVocab = 1 << 29;    // vocabulary size V (element indices, and sums of
+                                       // them with a tile or segment, stay far inside int32)
 constexpr int kMaxBlockParts = 2048;  // row partials of one block / request (staged in LDS)
 
 // Row statistics of a temperature softmax (see stat_fold in sv_device.hpp):

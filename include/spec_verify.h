@@ -98,6 +98,7 @@ extern "C" {
 /* Limits checked on the host. */
 #define SV_MAX_GAMMA 255   /* draft positions per chain block                     */
 #define SV_MAX_TREE_NODES 1024 /* nodes per tree, root included                   */
+#define SV_MAX_VOCAB 536870912 /* vocabulary size V (2^29), every entry point     */
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *spec_verify_status_string(int32_t status);

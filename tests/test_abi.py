@@ -52,6 +52,7 @@ def test_binding_constants_match_header():
 
     c = header_constants()
     assert sv.SV_DTYPE_F32 == c["SV_DTYPE_F32"] and sv.SV_DTYPE_BF16 == c["SV_DTYPE_BF16"]
+    assert sv.SV_MAX_VOCAB == c["SV_MAX_VOCAB"]
 
 
 def test_status_strings(lib):
@@ -79,6 +80,16 @@ def test_workspace_sizes(lib):
         assert sv.spec_verify_tree_greedy_workspace_bytes(*bad) == 0, bad
     # larger problems never need less workspace
     assert sv.spec_verify_chain_workspace_bytes(256, 16, 151936, 1) >= c3
+    # the vocabulary limit, on every entry point
+    vmax = sv.SV_MAX_VOCAB
+    assert sv.spec_verify_chain_workspace_bytes(1, 1, vmax, 1) > 0
+    assert sv.spec_verify_chain_workspace_bytes(1, 1, vmax + 1, 1) == 0
+    assert sv.spec_verify_chain_pointmass_workspace_bytes(1, 1, vmax + 1, 1) == 0
+    assert sv.spec_verify_tree_greedy_workspace_bytes(1, 2, vmax + 1, 1) == 0
+    assert sv.spec_verify_tree_stochastic_workspace_bytes(1, 2, vmax + 1, 1) == 0
+    assert sv.spec_outcome_topk_workspace_bytes(1, 1, vmax + 1, 1, 4) == 0
+    assert sv.spec_tree_build_workspace_bytes(1, 5, vmax + 1, 1, 4, 2, 5) == 0
+    assert sv.spec_tree_build_workspace_bytes(1, 5, vmax, 1, 4, 2, 5) > 0
 
 
 class HostBufs:
