@@ -468,25 +468,29 @@ __global__ __launch_bounds__(kThreads) void outcome_select_kernel(OutcomeArgs a)
         }
     };
     rescan();
-    double hit = 0.0;
+    double won = -INFINITY;  // lane c: log2 P of the outcome kept in round c
     int c = 0;
     for (; c < a.ncache; ++c) {
         double ws = bs;
         int wi = bi;
         wave_best(ws, wi);
         if (!(ws > -INFINITY)) break;  // no outcome with positive probability left
-        const double P = exp2(ws);
-        hit += P;
+        if (lane == c) won = ws;
         if (lane == 0) {
             ok_[c] = wi / per_row;
             oa_[c] = c_tok[wi];
-            op_[c] = P;
         }
         if (bi == wi) {  // the owner of the winning list advances it
             l_pos[bl] += 1;
             rescan();
         }
     }
+    // the kept outcomes' probabilities, one per lane off the rounds' critical
+    // path, and the hit probability summed in round order
+    const double P = lane < c ? exp2(won) : 0.0;
+    if (lane < c) op_[lane] = P;
+    double hit = 0.0;
+    for (int j = 0; j < c; ++j) hit += readlane_f64(P, j);
     if (lane == 0) {
         for (; c < a.ncache; ++c) {
             ok_[c] = -1;
