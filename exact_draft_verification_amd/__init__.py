@@ -11,7 +11,11 @@ Entry points (same names as the C ABI):
   spec_verify_chain(target, draft, draft_tokens, uniforms, temperature, ...)
   spec_verify_chain_pointmass(target, draft_tokens, uniforms, temperature, ...)
   spec_verify_tree_greedy(target, parents, tokens, ...)
+  spec_verify_tree_stochastic(target, draft, parents, tokens, uniforms, temperature, ...)
   spec_outcome_topk(logits, draft_tokens, temperature, ncache, ...)
+  spec_cache_lookup(accept_len, out_tokens, cache_k, cache_a, ...)
+  spec_tree_build(draft_logits, temperature, width, max_depth, budget, ...)
+and the *_workspace_bytes sizing functions.
 """
 from __future__ import annotations
 
@@ -19,7 +23,7 @@ import ctypes as _ct
 import os as _os
 
 __all__ = [
-    "SV_DTYPE_F32", "SV_DTYPE_BF16", "SpecVerifyError", "library_path", "load_library",
+    "SV_DTYPE_F32", "SV_DTYPE_BF16", "SV_MAX_VOCAB", "SpecVerifyError", "library_path", "load_library",
     "spec_verify_chain", "spec_verify_tree_greedy", "spec_verify_chain_workspace_bytes",
     "spec_verify_chain_pointmass", "spec_verify_chain_pointmass_workspace_bytes",
     "spec_outcome_topk", "spec_outcome_topk_workspace_bytes", "spec_cache_lookup",
