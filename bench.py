@@ -371,6 +371,11 @@ def measure(w, steps, warmup, torch, hip):
     n_ev = min(steps, 400)
     evs = hip.create(w.n_events * n_ev)
     torch.cuda.synchronize()
+    # The host needs about 30 us to enqueue one call, longer than a small
+    # workload's step: a spin kernel ahead of the calls (about 60 us of GPU
+    # time per call) lets all of them be queued first, so that they run back
+    # to back as in the graph instead of one by one on an idling GPU.
+    torch.cuda._sleep(n_ev * 150_000)
     for i in range(n_ev):
         w.step(i, h, evs[i * w.n_events:(i + 1) * w.n_events])
     torch.cuda.synchronize()
