@@ -177,10 +177,27 @@ def test_invalid_blocks(kind):
 
 def test_uniform_extremes():
     d = synth.chain_inputs(20, 3, 2500, "bf16", T=1.0, seed=13)
+    V = d["V"]
+    top = np.nextafter(np.float32(1), np.float32(0))
+    # The draw's uniform at 0 or just below 1 lies within the band of the
+    # CDF's end points, so the oracle comparison excludes these blocks; the
+    # assertions pin them instead.
+    # u = 0 everywhere: every test passes (each p_i(x_i) > 0 here), and the
+    # bonus draw takes the first token of positive probability under
+    # p_gamma, token 0 (every logit is finite and moderate).
     d["uniforms"] = np.zeros_like(d["uniforms"])
     g, _ = run_case(d, "u0")
-    assert (g["accept_len"] == 3).all()
-    d["uniforms"] = np.full_like(d["uniforms"], np.nextafter(np.float32(1), np.float32(0)))
+    assert (g["accept_len"] == 3).all() and (g["out_tokens"][:, 3] == 0).all()
+    # tests at u = 0, the draw at the largest float below 1: the bonus draw
+    # takes the last token, V - 1
+    d["uniforms"] = np.zeros_like(d["uniforms"])
+    d["uniforms"][:, 3] = top
+    g, _ = run_case(d, "u-draw-top")
+    assert (g["accept_len"] == 3).all() and (g["out_tokens"][:, 3] == V - 1).all()
+    # every uniform at the top: a test then passes only where r_i rounds to
+    # 1, which lies inside the boundary band (the run must still complete
+    # and agree wherever the band allows a comparison)
+    d["uniforms"] = np.full_like(d["uniforms"], top)
     run_case(d, "u-top")
 
 

@@ -134,3 +134,31 @@ def test_acceptance_frequency():
         a = px[reached, i]
         sd = np.sqrt((a * (1 - a)).sum())
         assert abs((k[reached] > i).sum() - a.sum()) < 4.5 * sd, i
+
+
+def test_uniform_extremes():
+    """Draws at the ends of the CDF (uniform 0, or the largest float below 1)
+    sit within the band of the CDF's end points, so the oracle comparison
+    excludes them; the assertions pin them: the first and the last token of
+    positive weight."""
+    d = synth.pointmass_inputs(20, 3, 2500, "bf16", T=1.0, seed=35)
+    V = d["V"]
+    tok = d["draft_tokens"]
+    top = np.nextafter(np.float32(1), np.float32(0))
+    # every test passes at u = 0 (each p_i(x_i) > 0); the bonus draw takes
+    # token 0 at u = 0 and token V - 1 just below 1
+    for u_draw, want in ((0.0, 0), (top, V - 1)):
+        d["uniforms"] = np.zeros_like(d["uniforms"])
+        d["uniforms"][:, 3] = u_draw
+        g, _ = run_case(d, f"pm-accept-draw{u_draw:.0f}")
+        assert (g["accept_len"] == 3).all() and (g["out_tokens"][:, 3] == want).all()
+    # the first test fails just below 1 (no p_0(x_0) is that close to 1
+    # here); the draw from p_0 without x_0 then takes the first or the last
+    # token other than x_0
+    for u_draw, want in ((0.0, np.where(tok[:, 0] == 0, 1, 0)),
+                         (top, np.where(tok[:, 0] == V - 1, V - 2, V - 1))):
+        d["uniforms"] = np.zeros_like(d["uniforms"])
+        d["uniforms"][:, 0] = top
+        d["uniforms"][:, 3] = u_draw
+        g, _ = run_case(d, f"pm-reject-draw{u_draw:.0f}")
+        assert (g["accept_len"] == 0).all() and (g["out_tokens"][:, 0] == want).all()
