@@ -220,34 +220,42 @@ __global__ __launch_bounds__(kThreads) void tree_search_kernel(TreeBuildArgs a) 
             bl = l;
         }
     };
-    // adds the candidate children of node v (all lanes; arguments uniform)
-    auto expand = [&](int v, int rv, int dv, double sv) {
-        int tk = -1, cr = -1;
-        float q = 0.0f;
+    // the candidate children of row rv: lane j < W gets child j's token,
+    // ln q and row (static tables, so the read may precede the list update)
+    struct Children {
+        int tk, cr;
+        float q;
+    };
+    auto children = [&](int rv) {
+        Children c{-1, -1, 0.0f};
         if (lane < W) {
-            tk = c_tok[rv * W + lane];
-            q = c_lq[rv * W + lane];
-            cr = c_row[rv * W + lane];
+            c.tk = c_tok[rv * W + lane];
+            c.q = c_lq[rv * W + lane];
+            c.cr = c_row[rv * W + lane];
         }
-        const int cnt = min(__popcll(__ballot(tk >= 0)), B - n);  // the children form a prefix
-        const double s = sv + static_cast<double>(q);
+        return c;
+    };
+    // adds the candidate children c of node v (all lanes; arguments uniform)
+    auto expand = [&](int v, int dv, double sv, const Children& c) {
+        const int cnt = min(__popcll(__ballot(c.tk >= 0)), B - n);  // the children form a prefix
+        const double s = sv + static_cast<double>(c.q);
         if (lane < cnt) {
             const int u = n + lane;
             n_score[u] = s;
-            n_row[u] = cr;
+            n_row[u] = c.cr;
             o_par[u] = v;
-            o_tok[u] = tk;
-            o_row[u] = cr;
+            o_tok[u] = c.tk;
+            o_row[u] = c.cr;
             o_sc[u] = s;
         }
         // only children with a row are ever expanded
-        const uint64_t expandable = __ballot(lane < cnt && cr >= 0);
+        const uint64_t expandable = __ballot(lane < cnt && c.cr >= 0);
         if (dv + 1 < N && expandable != 0) {
             const int f = __builtin_ctzll(expandable);
             const int l = nlists++;
             const double hs = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(s), f),
                                                __builtin_amdgcn_readlane(__double2loint(s), f));
-            const int hrd = pack_rd(__builtin_amdgcn_readlane(cr, f), dv + 1);
+            const int hrd = pack_rd(__builtin_amdgcn_readlane(c.cr, f), dv + 1);
             if (lane == (l & 63)) {
                 l_head[l] = n + f;
                 l_end[l] = n + cnt;
@@ -266,27 +274,40 @@ __global__ __launch_bounds__(kThreads) void tree_search_kernel(TreeBuildArgs a) 
         // reads without waiting for the global stores
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     };
-    expand(0, 0, 0, 0.0);  // the root is the only queued node at first
+    expand(0, 0, 0.0, children(0));  // the root is the only queued node at first
     while (n < B) {
         double ws = bs;
         int wn = bn, wrd = brd;
         wave_best_rd(ws, wn, wrd);
         if (wn == INT32_MAX) break;  // nothing left to expand
-        if (bn == wn) {              // the owner advances the popped list
+        const Children c = children(wrd >> 10);
+        if (bn == wn) {  // the owner advances the popped list
             const int e = l_end[bl];
             int h = wn + 1;
             while (h < e && n_row[h] < 0) ++h;
             l_head[bl] = h;
-            if (h < e) {
-                l_hs[bl] = n_score[h];
-                l_hrd[bl] = pack_rd(n_row[h], wrd & 1023);
-            }
             bs = -INFINITY;
             bn = INT32_MAX;
-            bl = -1;
-            for (int l = lane; l < nlists; l += 64) consider(l);
+            if (h < e) {
+                const double hs = n_score[h];
+                const int hrd = pack_rd(n_row[h], wrd & 1023);
+                l_hs[bl] = hs;
+                l_hrd[bl] = hrd;
+                if (nlists <= 64) {
+                    // the lane owns this one list: its head is the lane's best
+                    bs = hs;
+                    bn = h;
+                    brd = hrd;
+                }
+            }
+            if (nlists > 64) {
+                bl = -1;
+                for (int l = lane; l < nlists; l += 64) consider(l);
+            } else if (h >= e) {
+                bl = -1;
+            }
         }
-        expand(wn, wrd >> 10, wrd & 1023, ws);
+        expand(wn, wrd & 1023, ws, c);
     }
     for (int i = n + lane; i < B; i += 64) {
         o_par[i] = -1;
