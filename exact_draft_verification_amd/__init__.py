@@ -166,6 +166,17 @@ def _ptr(t):
     return None if t is None else _ct.c_void_p(t.data_ptr())
 
 
+def _new(shape, dtype, device, stream):
+    """torch.empty for a tensor the library writes on `stream`.  A tensor
+    allocated while another stream is current is marked as used on `stream`,
+    so torch's allocator does not hand its memory to other work while
+    `stream` may still be writing it."""
+    t = _torch().empty(shape, dtype=dtype, device=device)
+    if stream is not None:
+        t.record_stream(stream)
+    return t
+
+
 def _stream_handle(stream, device):
     torch = _torch()
     if stream is None:
@@ -192,7 +203,7 @@ def _workspace(nbytes: int, device, stream):
     key = (str(device), int(stream.cuda_stream))
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws = _new(max(nbytes, 256), torch.uint8, device, stream)
         _ws_cache[key] = ws
     return ws
 
@@ -222,11 +233,11 @@ def spec_verify_chain(target, draft, draft_tokens, uniforms, temperature, *, acc
     _check(draft_tokens, "draft_tokens", (B, g), dtype=torch.int32, device=dev)
     _check(uniforms, "uniforms", (B, g1), dtype=torch.float32, device=dev)
     if accept_len is None:
-        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+        accept_len = _new(B, torch.int32, dev, stream)
     if out_tokens is None:
-        out_tokens = torch.empty((B, g1), dtype=torch.int32, device=dev)
+        out_tokens = _new((B, g1), torch.int32, dev, stream)
     if final_dist is None and want_dist:
-        final_dist = torch.empty((B, V), dtype=torch.float32, device=dev)
+        final_dist = _new((B, V), torch.float32, dev, stream)
     _check(accept_len, "accept_len", (B,), dtype=torch.int32, device=dev)
     _check(out_tokens, "out_tokens", (B, g1), dtype=torch.int32, device=dev)
     if final_dist is not None:
@@ -267,11 +278,11 @@ def spec_verify_chain_pointmass(target, draft_tokens, uniforms, temperature, *, 
     _check(draft_tokens, "draft_tokens", (B, g), dtype=torch.int32, device=dev)
     _check(uniforms, "uniforms", (B, g1), dtype=torch.float32, device=dev)
     if accept_len is None:
-        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+        accept_len = _new(B, torch.int32, dev, stream)
     if out_tokens is None:
-        out_tokens = torch.empty((B, g1), dtype=torch.int32, device=dev)
+        out_tokens = _new((B, g1), torch.int32, dev, stream)
     if final_dist is None and want_dist:
-        final_dist = torch.empty((B, V), dtype=torch.float32, device=dev)
+        final_dist = _new((B, V), torch.float32, dev, stream)
     _check(accept_len, "accept_len", (B,), dtype=torch.int32, device=dev)
     _check(out_tokens, "out_tokens", (B, g1), dtype=torch.int32, device=dev)
     if final_dist is not None:
@@ -312,13 +323,13 @@ def spec_outcome_topk(logits, draft_tokens, temperature, ncache, *, out_k=None, 
     _check(draft_tokens, "draft_tokens", (R, g), dtype=torch.int32, device=dev)
     ncache = int(ncache)
     if out_k is None:
-        out_k = torch.empty((R, ncache), dtype=torch.int32, device=dev)
+        out_k = _new((R, ncache), torch.int32, dev, stream)
     if out_a is None:
-        out_a = torch.empty((R, ncache), dtype=torch.int32, device=dev)
+        out_a = _new((R, ncache), torch.int32, dev, stream)
     if out_p is None:
-        out_p = torch.empty((R, ncache), dtype=torch.float64, device=dev)
+        out_p = _new((R, ncache), torch.float64, dev, stream)
     if hit is None:
-        hit = torch.empty(R, dtype=torch.float64, device=dev)
+        hit = _new(R, torch.float64, dev, stream)
     _check(out_k, "out_k", (R, ncache), dtype=torch.int32, device=dev)
     _check(out_a, "out_a", (R, ncache), dtype=torch.int32, device=dev)
     _check(out_p, "out_p", (R, ncache), dtype=torch.float64, device=dev)
@@ -361,13 +372,13 @@ def spec_verify_tree_stochastic(target_logits, draft_logits, parents, tokens, un
     _check(tokens, "tokens", (B, n), dtype=torch.int32, device=dev)
     _check(uniforms, "uniforms", (B, n), dtype=torch.float32, device=dev)
     if accept_len is None:
-        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+        accept_len = _new(B, torch.int32, dev, stream)
     if accept_node is None:
-        accept_node = torch.empty(B, dtype=torch.int32, device=dev)
+        accept_node = _new(B, torch.int32, dev, stream)
     if out_tokens is None:
-        out_tokens = torch.empty((B, n), dtype=torch.int32, device=dev)
+        out_tokens = _new((B, n), torch.int32, dev, stream)
     if want_dist and final_dist is None:
-        final_dist = torch.empty((B, V), dtype=torch.float32, device=dev)
+        final_dist = _new((B, V), torch.float32, dev, stream)
     _check(accept_len, "accept_len", (B,), dtype=torch.int32, device=dev)
     _check(accept_node, "accept_node", (B,), dtype=torch.int32, device=dev)
     _check(out_tokens, "out_tokens", (B, n), dtype=torch.int32, device=dev)
@@ -412,7 +423,7 @@ def spec_tree_build(draft_logits, temperature, width, max_depth, budget, *, chil
 
     def out(t, name, shape, dt):
         if t is None:
-            t = torch.empty(shape, dtype=dt, device=dev)
+            t = _new(shape, dt, dev, stream)
         _check(t, name, shape, dtype=dt, device=dev)
         return t
 
@@ -454,7 +465,7 @@ def spec_cache_lookup(accept_len, out_tokens, cache_k, cache_a, *, slot=None, st
     _check(cache_k, "cache_k", (R, ncache), dtype=torch.int32, device=dev)
     _check(cache_a, "cache_a", (R, ncache), dtype=torch.int32, device=dev)
     if slot is None:
-        slot = torch.empty(R, dtype=torch.int32, device=dev)
+        slot = _new(R, torch.int32, dev, stream)
     _check(slot, "slot", (R,), dtype=torch.int32, device=dev)
     st = lib.spec_cache_lookup(_ptr(accept_len), _ptr(out_tokens), R, g1 - 1, _ptr(cache_k),
                                _ptr(cache_a), ncache, _ptr(slot), _stream_handle(stream, dev))
@@ -480,11 +491,11 @@ def spec_verify_tree_greedy(target, parents, tokens, *, accept_len=None, accept_
     _check(parents, "parents", (B, n), dtype=torch.int32, device=dev)
     _check(tokens, "tokens", (B, n), dtype=torch.int32, device=dev)
     if accept_len is None:
-        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+        accept_len = _new(B, torch.int32, dev, stream)
     if accept_node is None:
-        accept_node = torch.empty(B, dtype=torch.int32, device=dev)
+        accept_node = _new(B, torch.int32, dev, stream)
     if out_tokens is None:
-        out_tokens = torch.empty((B, n), dtype=torch.int32, device=dev)
+        out_tokens = _new((B, n), torch.int32, dev, stream)
     _check(accept_len, "accept_len", (B,), dtype=torch.int32, device=dev)
     _check(accept_node, "accept_node", (B,), dtype=torch.int32, device=dev)
     _check(out_tokens, "out_tokens", (B, n), dtype=torch.int32, device=dev)

@@ -105,3 +105,20 @@ def test_workspace_garbage_for_stochastic_trees():
         assert np.array_equal(out.cpu().numpy()[keep], o["out_tokens"][keep])
         same = node.cpu().numpy() == o["accept_node"]
         assert np.abs(dist.cpu().numpy()[same] - o["final_dist"][same]).max() <= 1e-5
+
+
+def test_explicit_stream_with_binding_workspace():
+    """Calls on a stream that is not the current one, with the binding's own
+    outputs and cached workspace: a small call, then a larger one that grows
+    the workspace (the smaller one is released while that stream may still
+    use it, which the binding declares to torch's allocator), then the small
+    call again.  Every result matches the oracle."""
+    torch, sv = require_gpu()
+    s = torch.cuda.Stream()
+    small = synth.chain_inputs(3, 4, 5000, "bf16", T=0.8, seed=61)
+    big = synth.chain_inputs(16, 6, 40000, "bf16", T=0.8, seed=62)
+    for label, d in (("small", small), ("big", big), ("small-again", small)):
+        g = gpu_chain(d, want_dist=True, stream=s)
+        o = oracle.chain(d["target"], d["draft"], d["draft_tokens"], d["uniforms"], d["T"],
+                         dtype=d["dtype"], want_dist=True)
+        compare_chain(g, o, f"stream-{label}")
