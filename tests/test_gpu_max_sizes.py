@@ -1,0 +1,86 @@
+"""GPU parity at the largest vocabulary the library accepts (needs an MI355X).
+
+V = 2^29 is the vocabulary limit checked on the host: below it, every 32-bit
+element index in the kernels, plus a tile or a segment, stays inside int32.
+The rows are seeded pools of bf16 logits tiled to full length, which is cheap
+to build at this size. The tokens that decide each case sit near the end of
+the rows, so element and byte offsets reach their largest values. Each decision
+is far from its boundary, so the oracle comparison covers every block."""
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import compare_chain, compare_tree, gpu_chain, gpu_tree, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+POOLS = (1_000_003, 999_983, 1_000_033, 999_979, 1_000_037, 999_961)
+
+
+def _rows(n, V, seed):
+    """n rows of V bf16 logits: seeded N(0, 1) pools of prime lengths, tiled."""
+    rng = np.random.default_rng(seed)
+    out = np.empty((n, V), np.uint16)
+    for r in range(n):
+        pool = synth.bf16_bits(rng.standard_normal(POOLS[r % len(POOLS)]).astype(np.float32))
+        out[r] = np.resize(pool, V)
+    return out
+
+
+def _bf16(x):
+    return synth.bf16_bits(np.array([x], np.float32))[0]
+
+
+def test_chain_at_the_largest_vocabulary():
+    torch, sv = require_gpu()
+    V = sv.SV_MAX_VOCAB
+    B, g = 2, 1
+    t0 = time.time()
+    tgt = _rows(2 * B, V, 81).reshape(B, 2, V)
+    dr = _rows(B, V, 82).reshape(B, 1, V)
+    x = V - 7
+    # block 0: target and draft both put most of their mass on x (p(x) ~ 0.8
+    # >= q(x) ~ 0.7, so the test passes), and the bonus row puts ~0.8 on
+    # V - 3, where the draw at u = 0.9 lands
+    tgt[0, 0, x], dr[0, 0, x], tgt[0, 1, V - 3] = _bf16(22.0), _bf16(21.5), _bf16(22.0)
+    # block 1: the draft is surer of x than the target (r ~ 0.16, rejected at
+    # u = 0.9), and the target's token V - 2 holds most of the residual, where
+    # the draw at u = 0.5 lands
+    tgt[1, 0, x], dr[1, 0, x], tgt[1, 0, V - 2] = _bf16(20.0), _bf16(21.0), _bf16(22.0)
+    d = dict(target=tgt, draft=dr, draft_tokens=np.full((B, g), x, np.int32),
+             uniforms=np.array([[0.5, 0.9], [0.9, 0.5]], np.float32), B=B, gamma=g, V=V,
+             dtype="bf16", T=1.0)
+    print(f"[case] max-V chain B={B} gamma={g} V={V}: inputs in {time.time() - t0:.1f}s", flush=True)
+    res = gpu_chain(d)
+    print(f"[case] max-V chain: GPU done at {time.time() - t0:.1f}s", flush=True)
+    o = oracle.chain(d["target"], d["draft"], d["draft_tokens"], d["uniforms"], d["T"],
+                     dtype="bf16")
+    print(f"[case] max-V chain: oracle done at {time.time() - t0:.1f}s", flush=True)
+    n, near = compare_chain(res, o, "max-V chain", check_dist=False)
+    assert n == B and near == 0
+    assert res["accept_len"].tolist() == [1, 0]
+    assert res["out_tokens"].tolist() == [[x, V - 3], [V - 2, -1]]
+
+
+def test_tree_at_the_largest_ragged_vocabulary():
+    """V = 2^29 - 3: rows are not 16-byte aligned (scalar heads and tails in
+    every segment), and each row's argmax sits in its last few elements."""
+    torch, sv = require_gpu()
+    V = sv.SV_MAX_VOCAB - 3
+    t0 = time.time()
+    rows = _rows(4, V, 83)
+    # root -> 1 -> 2 matches the argmax at every step; node 3 does not; the
+    # bonus token is row 2's argmax, the very last element
+    rows[0, V - 5], rows[1, V - 4], rows[2, V - 1] = _bf16(9.0), _bf16(9.0), _bf16(9.0)
+    d = dict(target=rows.reshape(1, 4, V), parents=np.array([[-1, 0, 1, 0]], np.int32),
+             tokens=np.array([[0, V - 5, V - 4, V - 6]], np.int32), dtype="bf16")
+    print(f"[case] max-V tree n=4 V={V}: inputs in {time.time() - t0:.1f}s", flush=True)
+    res = gpu_tree(d)
+    o = oracle.tree_greedy(d["target"], d["parents"], d["tokens"])
+    print(f"[case] max-V tree: done at {time.time() - t0:.1f}s", flush=True)
+    compare_tree(res, o, "max-V tree")
+    assert res["accept_len"].tolist() == [2] and res["accept_node"].tolist() == [2]
+    assert res["out_tokens"][0, :3].tolist() == [V - 5, V - 4, V - 1]
