@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import compare_chain, compare_tree, gpu_chain, gpu_tree, require_gpu
+from gpu_util import compare_chain, compare_tree, gpu_chain, gpu_pointmass, gpu_tree, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -84,3 +84,28 @@ def test_tree_at_the_largest_ragged_vocabulary():
     compare_tree(res, o, "max-V tree")
     assert res["accept_len"].tolist() == [2] and res["accept_node"].tolist() == [2]
     assert res["out_tokens"][0, :3].tolist() == [V - 5, V - 4, V - 1]
+
+
+def test_pointmass_at_the_largest_vocabulary():
+    torch, sv = require_gpu()
+    V = sv.SV_MAX_VOCAB
+    B, g = 2, 1
+    tgt = _rows(2 * B, V, 84).reshape(B, 2, V)
+    x = V - 7
+    # block 0: p(x) ~ 0.8 passes at u = 0.5; the bonus row's ~0.8 on V - 3
+    # takes the draw at u = 0.9.  Block 1: p(x) ~ 0.1 fails at u = 0.9; the
+    # draw from p without x lands on V - 2 (~0.8 of what is left) at u = 0.5
+    tgt[0, 0, x], tgt[0, 1, V - 3] = _bf16(22.0), _bf16(22.0)
+    tgt[1, 0, x], tgt[1, 0, V - 2] = _bf16(20.0), _bf16(22.0)
+    d = dict(target=tgt, draft_tokens=np.full((B, g), x, np.int32),
+             uniforms=np.array([[0.5, 0.9], [0.9, 0.5]], np.float32), B=B, gamma=g, V=V,
+             dtype="bf16", T=1.0)
+    print(f"[case] max-V point-mass B={B} gamma={g} V={V}", flush=True)
+    res = gpu_pointmass(d)
+    o = oracle.chain_pointmass(d["target"], d["draft_tokens"], d["uniforms"], d["T"],
+                               dtype="bf16")
+    n, near = compare_chain(res, o, "max-V point-mass", check_dist=False)
+    assert n == B and near == 0
+    assert res["accept_len"].tolist() == [1, 0]
+    assert res["out_tokens"].tolist() == [[x, V - 3], [V - 2, -1]]
+
