@@ -13,7 +13,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import compare_chain, compare_tree, gpu_chain, gpu_pointmass, gpu_tree, require_gpu
+from gpu_util import (compare_chain, compare_tree, gpu_chain, gpu_pointmass, gpu_tree,
+                      require_gpu, to_dev, to_dev_logits)
 
 pytestmark = pytest.mark.gpu
 
@@ -109,3 +110,32 @@ def test_pointmass_at_the_largest_vocabulary():
     assert res["accept_len"].tolist() == [1, 0]
     assert res["out_tokens"].tolist() == [[x, V - 3], [V - 2, -1]]
 
+
+
+def test_stochastic_tree_at_the_largest_vocabulary():
+    torch, sv = require_gpu()
+    V = sv.SV_MAX_VOCAB
+    n = 3
+    tgt = _rows(n, V, 86).reshape(1, n, V)
+    dr = _rows(n, V, 87).reshape(1, n, V)
+    y1, y2 = V - 7, V - 5
+    # node 1 (child of the root): both root rows put most of their mass on y1
+    # (p ~ 0.8 >= q ~ 0.7, passes at u = 0.5); node 2 (child of node 1): node
+    # 1's draft row is surer of y2 than its target row (r ~ 0.16, fails at
+    # u = 0.9).  The correction comes from target row 1, whose ~0.35 on y2
+    # takes the draw at u = 0.9
+    tgt[0, 0, y1], dr[0, 0, y1] = _bf16(22.0), _bf16(21.5)
+    tgt[0, 1, y2], dr[0, 1, y2] = _bf16(20.0), _bf16(21.0)
+    par = np.array([[-1, 0, 1]], np.int32)
+    tok = np.array([[0, y1, y2]], np.int32)
+    uni = np.array([[0.9, 0.5, 0.9]], np.float32)
+    print(f"[case] max-V stochastic tree n={n} V={V}", flush=True)
+    acc, node, out, _ = sv.spec_verify_tree_stochastic(
+        to_dev_logits(tgt, "bf16"), to_dev_logits(dr, "bf16"), to_dev(par, np.int32),
+        to_dev(tok, np.int32), to_dev(uni, np.float32), 1.0)
+    torch.cuda.synchronize()
+    o = oracle.tree_stochastic(tgt, dr, par, tok, uni, 1.0, dtype="bf16")
+    assert o["margin"][0] >= 1e-6
+    assert acc.cpu().tolist() == o["accept_len"].tolist() == [1]
+    assert node.cpu().tolist() == o["accept_node"].tolist() == [1]
+    assert out.cpu().tolist() == o["out_tokens"].tolist() == [[y1, y2, -1]]
