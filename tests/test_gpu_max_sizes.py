@@ -139,3 +139,25 @@ def test_stochastic_tree_at_the_largest_vocabulary():
     assert acc.cpu().tolist() == o["accept_len"].tolist() == [1]
     assert node.cpu().tolist() == o["accept_node"].tolist() == [1]
     assert out.cpu().tolist() == o["out_tokens"].tolist() == [[y1, y2, -1]]
+
+
+def test_tree_construction_at_the_largest_vocabulary():
+    torch, sv = require_gpu()
+    V = sv.SV_MAX_VOCAB
+    W, N, budget = 2, 2, 5
+    rows = _rows(3, V, 88).reshape(1, 3, V)
+    # root row: V - 3 (~0.6) then V - 9 (~0.23); row 1, the child through
+    # V - 3 and the best queued node after the root, puts ~0.6 on V - 1 and
+    # ~0.23 on V - 2, which fill the budget
+    rows[0, 0, V - 3], rows[0, 0, V - 9] = _bf16(22.0), _bf16(21.0)
+    rows[0, 1, V - 1], rows[0, 1, V - 2] = _bf16(22.0), _bf16(21.0)
+    print(f"[case] max-V tree construction M=3 V={V} W={W} N={N} budget={budget}", flush=True)
+    par, tok, row, sc, n = sv.spec_tree_build(to_dev_logits(rows, "bf16"), 1.0, W, N, budget)
+    torch.cuda.synchronize()
+    o = oracle.tree_build(rows, 1.0, W, N, budget, dtype="bf16")
+    assert o["min_gap"][0] >= 1e-4
+    assert n.cpu().tolist() == o["n"].tolist() == [5]
+    assert par.cpu().tolist() == o["parents"].tolist() == [[-1, 0, 0, 1, 1]]
+    assert tok.cpu().tolist() == o["tokens"].tolist() == [[-1, V - 3, V - 9, V - 1, V - 2]]
+    assert row.cpu().tolist() == o["rows"].tolist()
+    assert np.allclose(sc.cpu().numpy(), o["score"], rtol=0, atol=1e-4)
