@@ -170,9 +170,11 @@ def _new(shape, dtype, device, stream):
     """torch.empty for a tensor the library writes on `stream`.  A tensor
     allocated while another stream is current is marked as used on `stream`,
     so torch's allocator does not hand its memory to other work while
-    `stream` may still be writing it."""
-    t = _torch().empty(shape, dtype=dtype, device=device)
-    if stream is not None:
+    `stream` may still be writing it (when `stream` is the current stream,
+    as under graph capture, the allocation already belongs to it)."""
+    torch = _torch()
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(device):
         t.record_stream(stream)
     return t
 

@@ -97,3 +97,16 @@ def test_graph_every_entry_point():
                       dtype=torch.uint8, device=dev)
     check_graph(lambda: sv.spec_tree_build(blg, b["T"], 4, 3, 30, workspace=bws),
                 "tree construction")
+
+
+def test_graph_with_explicit_stream_and_binding_workspace():
+    """The call names the capture stream explicitly and lets the binding
+    provide its workspace (allocated by the warm-up call, reused under
+    capture) and its outputs."""
+    torch, sv = require_gpu()
+    d = synth.chain_inputs(4, 5, 3001, "bf16", T=0.8, seed=121)
+    tg, dr = to_dev_logits(d["target"], "bf16"), to_dev_logits(d["draft"], "bf16")
+    tok, uni = to_dev(d["draft_tokens"], np.int32), to_dev(d["uniforms"], np.float32)
+    check_graph(lambda: sv.spec_verify_chain(tg, dr, tok, uni, d["T"], want_dist=True,
+                                             stream=torch.cuda.current_stream()),
+                "chain, explicit stream")
