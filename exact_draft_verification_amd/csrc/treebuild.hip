@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void tree_search_kernel(TreeBuildArgs a) 
     const int nseg = a.st.nseg, kb = a.st.kb;
     double* n_score = reinterpret_cast<double*>(s_dyn);  // [B] node scores
     double* l_hs = n_score + B;                          // [B] list head scores
-    float* c_lq = reinterpret_cast<float*>(l_hs + B);    // [slots] children per row
+    double* c_lq = l_hs + B;                             // [slots] children's ln q per row
     int* c_tok = reinterpret_cast<int*>(c_lq + slots);   // [slots]
     int* c_row = c_tok + slots;                          // [slots]
     int* n_row = c_row + slots;                          // [B]
@@ -119,8 +119,7 @@ __global__ __launch_bounds__(kThreads) void tree_search_kernel(TreeBuildArgs a) 
                     const bool ok = c[q].idx != INT32_MAX && c[q].val != -INFINITY;  // a prefix
                     c_tok[m * W + q] = ok ? c[q].idx : -1;
                     c_lq[m * W + q] =
-                        ok ? static_cast<float>((static_cast<double>(c[q].val) * a.st.c_d - L) * kLn2)
-                           : -INFINITY;
+                        ok ? (static_cast<double>(c[q].val) * a.st.c_d - L) * kLn2 : -INFINITY;
                 }
             }
             continue;
@@ -150,8 +149,7 @@ __global__ __launch_bounds__(kThreads) void tree_search_kernel(TreeBuildArgs a) 
             }
             if (best == 0) break;  // fewer than W tokens of positive probability
             c_tok[m * W + j] = static_cast<int>(key_index(best));
-            c_lq[m * W + j] =
-                static_cast<float>((static_cast<double>(key_value(best)) * a.st.c_d - L) * kLn2);
+            c_lq[m * W + j] = (static_cast<double>(key_value(best)) * a.st.c_d - L) * kLn2;
             prev = best;
         }
         for (; j < W; ++j) {
@@ -224,10 +222,10 @@ __global__ __launch_bounds__(kThreads) void tree_search_kernel(TreeBuildArgs a) 
     // ln q and row (static tables, so the read may precede the list update)
     struct Children {
         int tk, cr;
-        float q;
+        double q;
     };
     auto children = [&](int rv) {
-        Children c{-1, -1, 0.0f};
+        Children c{-1, -1, 0.0};
         if (lane < W) {
             c.tk = c_tok[rv * W + lane];
             c.q = c_lq[rv * W + lane];
@@ -238,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void tree_search_kernel(TreeBuildArgs a) 
     // adds the candidate children c of node v (all lanes; arguments uniform)
     auto expand = [&](int v, int dv, double sv, const Children& c) {
         const int cnt = min(__popcll(__ballot(c.tk >= 0)), B - n);  // the children form a prefix
-        const double s = sv + static_cast<double>(c.q);
+        const double s = sv + c.q;
         if (lane < cnt) {
             const int u = n + lane;
             n_score[u] = s;
@@ -323,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void tree_search_kernel(TreeBuildArgs a) 
 size_t tree_search_lds_bytes(int M, int W, int budget) {
     const size_t slots = static_cast<size_t>(M) * W;
     return static_cast<size_t>(budget) * (2 * sizeof(double) + 4 * sizeof(int)) +
-           slots * (sizeof(float) + 2 * sizeof(int));
+           slots * (sizeof(double) + 2 * sizeof(int));
 }
 
 hipError_t launch_tree_search(const TreeBuildArgs& a, hipStream_t s) {

@@ -58,10 +58,13 @@ def _declare(lib):
     lib.oracle_chain_pointmass_du.argtypes = [P, I, P, P, I, I, I, D, P, P, P, P, P, P, I]
     lib.oracle_outcome_topk.argtypes = [P, I, P, I, I, I, D, I, P, P, P, P, P]
     lib.oracle_tree_build.argtypes = [P, I, I, I, I, D, I, I, I, P, P, P, P, P, P, P]
-    lib.oracle_tree_stochastic.argtypes = [P, P, I, P, P, P, I, I, I, D, P, P, P, P, P]
+    lib.oracle_tree_score.argtypes = [P, I, I, I, I, D, I, P, P, P, P, P]
+    lib.oracle_tree_stochastic.argtypes = [P, P, I, P, P, P, I, I, I, D, P, P, P, P, P, P]
+    lib.oracle_tree_stochastic_du.argtypes = [P, P, I, P, P, P, I, I, I, D, P, P, P, P, P, P]
     for f in (lib.oracle_chain, lib.oracle_chain_du, lib.oracle_chain_alpha,
               lib.oracle_tree_greedy, lib.oracle_chain_pointmass, lib.oracle_chain_pointmass_du,
-              lib.oracle_outcome_topk, lib.oracle_tree_build, lib.oracle_tree_stochastic):
+              lib.oracle_outcome_topk, lib.oracle_tree_build, lib.oracle_tree_stochastic,
+              lib.oracle_tree_stochastic_du, lib.oracle_tree_score):
         f.restype = I
     return lib
 
@@ -222,27 +225,39 @@ def tree_stochastic(target, draft, parents, tokens, uniforms, T, dtype="bf16",
     """Stochastic tree verification: one Bernoulli test per node with
     probability min(1, p/q) from its parent's rows, the deepest node whose
     whole path passed wins, and the correction is drawn from p after it with
-    u[:, 0].  Returns accept_len, accept_node [B], out_tokens [B, n], margin
-    [B] and, if asked, final_dist [B, V]."""
+    u[:, 0].  float32 uniforms use the library's interface; float64 uniforms
+    are taken as given (continuous-u enumeration in the tests).  Returns
+    accept_len, accept_node [B], out_tokens [B, n], margin [B], alpha [B, n]
+    (every node's test probability; NaN for the root) and, if asked,
+    final_dist [B, V]."""
     lib = _load()
     target = _logits(target, dtype)
     draft = _logits(draft, dtype)
     B, n, V = target.shape
-    assert draft.shape == (B, n, V)
+    if draft.shape != (B, n, V):
+        raise ValueError("draft must have the target's shape [B, n, V]")
     par = np.ascontiguousarray(parents, dtype=np.int32)
     tok = np.ascontiguousarray(tokens, dtype=np.int32)
-    u = np.ascontiguousarray(uniforms, dtype=np.float32)
+    u = np.ascontiguousarray(uniforms)
+    if u.shape != (B, n):
+        raise ValueError("uniforms must be [B, n]")
     acc = np.empty(B, np.int32)
     node = np.empty(B, np.int32)
     out = np.empty((B, n), np.int32)
     margin = np.empty(B, np.float64)
+    alpha = np.empty((B, n), np.float64)
     dist = np.empty((B, V), np.float64) if want_dist else None
-    rc = lib.oracle_tree_stochastic(_ptr(target), _ptr(draft), _DT[dtype], _ptr(par), _ptr(tok),
-                                    _ptr(u), B, n, V, float(T), _ptr(acc), _ptr(node), _ptr(out),
-                                    _ptr(dist), _ptr(margin))
+    if u.dtype == np.float64:
+        fn = lib.oracle_tree_stochastic_du
+    else:
+        fn = lib.oracle_tree_stochastic
+        u = np.ascontiguousarray(u, dtype=np.float32)
+    rc = fn(_ptr(target), _ptr(draft), _DT[dtype], _ptr(par), _ptr(tok), _ptr(u), B, n, V,
+            float(T), _ptr(acc), _ptr(node), _ptr(out), _ptr(dist), _ptr(margin), _ptr(alpha))
     if rc != 0:
         raise ValueError(f"oracle_tree_stochastic rejected its arguments (rc={rc})")
-    return dict(accept_len=acc, accept_node=node, out_tokens=out, margin=margin, final_dist=dist)
+    return dict(accept_len=acc, accept_node=node, out_tokens=out, margin=margin, alpha=alpha,
+                final_dist=dist)
 
 def tree_build(logits, T, W, N, budget, child_row=None, dtype="f32") -> dict:
     """Best-first construction of a draft tree from per-potential-node draft
@@ -270,6 +285,28 @@ def tree_build(logits, T, W, N, budget, child_row=None, dtype="f32") -> dict:
     if rc != 0:
         raise ValueError(f"oracle_tree_build rejected its arguments (rc={rc})")
     return dict(parents=par, tokens=tok, rows=rows, score=sc, n=n, min_gap=gap)
+
+def tree_score(logits, parents, tokens, rows, n, T, dtype="f32") -> np.ndarray:
+    """Scores [R, budget] of given trees under the draft rows [R, M, V]: the
+    sum of ln q(token) along each node's path, each token in its parent's row
+    ("JetSpec" reading notes, Eq. 15); -inf past the last node, NaN for a
+    malformed tree."""
+    lib = _load()
+    logits = _logits(logits, dtype)
+    R, M, V = logits.shape
+    par = np.ascontiguousarray(parents, dtype=np.int32)
+    budget = par.shape[1]
+    tok = np.ascontiguousarray(tokens, dtype=np.int32)
+    rw = np.ascontiguousarray(rows, dtype=np.int32)
+    nn = np.ascontiguousarray(n, dtype=np.int32)
+    assert par.shape == tok.shape == rw.shape == (R, budget) and nn.shape == (R,)
+    sc = np.empty((R, budget), np.float64)
+    rc = lib.oracle_tree_score(_ptr(logits), _DT[dtype], R, M, V, float(T), budget, _ptr(par),
+                               _ptr(tok), _ptr(rw), _ptr(nn), _ptr(sc))
+    if rc != 0:
+        raise ValueError(f"oracle_tree_score rejected its arguments (rc={rc})")
+    return sc
+
 
 def cache_lookup(accept_len, out_tokens, cache_k, cache_a) -> np.ndarray:
     """The cache slot hit by each verified block ("JetSpec++", Section 4.2:

@@ -45,10 +45,12 @@
  *    maximal depth the lowest node index wins;
  *  - invalid input (a draft token outside [0, V), a NaN or +inf logit, a row
  *    with no finite logit, a malformed parent array) makes that block
- *    invalid: accept_len = -1 and all its output tokens -1;
- *  - the library interface supports chain rows whose largest finite logit m
- *    satisfies |m| / T <= 2^28; a row outside that domain makes its block
- *    invalid here too.
+ *    invalid: accept_len = -1 and all its output tokens -1.  Every other
+ *    input, however large its logits or small its temperature, is evaluated
+ *    by the definitions below in double precision.
+ *
+ * Every allocation is checked; an entry point that cannot get its memory
+ * frees what it holds and returns -2.
  */
 #include <math.h>
 #include <pthread.h>
@@ -89,10 +91,6 @@ static int row_softmax_stats(const void *base, int dtype, int64_t off, int V, do
     }
     if (m == -INFINITY)
         return -1;
-    /* Interface domain: the library accepts rows whose largest finite logit
-     * satisfies |m| / T <= 2^28; larger magnitudes make the block invalid. */
-    if (fabs(m / T) > 268435456.0)
-        return -1;
     double S = 0.0;
     for (int v = 0; v < V; ++v) {
         double z = logit_at(base, dtype, off + v);
@@ -131,11 +129,13 @@ typedef struct {
     double *ratios;     /* nullable [B][gamma]: r_i at every position */
     int32_t *fallback;  /* nullable [B]: 1 if the W = 0 fallback was taken */
     double *work;       /* [nthreads][V] scratch for w(v) */
+    double *rowstats;   /* [nthreads][4 (gamma+1)] scratch for (m, S) of p and q */
     int nthreads;
 } chain_job;
 
-/* One chain block, following [SD] and [J++] F.1 step by step. */
-static void chain_block(const chain_job *J, int b, double *w)
+/* One chain block, following [SD] and [J++] F.1 step by step.  w holds V
+ * doubles and st 4 (gamma+1) doubles of the calling thread's scratch. */
+static void chain_block(const chain_job *J, int b, double *w, double *st)
 {
     const int g = J->gamma, V = J->V, dt = J->dtype;
     const double T = J->T;
@@ -163,17 +163,14 @@ static void chain_block(const chain_job *J, int b, double *w)
     for (int i = 0; i < g; ++i)
         if (d[i] < 0 || d[i] >= V)
             return;
-    double *mp = malloc(sizeof(double) * (size_t)(g + 1));
-    double *Sp = malloc(sizeof(double) * (size_t)(g + 1));
-    double *mq = malloc(sizeof(double) * (size_t)g);
-    double *Sq = malloc(sizeof(double) * (size_t)g);
+    double *mp = st, *Sp = st + (g + 1), *mq = st + 2 * (g + 1), *Sq = st + 3 * (g + 1);
     int bad = 0;
     for (int j = 0; j <= g && !bad; ++j)
         bad |= row_softmax_stats(J->target, dt, b * tblk + j * trow, V, T, &mp[j], &Sp[j]);
     for (int j = 0; j < g && !bad; ++j)
         bad |= row_softmax_stats(J->draft, dt, b * dblk + j * trow, V, T, &mq[j], &Sq[j]);
     if (bad)
-        goto done;
+        return;
 
     /* Ratio r_i = min(1, p_i(x)/q_i(x)) at every draft position ([SD]
      * "Acceptance depends on ..."; [JN] Eq. 1). */
@@ -264,16 +261,12 @@ static void chain_block(const chain_job *J, int b, double *w)
     if (J->final_dist)
         for (int v = 0; v < V; ++v)
             J->final_dist[(int64_t)b * V + v] = w[v] / W;
-done:
-    free(mp);
-    free(Sp);
-    free(mq);
-    free(Sq);
 }
 
 typedef struct {
     const chain_job *J;
     int tid;
+    void (*block)(const chain_job *, int, double *, double *);
 } chain_arg;
 
 static void *chain_worker(void *p)
@@ -281,37 +274,56 @@ static void *chain_worker(void *p)
     const chain_arg *a = (const chain_arg *)p;
     const chain_job *J = a->J;
     double *w = J->work + (int64_t)a->tid * J->V;
+    double *st = J->rowstats + (int64_t)a->tid * 4 * (J->gamma + 1);
     for (int b = a->tid; b < J->B; b += J->nthreads)
-        chain_block(J, b, w);
+        a->block(J, b, w, st);
     return NULL;
 }
 
-static int run_chain(chain_job *J)
+/* Runs fn(arg_i) for i < n on up to n threads; a thread that cannot be
+ * started has its share run on the calling thread instead. */
+static void run_parallel(void *(*fn)(void *), void *args, size_t arg_size, int n)
+{
+    pthread_t *th = n > 1 ? malloc(sizeof(pthread_t) * (size_t)n) : NULL;
+    char *started = n > 1 ? calloc((size_t)n, 1) : NULL;
+    for (int i = 0; i < n; ++i) {
+        void *ai = (char *)args + (size_t)i * arg_size;
+        if (th && started && pthread_create(&th[i], NULL, fn, ai) == 0)
+            started[i] = 1;
+        else
+            fn(ai);
+    }
+    for (int i = 0; i < n; ++i)
+        if (th && started && started[i])
+            pthread_join(th[i], NULL);
+    free(th);
+    free(started);
+}
+
+static int run_chain(chain_job *J, void (*block)(const chain_job *, int, double *, double *))
 {
     int nt = J->nthreads < 1 ? 1 : J->nthreads;
     if (nt > J->B)
         nt = J->B;
     J->nthreads = nt;
     J->work = malloc(sizeof(double) * (size_t)nt * (size_t)J->V);
-    if (!J->work)
-        return -2;
-    if (nt == 1) {
-        chain_arg a = {J, 0};
-        chain_worker(&a);
-    } else {
-        pthread_t *th = malloc(sizeof(pthread_t) * (size_t)nt);
-        chain_arg *args = malloc(sizeof(chain_arg) * (size_t)nt);
-        for (int i = 0; i < nt; ++i) {
-            args[i].J = J;
-            args[i].tid = i;
-            pthread_create(&th[i], NULL, chain_worker, &args[i]);
-        }
-        for (int i = 0; i < nt; ++i)
-            pthread_join(th[i], NULL);
-        free(th);
+    J->rowstats = malloc(sizeof(double) * (size_t)nt * 4 * (size_t)(J->gamma + 1));
+    chain_arg *args = malloc(sizeof(chain_arg) * (size_t)nt);
+    if (!J->work || !J->rowstats || !args) {
+        free(J->work);
+        free(J->rowstats);
         free(args);
+        return -2;
     }
+    for (int i = 0; i < nt; ++i) {
+        args[i].J = J;
+        args[i].tid = i;
+        args[i].block = block;
+    }
+    run_parallel(chain_worker, args, sizeof(chain_arg), nt);
+    free(args);
     free(J->work);
+    free(J->rowstats);
     return 0;
 }
 
@@ -330,8 +342,8 @@ int oracle_chain_du(const void *target, const void *draft, int dtype,
     if (dtype != ORC_F32 && dtype != ORC_BF16)
         return -1;
     chain_job J = {target, draft, dtype, draft_tokens, uniforms, B, gamma, V, T, accept_len,
-                   out_tokens, final_dist, margin, ratios, fallback, NULL, nthreads};
-    return run_chain(&J);
+                   out_tokens, final_dist, margin, ratios, fallback, NULL, NULL, nthreads};
+    return run_chain(&J, chain_block);
 }
 
 /* Chain verification with the float32 uniforms of the library interface;
@@ -367,7 +379,7 @@ int oracle_chain(const void *target, const void *draft, int dtype, const int32_t
  * block it is drawn from the bonus row p_gamma.  Same readings as the chain:
  * u[i] drives test i, u[gamma] the final draw by inverse CDF in ascending
  * token id; an empty residual falls back to p_k (flagged, margin 0). */
-static void pointmass_block(const chain_job *J, int b, double *w)
+static void pointmass_block(const chain_job *J, int b, double *w, double *st)
 {
     const int g = J->gamma, V = J->V, dt = J->dtype;
     const double T = J->T;
@@ -393,13 +405,12 @@ static void pointmass_block(const chain_job *J, int b, double *w)
     for (int i = 0; i < g; ++i)
         if (d[i] < 0 || d[i] >= V)
             return;
-    double *mp = malloc(sizeof(double) * (size_t)(g + 1));
-    double *Sp = malloc(sizeof(double) * (size_t)(g + 1));
+    double *mp = st, *Sp = st + (g + 1);
     int bad = 0;
     for (int j = 0; j <= g && !bad; ++j)
         bad |= row_softmax_stats(J->target, dt, b * tblk + j * trow, V, T, &mp[j], &Sp[j]);
     if (bad)
-        goto done;
+        return;
 
     /* Tests: r_i = p_i(x_i). */
     double margin = INFINITY;
@@ -470,19 +481,6 @@ static void pointmass_block(const chain_job *J, int b, double *w)
     if (J->final_dist)
         for (int v = 0; v < V; ++v)
             J->final_dist[(int64_t)b * V + v] = w[v] / W;
-done:
-    free(mp);
-    free(Sp);
-}
-
-static void *pointmass_worker(void *p)
-{
-    const chain_arg *a = (const chain_arg *)p;
-    const chain_job *J = a->J;
-    double *w = J->work + (int64_t)a->tid * J->V;
-    for (int b = a->tid; b < J->B; b += J->nthreads)
-        pointmass_block(J, b, w);
-    return NULL;
 }
 
 /* Point-mass chain verification over B blocks: target [B][gamma+1][V],
@@ -500,27 +498,8 @@ int oracle_chain_pointmass_du(const void *target, int dtype, const int32_t *draf
     if (dtype != ORC_F32 && dtype != ORC_BF16)
         return -1;
     chain_job J = {target, NULL, dtype, draft_tokens, uniforms, B, gamma, V, T, accept_len,
-                   out_tokens, final_dist, margin, ratios, fallback, NULL, nthreads};
-    int nt = J.nthreads < 1 ? 1 : J.nthreads;
-    if (nt > B)
-        nt = B;
-    J.nthreads = nt;
-    J.work = malloc(sizeof(double) * (size_t)nt * (size_t)V);
-    if (!J.work)
-        return -2;
-    pthread_t *th = malloc(sizeof(pthread_t) * (size_t)nt);
-    chain_arg *args = malloc(sizeof(chain_arg) * (size_t)nt);
-    for (int i = 0; i < nt; ++i) {
-        args[i].J = &J;
-        args[i].tid = i;
-        pthread_create(&th[i], NULL, pointmass_worker, &args[i]);
-    }
-    for (int i = 0; i < nt; ++i)
-        pthread_join(th[i], NULL);
-    free(th);
-    free(args);
-    free(J.work);
-    return 0;
+                   out_tokens, final_dist, margin, ratios, fallback, NULL, NULL, nthreads};
+    return run_chain(&J, pointmass_block);
 }
 
 /* The same with the float32 uniforms of the library interface. */
@@ -565,9 +544,9 @@ static int outcome_cmp(const void *x, const void *y)
 
 /* Outcome scores and cache selection for R requests ([J++] Section 4.2,
  * "Outcome Selection"; Appendix F.1 and Proposition 1).  Row j of a request
- * (j = 0..gamma) is the decoder's estimate of the target's next-token
- * distribution after the block's first j draft tokens, taken as a softmax at
- * temperature T.  With p_j(x_j) the probability row j gives draft token x_j:
+ * (j = 0..gamma) holds logits that stand for the target's distribution of the
+ * token following the anchor and draft tokens x_0..x_{j-1}; its softmax at
+ * temperature T is p_j.  With p_j(x_j) the probability row j gives draft token x_j:
  *   P(k, a) = prod_{i<k} p_i(x_i) * p_k(a)   for k < gamma and a != x_k,
  *   P(gamma, a) = prod_{i<gamma} p_i(x_i) * p_gamma(a),
  * the probability that verification of the block ends with k accepted tokens
@@ -575,8 +554,8 @@ static int outcome_cmp(const void *x, const void *y)
  * (ties: smaller k, then smaller a; outcomes of probability 0 are never
  * kept, their slots hold k = a = -1 and probability 0); the hit probability
  * is the sum of the kept probabilities.  An invalid request (a token outside
- * [0, V), a NaN or +inf logit, a row without a finite logit, the |m|/T
- * domain) gets k = a = -1 everywhere and hit probability -1.  all_scores
+ * [0, V), a NaN or +inf logit, a row without a finite logit) gets
+ * k = a = -1 everywhere and hit probability -1.  all_scores
  * (nullable, [R][gamma+1][V]) receives every P(k, a), 0 where a = x_k. */
 int oracle_outcome_topk(const void *logits, int dtype, const int32_t *draft_tokens, int R,
                         int gamma, int V, double T, int ncache, int32_t *out_k, int32_t *out_a,
@@ -593,8 +572,12 @@ int oracle_outcome_topk(const void *logits, int dtype, const int32_t *draft_toke
     outcome *cand = malloc(sizeof(outcome) * (size_t)n);
     double *m = malloc(sizeof(double) * (size_t)rows);
     double *S = malloc(sizeof(double) * (size_t)rows);
-    if (!cand || !m || !S)
+    if (!cand || !m || !S) {
+        free(cand);
+        free(m);
+        free(S);
         return -2;
+    }
     for (int r = 0; r < R; ++r) {
         const int32_t *x = draft_tokens + (int64_t)r * gamma;
         const int64_t base = (int64_t)r * n;
@@ -685,12 +668,13 @@ typedef struct {
     const int32_t *parents, *tokens;
     int B, n, V;
     int32_t *accept_len, *accept_node, *out_tokens, *amax_out;
+    int32_t *scratch; /* [nthreads][3 n] */
     int nthreads;
 } tree_job;
 
 /* Greedy tree verification of one request ([JN] "Tree verification",
  * Fig. 5 and the greedy note; Eq. 17 for the accepted length). */
-static void tree_request(const tree_job *J, int b)
+static void tree_request(const tree_job *J, int b, int32_t *scratch)
 {
     const int n = J->n, V = J->V;
     const int32_t *par = J->parents + (int64_t)b * n;
@@ -713,9 +697,7 @@ static void tree_request(const tree_job *J, int b)
             return;
 
     /* Target argmax of every node row, lowest token id on ties. */
-    int32_t *amax = malloc(sizeof(int32_t) * (size_t)n);
-    int32_t *acc = malloc(sizeof(int32_t) * (size_t)n);
-    int32_t *depth = malloc(sizeof(int32_t) * (size_t)n);
+    int32_t *amax = scratch, *acc = scratch + n, *depth = scratch + 2 * n;
     for (int j = 0; j < n; ++j) {
         int64_t off = ((int64_t)b * n + j) * V;
         double best = -INFINITY;
@@ -723,14 +705,14 @@ static void tree_request(const tree_job *J, int b)
         for (int v = 0; v < V; ++v) {
             double z = logit_at(J->target, J->dtype, off + v);
             if (isnan(z) || z == INFINITY)
-                goto done;
+                return;
             if (z > best) {
                 best = z;
                 arg = v;
             }
         }
         if (arg < 0)
-            goto done; /* no finite logit in this row */
+            return; /* no finite logit in this row */
         amax[j] = arg;
     }
     if (J->amax_out)
@@ -757,10 +739,6 @@ static void tree_request(const tree_job *J, int b)
     out[depth[best]] = amax[best];
     J->accept_len[b] = depth[best];
     J->accept_node[b] = best;
-done:
-    free(amax);
-    free(acc);
-    free(depth);
 }
 
 typedef struct {
@@ -771,8 +749,9 @@ typedef struct {
 static void *tree_worker(void *p)
 {
     const tree_arg *a = (const tree_arg *)p;
+    int32_t *scratch = a->J->scratch + (int64_t)a->tid * 3 * a->J->n;
     for (int b = a->tid; b < a->J->B; b += a->J->nthreads)
-        tree_request(a->J, b);
+        tree_request(a->J, b, scratch);
     return NULL;
 }
 
@@ -786,25 +765,23 @@ int oracle_tree_greedy(const void *target, int dtype, const int32_t *parents,
     if (B < 1 || n < 1 || V < 1 || (dtype != ORC_F32 && dtype != ORC_BF16))
         return -1;
     tree_job J = {target, dtype, parents, tokens, B, n, V, accept_len, accept_node, out_tokens,
-                  amax_out, nthreads < 1 ? 1 : nthreads};
+                  amax_out, NULL, nthreads < 1 ? 1 : nthreads};
     if (J.nthreads > B)
         J.nthreads = B;
-    if (J.nthreads == 1) {
-        tree_arg a = {&J, 0};
-        tree_worker(&a);
-        return 0;
-    }
-    pthread_t *th = malloc(sizeof(pthread_t) * (size_t)J.nthreads);
+    J.scratch = malloc(sizeof(int32_t) * 3 * (size_t)n * (size_t)J.nthreads);
     tree_arg *args = malloc(sizeof(tree_arg) * (size_t)J.nthreads);
+    if (!J.scratch || !args) {
+        free(J.scratch);
+        free(args);
+        return -2;
+    }
     for (int i = 0; i < J.nthreads; ++i) {
         args[i].J = &J;
         args[i].tid = i;
-        pthread_create(&th[i], NULL, tree_worker, &args[i]);
     }
-    for (int i = 0; i < J.nthreads; ++i)
-        pthread_join(th[i], NULL);
-    free(th);
+    run_parallel(tree_worker, args, sizeof(tree_arg), J.nthreads);
     free(args);
+    free(J.scratch);
     return 0;
 }
 
@@ -836,8 +813,8 @@ int oracle_tree_greedy(const void *target, int dtype, const int32_t *parents,
  * Outputs per request ([R][budget]): parents (root -1), tokens (root -1),
  * node_row (-1 for none), score (natural log; -inf past the end), and
  * n_nodes [R]; past the end parents, tokens and node_row are -1.  An invalid
- * request (a NaN or +inf logit, a row without a finite logit, or the |m|/T
- * domain, in any of its M rows) gets n_nodes = -1 and every node output
+ * request (a NaN or +inf logit, or a row without a finite logit, in any of
+ * its M rows) gets n_nodes = -1 and every node output
  * -1 / -inf; a child_row entry outside [-1, M) makes every request invalid.
  * min_gap (nullable, [R]) receives, over the pops that expand a node, the
  * smallest difference between the popped score and the score of any other
@@ -865,8 +842,15 @@ int oracle_tree_build(const void *logits, int dtype, int R, int M, int V, double
     char *inq = malloc((size_t)budget);
     int *ctok = malloc(sizeof(int) * (size_t)W);
     char *taken = malloc((size_t)V);
-    if (!m || !S || !depth || !inq || !ctok || !taken)
+    if (!m || !S || !depth || !inq || !ctok || !taken) {
+        free(m);
+        free(S);
+        free(depth);
+        free(inq);
+        free(ctok);
+        free(taken);
         return -2;
+    }
     for (int r = 0; r < R; ++r) {
         const int64_t o = (int64_t)r * budget;
         int32_t *par = parents + o, *tok = tokens + o, *row = node_row + o;
@@ -954,6 +938,55 @@ int oracle_tree_build(const void *logits, int dtype, int R, int M, int V, double
     return 0;
 }
 
+/* Scores of a given tree under the draft rows ([JN] Eq. 15: a node's score
+ * is the sum of the draft log probabilities ln q(token) along its path, each
+ * token taken in the row of its parent).  For each request r with
+ * n = n_nodes[r] nodes (parents[r][0] = -1, 0 <= parents[r][j] < j, every
+ * parent with a child having a row in [0, M), tokens in [0, V)): score[r][0]
+ * = 0 and score[r][j] = score[r][parents[j]] + ln q_{row(parents[j])}(
+ * tokens[j]); -inf past the last node.  A request whose tree breaks those
+ * conditions, or one with a NaN, +inf or all -inf row among the rows it uses,
+ * gets NaN scores.  (Tests use it to score a tree built elsewhere.) */
+int oracle_tree_score(const void *logits, int dtype, int R, int M, int V, double T, int budget,
+                      const int32_t *parents, const int32_t *tokens, const int32_t *node_row,
+                      const int32_t *n_nodes, double *score)
+{
+    if (!logits || !parents || !tokens || !node_row || !n_nodes || !score)
+        return -1;
+    if (R < 1 || M < 1 || V < 1 || budget < 1 || !(T > 0.0) || !isfinite(T))
+        return -1;
+    if (dtype != ORC_F32 && dtype != ORC_BF16)
+        return -1;
+    for (int r = 0; r < R; ++r) {
+        const int64_t o = (int64_t)r * budget;
+        const int32_t *par = parents + o, *tok = tokens + o, *row = node_row + o;
+        double *sc = score + o;
+        const int n = n_nodes[r];
+        for (int j = 0; j < budget; ++j)
+            sc[j] = -INFINITY;
+        int bad = n < 1 || n > budget || par[0] != -1;
+        for (int j = 1; j < n && !bad; ++j)
+            bad |= par[j] < 0 || par[j] >= j || tok[j] < 0 || tok[j] >= V ||
+                   row[par[j]] < 0 || row[par[j]] >= M;
+        if (!bad) {
+            sc[0] = 0.0;
+            for (int j = 1; j < n && !bad; ++j) {
+                const int64_t off = ((int64_t)r * M + row[par[j]]) * V;
+                double m, S;
+                if (row_softmax_stats(logits, dtype, off, V, T, &m, &S)) {
+                    bad = 1;
+                    break;
+                }
+                sc[j] = sc[par[j]] + logprob_at(logits, dtype, off, tok[j], T, m, S);
+            }
+        }
+        if (bad)
+            for (int j = 0; j < budget; ++j)
+                sc[j] = NAN;
+    }
+    return 0;
+}
+
 /* ----------------------------------------------------------------------
  * Stochastic tree verification ([JN] section "Tree verification", Eq. 16-17
  * and Fig. 5).
@@ -983,16 +1016,20 @@ int oracle_tree_build(const void *logits, int dtype, int R, int M, int V, double
  * excluded), the drawn token, then -1.  final_dist (nullable, [B][V])
  * receives p_{v*}; margin (nullable, [B]) the smallest |u_j - alpha_j| over
  * the nodes whose parent is accepted, and the draw's distance to the nearest
- * CDF breakpoint relative to W.  An invalid request (a malformed parent
- * array, a token outside [0, V), a NaN or +inf logit or a row without a
- * finite logit in any target or draft row, or the |m|/T domain) gets
- * accept_len = accept_node = -1 and all tokens -1.
+ * CDF breakpoint relative to W; alpha (nullable, [B][n]) every node's test
+ * probability alpha_j (NaN for the root and for an invalid request).  An
+ * invalid request (a malformed parent array, a token outside [0, V), a NaN
+ * or +inf logit or a row without a finite logit in any target or draft row)
+ * gets accept_len = accept_node = -1 and all tokens -1.
+ * oracle_tree_stochastic_du takes double uniforms (the exact-enumeration
+ * tests drive it with continuous u); oracle_tree_stochastic takes the
+ * float32 uniforms of the library interface, each widened exactly.
  */
-int oracle_tree_stochastic(const void *target, const void *draft, int dtype,
-                           const int32_t *parents, const int32_t *tokens, const float *uniforms,
-                           int B, int n, int V, double T, int32_t *accept_len,
-                           int32_t *accept_node, int32_t *out_tokens, double *final_dist,
-                           double *margin)
+int oracle_tree_stochastic_du(const void *target, const void *draft, int dtype,
+                              const int32_t *parents, const int32_t *tokens,
+                              const double *uniforms, int B, int n, int V, double T,
+                              int32_t *accept_len, int32_t *accept_node, int32_t *out_tokens,
+                              double *final_dist, double *margin, double *alpha_out)
 {
     if (!target || !draft || !parents || !tokens || !uniforms || !accept_len || !accept_node ||
         !out_tokens)
@@ -1005,11 +1042,14 @@ int oracle_tree_stochastic(const void *target, const void *draft, int dtype,
     double *mq = malloc(sizeof(double) * (size_t)n), *Sq = malloc(sizeof(double) * (size_t)n);
     int *acc = malloc(sizeof(int) * (size_t)n), *depth = malloc(sizeof(int) * (size_t)n);
     double *w = malloc(sizeof(double) * (size_t)V);
-    if (!mp || !Sp || !mq || !Sq || !acc || !depth || !w)
-        return -2;
+    int rc = 0;
+    if (!mp || !Sp || !mq || !Sq || !acc || !depth || !w) {
+        rc = -2;
+        goto out;
+    }
     for (int b = 0; b < B; ++b) {
         const int32_t *par = parents + (int64_t)b * n, *tok = tokens + (int64_t)b * n;
-        const float *u = uniforms + (int64_t)b * n;
+        const double *u = uniforms + (int64_t)b * n;
         int32_t *out = out_tokens + (int64_t)b * n;
         const int64_t base = (int64_t)b * n * V;
         for (int j = 0; j < n; ++j)
@@ -1017,6 +1057,9 @@ int oracle_tree_stochastic(const void *target, const void *draft, int dtype,
         accept_len[b] = accept_node[b] = -1;
         if (margin)
             margin[b] = 0.0;
+        if (alpha_out)
+            for (int j = 0; j < n; ++j)
+                alpha_out[(int64_t)b * n + j] = NAN;
         if (final_dist)
             for (int v = 0; v < V; ++v)
                 final_dist[(int64_t)b * V + v] = 0.0;
@@ -1045,11 +1088,12 @@ int oracle_tree_stochastic(const void *target, const void *draft, int dtype,
                 alpha = 1.0;
             else
                 alpha = fmin(1.0, exp(lp - lq));
-            const double uj = (double)u[j];
-            acc[j] = acc[p] && uj < alpha;
+            if (alpha_out)
+                alpha_out[(int64_t)b * n + j] = alpha;
+            acc[j] = acc[p] && u[j] < alpha;
             depth[j] = depth[p] + 1;
             if (acc[p])
-                mg = fmin(mg, fabs(uj - alpha));
+                mg = fmin(mg, fabs(u[j] - alpha));
         }
         int best = 0;
         for (int j = 1; j < n; ++j)
@@ -1062,7 +1106,7 @@ int oracle_tree_stochastic(const void *target, const void *draft, int dtype,
             w[v] = prob_at(target, dtype, prow, v, T, mp[best], Sp[best]);
             W += w[v];
         }
-        const double t = (double)u[0] * W;
+        const double t = u[0] * W;
         double C = 0.0, Cprev = 0.0;
         int drawn = -1;
         for (int v = 0; v < V; ++v) {
@@ -1095,6 +1139,7 @@ int oracle_tree_stochastic(const void *target, const void *draft, int dtype,
             for (int v = 0; v < V; ++v)
                 final_dist[(int64_t)b * V + v] = w[v] / W;
     }
+out:
     free(mp);
     free(Sp);
     free(mq);
@@ -1102,5 +1147,26 @@ int oracle_tree_stochastic(const void *target, const void *draft, int dtype,
     free(acc);
     free(depth);
     free(w);
-    return 0;
+    return rc;
+}
+
+int oracle_tree_stochastic(const void *target, const void *draft, int dtype,
+                           const int32_t *parents, const int32_t *tokens, const float *uniforms,
+                           int B, int n, int V, double T, int32_t *accept_len,
+                           int32_t *accept_node, int32_t *out_tokens, double *final_dist,
+                           double *margin, double *alpha_out)
+{
+    if (!uniforms || B < 1 || n < 1)
+        return -1;
+    const size_t nu = (size_t)B * (size_t)n;
+    double *ud = malloc(sizeof(double) * nu);
+    if (!ud)
+        return -2;
+    for (size_t i = 0; i < nu; ++i)
+        ud[i] = (double)uniforms[i];
+    const int rc = oracle_tree_stochastic_du(target, draft, dtype, parents, tokens, ud, B, n, V,
+                                             T, accept_len, accept_node, out_tokens, final_dist,
+                                             margin, alpha_out);
+    free(ud);
+    return rc;
 }

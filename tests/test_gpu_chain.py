@@ -20,7 +20,7 @@ def run_case(d, label, want_dist=True):
     g = gpu_chain(d, want_dist=want_dist)
     o = oracle.chain(d["target"], d["draft"], d["draft_tokens"], d["uniforms"], d["T"],
                      dtype=d["dtype"], want_dist=want_dist)
-    n, near = compare_chain(g, o, label)
+    n, near = compare_chain(g, o, label, d=d)
     print(f"[case] {label}: compared {n} blocks, {near} inside the boundary band", flush=True)
     return g, o
 
@@ -155,7 +155,7 @@ def test_large_logits():
     run_case(d, "pm1e4")
 
 
-@pytest.mark.parametrize("kind", ["nan", "posinf", "allneginf", "token_hi", "token_neg", "domain"])
+@pytest.mark.parametrize("kind", ["nan", "posinf", "allneginf", "token_hi", "token_neg"])
 def test_invalid_blocks(kind):
     d = synth.chain_inputs(4, 3, 1030, "f32", T=1.0, seed=12)
     if kind == "nan":
@@ -166,11 +166,29 @@ def test_invalid_blocks(kind):
         d["target"][1, 0, :] = -np.inf
     elif kind == "token_hi":
         d["draft_tokens"][1, 2] = 1030
-    elif kind == "token_neg":
-        d["draft_tokens"][1, 0] = -1
     else:
-        d["draft"][1, 1, 3] = 3.0e8
+        d["draft_tokens"][1, 0] = -1
     g, o = run_case(d, f"invalid-{kind}")
+    assert o["accept_len"][1] == -1
+    assert g["accept_len"][1] == -1 and (g["out_tokens"][1] == -1).all()
+    assert (g["accept_len"][[0, 2, 3]] >= 0).all()
+
+
+@pytest.mark.parametrize("how", ["logit", "temperature"])
+def test_outside_library_domain(how):
+    """The library restricts rows to |largest finite logit| / T <= 2^28 and
+    flags a block with a row beyond it -1.  The oracle evaluates such rows
+    (they are nearly one-hot in fp32, so it returns a real outcome), and the
+    comparison counts these blocks apart: they must be flagged, never
+    matched."""
+    if how == "logit":
+        d = synth.chain_inputs(4, 3, 1030, "f32", T=1.0, seed=12)
+        d["draft"][1, 1, 3] = 3.0e8
+    else:
+        d = synth.chain_inputs(4, 3, 1030, "f32", T=1e-6, seed=12)
+        d["target"][1, 2] += np.float32(300.0)
+    g, o = run_case(d, f"domain-{how}")
+    assert o["accept_len"][1] >= 0  # the oracle has no such restriction
     assert g["accept_len"][1] == -1 and (g["out_tokens"][1] == -1).all()
     assert (g["accept_len"][[0, 2, 3]] >= 0).all()
 
@@ -211,7 +229,7 @@ def test_repeated_calls_share_workspace():
     first = gpu_chain(d, workspace=ws)
     o = oracle.chain(d["target"], d["draft"], d["draft_tokens"], d["uniforms"], d["T"],
                      dtype=d["dtype"])
-    compare_chain(first, o, "reuse-first")
+    compare_chain(first, o, "reuse-first", d=d)
     for fill in (0x00, 0xFF, 0x7F):
         ws.fill_(fill)
         again = gpu_chain(d, workspace=ws)

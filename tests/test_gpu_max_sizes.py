@@ -60,7 +60,7 @@ def test_chain_at_the_largest_vocabulary():
     o = oracle.chain(d["target"], d["draft"], d["draft_tokens"], d["uniforms"], d["T"],
                      dtype="bf16")
     print(f"[case] max-V chain: oracle done at {time.time() - t0:.1f}s", flush=True)
-    n, near = compare_chain(res, o, "max-V chain", check_dist=False)
+    n, near = compare_chain(res, o, "max-V chain", check_dist=False, d=d)
     assert n == B and near == 0
     assert res["accept_len"].tolist() == [1, 0]
     assert res["out_tokens"].tolist() == [[x, V - 3], [V - 2, -1]]
@@ -105,7 +105,8 @@ def test_pointmass_at_the_largest_vocabulary():
     res = gpu_pointmass(d)
     o = oracle.chain_pointmass(d["target"], d["draft_tokens"], d["uniforms"], d["T"],
                                dtype="bf16")
-    n, near = compare_chain(res, o, "max-V point-mass", check_dist=False)
+    n, near = compare_chain(res, o, "max-V point-mass", check_dist=False, d=d,
+                               pointmass=True)
     assert n == B and near == 0
     assert res["accept_len"].tolist() == [1, 0]
     assert res["out_tokens"].tolist() == [[x, V - 3], [V - 2, -1]]

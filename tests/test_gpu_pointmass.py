@@ -22,7 +22,7 @@ def run_case(d, label, want_dist=True):
     g = gpu_pointmass(d, want_dist=want_dist)
     o = oracle.chain_pointmass(d["target"], d["draft_tokens"], d["uniforms"], d["T"],
                                dtype=d["dtype"], want_dist=want_dist)
-    n, near = compare_chain(g, o, label)
+    n, near = compare_chain(g, o, label, d=d, pointmass=True)
     print(f"[case] {label}: compared {n} blocks, {near} inside the boundary band", flush=True)
     return g, o
 
