@@ -75,30 +75,34 @@ def load_library():
     lib.spec_verify_chain_workspace_bytes.restype = SZ
     lib.spec_verify_tree_greedy_workspace_bytes.argtypes = [I32, I32, I32, I32]
     lib.spec_verify_tree_greedy_workspace_bytes.restype = SZ
-    lib.spec_verify_chain.argtypes = [P, P, I32, P, P, I32, I32, I32, D, P, P, P, P, SZ, P, P]
-    lib.spec_verify_chain.restype = I32
+    chain_args = [P, P, I32, P, P, I32, I32, I32, D, P, P, P, P, SZ, P]
     lib.spec_verify_chain_pointmass_workspace_bytes.argtypes = [I32, I32, I32, I32]
     lib.spec_verify_chain_pointmass_workspace_bytes.restype = SZ
-    lib.spec_verify_chain_pointmass.argtypes = [P, I32, P, P, I32, I32, I32, D, P, P, P, P, SZ, P, P]
-    lib.spec_verify_chain_pointmass.restype = I32
+    pointmass_args = [P, I32, P, P, I32, I32, I32, D, P, P, P, P, SZ, P]
     lib.spec_outcome_topk_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
     lib.spec_outcome_topk_workspace_bytes.restype = SZ
-    lib.spec_outcome_topk.argtypes = [P, I32, P, I32, I32, I32, D, I32, P, P, P, P, P, SZ, P, P]
-    lib.spec_outcome_topk.restype = I32
-    lib.spec_verify_tree_greedy.argtypes = [P, I32, P, P, I32, I32, I32, P, P, P, P, SZ, P, P]
-    lib.spec_verify_tree_greedy.restype = I32
+    outcome_args = [P, I32, P, I32, I32, I32, D, I32, P, P, P, P, P, SZ, P]
+    greedy_args = [P, I32, P, P, I32, I32, I32, P, P, P, P, SZ, P]
     lib.spec_verify_tree_stochastic_workspace_bytes.argtypes = [I32, I32, I32, I32]
     lib.spec_verify_tree_stochastic_workspace_bytes.restype = SZ
-    lib.spec_verify_tree_stochastic.argtypes = [P, P, I32, P, P, P, I32, I32, I32, D, P, P, P, P,
-                                                P, SZ, P, P]
-    lib.spec_verify_tree_stochastic.restype = I32
+    stochastic_args = [P, P, I32, P, P, P, I32, I32, I32, D, P, P, P, P, P, SZ, P]
     lib.spec_cache_lookup.argtypes = [P, P, I32, I32, P, P, I32, P, P]
     lib.spec_cache_lookup.restype = I32
     lib.spec_tree_build_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
     lib.spec_tree_build_workspace_bytes.restype = SZ
-    lib.spec_tree_build.argtypes = [P, I32, P, I32, I32, I32, D, I32, I32, I32, P, P, P, P, P, P,
-                                    SZ, P, P]
-    lib.spec_tree_build.restype = I32
+    build_args = [P, I32, P, I32, I32, I32, D, I32, I32, I32, P, P, P, P, P, P, SZ, P]
+    # the product entry points, and their instrumented twins (one more
+    # argument: the hipEvent_t array the benchmark times kernels with)
+    for name, args in (("spec_verify_chain", chain_args),
+                       ("spec_verify_chain_pointmass", pointmass_args),
+                       ("spec_outcome_topk", outcome_args),
+                       ("spec_verify_tree_greedy", greedy_args),
+                       ("spec_verify_tree_stochastic", stochastic_args),
+                       ("spec_tree_build", build_args)):
+        for fn, extra in ((name, []), (name + "_timed", [P])):
+            f = getattr(lib, fn)
+            f.argtypes = args + extra
+            f.restype = I32
     _lib = lib
     return lib
 
@@ -166,6 +170,10 @@ def _ptr(t):
     return None if t is None else _ct.c_void_p(t.data_ptr())
 
 
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
 def _new(shape, dtype, device, stream):
     """torch.empty for a tensor the library writes on `stream`.  A tensor
     allocated while another stream is current is marked as used on `stream`,
@@ -186,11 +194,14 @@ def _stream_handle(stream, device):
     return _ct.c_void_p(stream.cuda_stream)
 
 
-def _events(phase_events):
+def _invoke(lib, name, phase_events, *args):
+    """Calls the entry point `name`, or, when phase_events (a sequence of
+    hipEvent_t handles) is given, its instrumented twin `name`_timed, which
+    records them around the dominant kernel (benchmark timing only)."""
     if phase_events is None:
-        return None
+        return getattr(lib, name)(*args)
     arr = (_ct.c_void_p * len(phase_events))(*[_ct.c_void_p(int(e)) for e in phase_events])
-    return _ct.cast(arr, _ct.c_void_p), arr
+    return getattr(lib, name + "_timed")(*args, _ct.cast(arr, _ct.c_void_p))
 
 
 _ws_cache: dict = {}
@@ -249,12 +260,9 @@ def spec_verify_chain(target, draft, draft_tokens, uniforms, temperature, *, acc
         raise SpecVerifyError(2, "spec_verify_chain")
     if workspace is None:
         workspace = _workspace(need, dev, stream)
-    ev = _events(phase_events)
-    st = lib.spec_verify_chain(_ptr(target), _ptr(draft), code, _ptr(draft_tokens),
-                               _ptr(uniforms), B, g, V, float(temperature), _ptr(accept_len),
-                               _ptr(out_tokens), _ptr(final_dist), _ptr(workspace),
-                               workspace.numel() * workspace.element_size(),
-                               _stream_handle(stream, dev), None if ev is None else ev[0])
+    st = _invoke(lib, "spec_verify_chain", phase_events, _ptr(target), _ptr(draft), code,
+                 _ptr(draft_tokens), _ptr(uniforms), B, g, V, float(temperature), _ptr(accept_len),
+                 _ptr(out_tokens), _ptr(final_dist), _ptr(workspace), _nbytes(workspace), _stream_handle(stream, dev))
     if st != 0:
         raise SpecVerifyError(st, "spec_verify_chain")
     return accept_len, out_tokens, final_dist
@@ -294,13 +302,9 @@ def spec_verify_chain_pointmass(target, draft_tokens, uniforms, temperature, *, 
         raise SpecVerifyError(2, "spec_verify_chain_pointmass")
     if workspace is None:
         workspace = _workspace(need, dev, stream)
-    ev = _events(phase_events)
-    st = lib.spec_verify_chain_pointmass(_ptr(target), code, _ptr(draft_tokens), _ptr(uniforms),
-                                         B, g, V, float(temperature), _ptr(accept_len),
-                                         _ptr(out_tokens), _ptr(final_dist), _ptr(workspace),
-                                         workspace.numel() * workspace.element_size(),
-                                         _stream_handle(stream, dev),
-                                         None if ev is None else ev[0])
+    st = _invoke(lib, "spec_verify_chain_pointmass", phase_events, _ptr(target), code,
+                 _ptr(draft_tokens), _ptr(uniforms), B, g, V, float(temperature), _ptr(accept_len),
+                 _ptr(out_tokens), _ptr(final_dist), _ptr(workspace), _nbytes(workspace), _stream_handle(stream, dev))
     if st != 0:
         raise SpecVerifyError(st, "spec_verify_chain_pointmass")
     return accept_len, out_tokens, final_dist
@@ -341,11 +345,10 @@ def spec_outcome_topk(logits, draft_tokens, temperature, ncache, *, out_k=None, 
         raise SpecVerifyError(2, "spec_outcome_topk")
     if workspace is None:
         workspace = _workspace(need, dev, stream)
-    ev = _events(phase_events)
-    st = lib.spec_outcome_topk(_ptr(logits), code, _ptr(draft_tokens), R, g, V, float(temperature),
-                               ncache, _ptr(out_k), _ptr(out_a), _ptr(out_p), _ptr(hit),
-                               _ptr(workspace), workspace.numel() * workspace.element_size(),
-                               _stream_handle(stream, dev), None if ev is None else ev[0])
+    st = _invoke(lib, "spec_outcome_topk", phase_events, _ptr(logits), code, _ptr(draft_tokens), R,
+                 g, V, float(temperature), ncache, _ptr(out_k), _ptr(out_a), _ptr(out_p),
+                 _ptr(hit), _ptr(workspace), _nbytes(workspace),
+                 _stream_handle(stream, dev))
     if st != 0:
         raise SpecVerifyError(st, "spec_outcome_topk")
     return out_k, out_a, out_p, hit
@@ -391,13 +394,11 @@ def spec_verify_tree_stochastic(target_logits, draft_logits, parents, tokens, un
         raise SpecVerifyError(2, "spec_verify_tree_stochastic")
     if workspace is None:
         workspace = _workspace(need, dev, stream)
-    ev = _events(phase_events)
-    st = lib.spec_verify_tree_stochastic(
-        _ptr(target_logits), _ptr(draft_logits), code, _ptr(parents), _ptr(tokens),
-        _ptr(uniforms), B, n, V, float(temperature), _ptr(accept_len), _ptr(accept_node),
-        _ptr(out_tokens), _ptr(final_dist), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream_handle(stream, dev),
-        None if ev is None else ev[0])
+    st = _invoke(lib, "spec_verify_tree_stochastic", phase_events, _ptr(target_logits),
+                 _ptr(draft_logits), code, _ptr(parents), _ptr(tokens), _ptr(uniforms), B, n, V,
+                 float(temperature), _ptr(accept_len), _ptr(accept_node), _ptr(out_tokens),
+                 _ptr(final_dist), _ptr(workspace), _nbytes(workspace),
+                 _stream_handle(stream, dev))
     if st != 0:
         raise SpecVerifyError(st, "spec_verify_tree_stochastic")
     return accept_len, accept_node, out_tokens, final_dist
@@ -439,12 +440,10 @@ def spec_tree_build(draft_logits, temperature, width, max_depth, budget, *, chil
         raise SpecVerifyError(2, "spec_tree_build")
     if workspace is None:
         workspace = _workspace(need, dev, stream)
-    ev = _events(phase_events)
-    st = lib.spec_tree_build(_ptr(draft_logits), code, _ptr(child_row), R, M, V, float(temperature),
-                             W, int(max_depth), budget, _ptr(parents), _ptr(tokens), _ptr(node_row),
-                             _ptr(score), _ptr(n_nodes), _ptr(workspace),
-                             workspace.numel() * workspace.element_size(),
-                             _stream_handle(stream, dev), None if ev is None else ev[0])
+    st = _invoke(lib, "spec_tree_build", phase_events, _ptr(draft_logits), code, _ptr(child_row),
+                 R, M, V, float(temperature), W, int(max_depth), budget, _ptr(parents),
+                 _ptr(tokens), _ptr(node_row), _ptr(score), _ptr(n_nodes), _ptr(workspace),
+                 _nbytes(workspace), _stream_handle(stream, dev))
     if st != 0:
         raise SpecVerifyError(st, "spec_tree_build")
     return parents, tokens, node_row, score, n_nodes
@@ -506,11 +505,10 @@ def spec_verify_tree_greedy(target, parents, tokens, *, accept_len=None, accept_
         raise SpecVerifyError(2, "spec_verify_tree_greedy")
     if workspace is None:
         workspace = _workspace(need, dev, stream)
-    ev = _events(phase_events)
-    st = lib.spec_verify_tree_greedy(_ptr(target), code, _ptr(parents), _ptr(tokens), B, n, V,
-                                     _ptr(accept_len), _ptr(accept_node), _ptr(out_tokens),
-                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                     _stream_handle(stream, dev), None if ev is None else ev[0])
+    st = _invoke(lib, "spec_verify_tree_greedy", phase_events, _ptr(target), code, _ptr(parents),
+                 _ptr(tokens), B, n, V, _ptr(accept_len), _ptr(accept_node), _ptr(out_tokens),
+                 _ptr(workspace), _nbytes(workspace),
+                 _stream_handle(stream, dev))
     if st != 0:
         raise SpecVerifyError(st, "spec_verify_tree_greedy")
     return accept_len, accept_node, out_tokens

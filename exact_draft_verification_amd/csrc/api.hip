@@ -8,6 +8,7 @@
 #include <cstring>
 
 #include "spec_verify.h"
+#include "spec_verify_timing.h"
 #include "sv_kernels.hpp"
 
 namespace sv {
@@ -321,8 +322,19 @@ extern "C" int32_t spec_verify_chain(const void* target_logits, const void* draf
                                      const float* uniforms, int32_t B, int32_t gamma, int32_t V,
                                      double temperature, int32_t* accept_len,
                                      int32_t* out_tokens, float* final_dist, void* workspace,
-                                     size_t workspace_bytes, void* stream,
-                                     void* const* phase_events) {
+                                     size_t workspace_bytes, void* stream) {
+    return chain_call(target_logits, draft_logits, false, dtype, draft_tokens, uniforms, B, gamma,
+                      V, temperature, accept_len, out_tokens, final_dist, workspace,
+                      workspace_bytes, stream, nullptr);
+}
+
+extern "C" int32_t spec_verify_chain_timed(const void* target_logits, const void* draft_logits,
+                                           int32_t dtype, const int32_t* draft_tokens,
+                                           const float* uniforms, int32_t B, int32_t gamma,
+                                           int32_t V, double temperature, int32_t* accept_len,
+                                           int32_t* out_tokens, float* final_dist,
+                                           void* workspace, size_t workspace_bytes, void* stream,
+                                           void* const* phase_events) {
     return chain_call(target_logits, draft_logits, false, dtype, draft_tokens, uniforms, B, gamma,
                       V, temperature, accept_len, out_tokens, final_dist, workspace,
                       workspace_bytes, stream, phase_events);
@@ -334,8 +346,17 @@ extern "C" int32_t spec_verify_chain_pointmass(const void* target_logits, int32_
                                                int32_t V, double temperature,
                                                int32_t* accept_len, int32_t* out_tokens,
                                                float* final_dist, void* workspace,
-                                               size_t workspace_bytes, void* stream,
-                                               void* const* phase_events) {
+                                               size_t workspace_bytes, void* stream) {
+    return chain_call(target_logits, nullptr, true, dtype, draft_tokens, uniforms, B, gamma, V,
+                      temperature, accept_len, out_tokens, final_dist, workspace,
+                      workspace_bytes, stream, nullptr);
+}
+
+extern "C" int32_t spec_verify_chain_pointmass_timed(
+    const void* target_logits, int32_t dtype, const int32_t* draft_tokens, const float* uniforms,
+    int32_t B, int32_t gamma, int32_t V, double temperature, int32_t* accept_len,
+    int32_t* out_tokens, float* final_dist, void* workspace, size_t workspace_bytes, void* stream,
+    void* const* phase_events) {
     return chain_call(target_logits, nullptr, true, dtype, draft_tokens, uniforms, B, gamma, V,
                       temperature, accept_len, out_tokens, final_dist, workspace,
                       workspace_bytes, stream, phase_events);
@@ -347,12 +368,11 @@ extern "C" size_t spec_outcome_topk_workspace_bytes(int32_t R, int32_t gamma, in
     return outcome_plan(R, gamma, V, dtype, ncache, &p) == SV_OK ? p.bytes : 0;
 }
 
-extern "C" int32_t spec_outcome_topk(const void* logits, int32_t dtype,
-                                     const int32_t* draft_tokens, int32_t R, int32_t gamma,
-                                     int32_t V, double temperature, int32_t ncache,
-                                     int32_t* out_k, int32_t* out_a, double* out_p, double* hit,
-                                     void* workspace, size_t workspace_bytes, void* stream,
-                                     void* const* phase_events) {
+static int32_t outcome_topk_call(const void* logits, int32_t dtype, const int32_t* draft_tokens,
+                                 int32_t R, int32_t gamma, int32_t V, double temperature,
+                                 int32_t ncache, int32_t* out_k, int32_t* out_a, double* out_p,
+                                 double* hit, void* workspace, size_t workspace_bytes,
+                                 void* stream, void* const* phase_events) {
     OutcomePlan p;
     int32_t st = outcome_plan(R, gamma, V, dtype, ncache, &p);
     if (st != SV_OK) return st;
@@ -398,19 +418,37 @@ extern "C" int32_t spec_outcome_topk(const void* logits, int32_t dtype,
     return SV_OK;
 }
 
+extern "C" int32_t spec_outcome_topk(const void* logits, int32_t dtype,
+                                     const int32_t* draft_tokens, int32_t R, int32_t gamma,
+                                     int32_t V, double temperature, int32_t ncache,
+                                     int32_t* out_k, int32_t* out_a, double* out_p, double* hit,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+    return outcome_topk_call(logits, dtype, draft_tokens, R, gamma, V, temperature, ncache, out_k,
+                             out_a, out_p, hit, workspace, workspace_bytes, stream, nullptr);
+}
+
+extern "C" int32_t spec_outcome_topk_timed(const void* logits, int32_t dtype,
+                                           const int32_t* draft_tokens, int32_t R, int32_t gamma,
+                                           int32_t V, double temperature, int32_t ncache,
+                                           int32_t* out_k, int32_t* out_a, double* out_p,
+                                           double* hit, void* workspace, size_t workspace_bytes,
+                                           void* stream, void* const* phase_events) {
+    return outcome_topk_call(logits, dtype, draft_tokens, R, gamma, V, temperature, ncache, out_k,
+                             out_a, out_p, hit, workspace, workspace_bytes, stream, phase_events);
+}
+
 extern "C" size_t spec_tree_build_workspace_bytes(int32_t R, int32_t M, int32_t V, int32_t dtype,
                                                   int32_t W, int32_t max_depth, int32_t budget) {
     TreeBuildPlan p;
     return tree_build_plan(R, M, V, dtype, W, max_depth, budget, &p) == SV_OK ? p.bytes : 0;
 }
 
-extern "C" int32_t spec_tree_build(const void* draft_logits, int32_t dtype,
-                                   const int32_t* child_row, int32_t R, int32_t M, int32_t V,
-                                   double temperature, int32_t W, int32_t max_depth,
-                                   int32_t budget, int32_t* parents, int32_t* tokens,
-                                   int32_t* node_row, double* score, int32_t* n_nodes,
-                                   void* workspace, size_t workspace_bytes, void* stream,
-                                   void* const* phase_events) {
+static int32_t tree_build_call(const void* draft_logits, int32_t dtype, const int32_t* child_row,
+                               int32_t R, int32_t M, int32_t V, double temperature, int32_t W,
+                               int32_t max_depth, int32_t budget, int32_t* parents,
+                               int32_t* tokens, int32_t* node_row, double* score,
+                               int32_t* n_nodes, void* workspace, size_t workspace_bytes,
+                               void* stream, void* const* phase_events) {
     TreeBuildPlan p;
     int32_t st = tree_build_plan(R, M, V, dtype, W, max_depth, budget, &p);
     if (st != SV_OK) return st;
@@ -465,13 +503,36 @@ extern "C" int32_t spec_tree_build(const void* draft_logits, int32_t dtype,
     return SV_OK;
 }
 
+extern "C" int32_t spec_tree_build(const void* draft_logits, int32_t dtype,
+                                   const int32_t* child_row, int32_t R, int32_t M, int32_t V,
+                                   double temperature, int32_t W, int32_t max_depth,
+                                   int32_t budget, int32_t* parents, int32_t* tokens,
+                                   int32_t* node_row, double* score, int32_t* n_nodes,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+    return tree_build_call(draft_logits, dtype, child_row, R, M, V, temperature, W, max_depth,
+                           budget, parents, tokens, node_row, score, n_nodes, workspace,
+                           workspace_bytes, stream, nullptr);
+}
+
+extern "C" int32_t spec_tree_build_timed(const void* draft_logits, int32_t dtype,
+                                         const int32_t* child_row, int32_t R, int32_t M, int32_t V,
+                                         double temperature, int32_t W, int32_t max_depth,
+                                         int32_t budget, int32_t* parents, int32_t* tokens,
+                                         int32_t* node_row, double* score, int32_t* n_nodes,
+                                         void* workspace, size_t workspace_bytes, void* stream,
+                                         void* const* phase_events) {
+    return tree_build_call(draft_logits, dtype, child_row, R, M, V, temperature, W, max_depth,
+                           budget, parents, tokens, node_row, score, n_nodes, workspace,
+                           workspace_bytes, stream, phase_events);
+}
+
 extern "C" size_t spec_verify_tree_stochastic_workspace_bytes(int32_t B, int32_t n, int32_t V,
                                                               int32_t dtype) {
     ChainPlan p;
     return tree_stoch_plan(B, n, V, dtype, &p) == SV_OK ? p.bytes : 0;
 }
 
-extern "C" int32_t spec_verify_tree_stochastic(
+static int32_t tree_stochastic_call(
     const void* target_logits, const void* draft_logits, int32_t dtype, const int32_t* parents,
     const int32_t* tokens, const float* uniforms, int32_t B, int32_t n, int32_t V,
     double temperature, int32_t* accept_len, int32_t* accept_node, int32_t* out_tokens,
@@ -544,6 +605,27 @@ extern "C" int32_t spec_verify_tree_stochastic(
     return SV_OK;
 }
 
+extern "C" int32_t spec_verify_tree_stochastic(
+    const void* target_logits, const void* draft_logits, int32_t dtype, const int32_t* parents,
+    const int32_t* tokens, const float* uniforms, int32_t B, int32_t n, int32_t V,
+    double temperature, int32_t* accept_len, int32_t* accept_node, int32_t* out_tokens,
+    float* final_dist, void* workspace, size_t workspace_bytes, void* stream) {
+    return tree_stochastic_call(target_logits, draft_logits, dtype, parents, tokens, uniforms, B,
+                                n, V, temperature, accept_len, accept_node, out_tokens,
+                                final_dist, workspace, workspace_bytes, stream, nullptr);
+}
+
+extern "C" int32_t spec_verify_tree_stochastic_timed(
+    const void* target_logits, const void* draft_logits, int32_t dtype, const int32_t* parents,
+    const int32_t* tokens, const float* uniforms, int32_t B, int32_t n, int32_t V,
+    double temperature, int32_t* accept_len, int32_t* accept_node, int32_t* out_tokens,
+    float* final_dist, void* workspace, size_t workspace_bytes, void* stream,
+    void* const* phase_events) {
+    return tree_stochastic_call(target_logits, draft_logits, dtype, parents, tokens, uniforms, B,
+                                n, V, temperature, accept_len, accept_node, out_tokens,
+                                final_dist, workspace, workspace_bytes, stream, phase_events);
+}
+
 extern "C" int32_t spec_cache_lookup(const int32_t* accept_len, const int32_t* out_tokens,
                                      int32_t R, int32_t gamma, const int32_t* cache_k,
                                      const int32_t* cache_a, int32_t ncache, int32_t* slot,
@@ -560,12 +642,11 @@ extern "C" int32_t spec_cache_lookup(const int32_t* accept_len, const int32_t* o
                : SV_ERR_HIP;
 }
 
-extern "C" int32_t spec_verify_tree_greedy(const void* target_logits, int32_t dtype,
-                                           const int32_t* parents, const int32_t* tokens,
-                                           int32_t B, int32_t n, int32_t V, int32_t* accept_len,
-                                           int32_t* accept_node, int32_t* out_tokens,
-                                           void* workspace, size_t workspace_bytes, void* stream,
-                                           void* const* phase_events) {
+static int32_t tree_greedy_call(const void* target_logits, int32_t dtype, const int32_t* parents,
+                                const int32_t* tokens, int32_t B, int32_t n, int32_t V,
+                                int32_t* accept_len, int32_t* accept_node, int32_t* out_tokens,
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                void* const* phase_events) {
     TreePlan p;
     int32_t st = tree_plan(B, n, V, dtype, &p);
     if (st != SV_OK) return st;
@@ -597,4 +678,26 @@ extern "C" int32_t spec_verify_tree_greedy(const void* target_logits, int32_t dt
         return SV_ERR_HIP;
     if (launch_tree_resolve(a, s) != hipSuccess) return SV_ERR_HIP;
     return SV_OK;
+}
+
+extern "C" int32_t spec_verify_tree_greedy(const void* target_logits, int32_t dtype,
+                                           const int32_t* parents, const int32_t* tokens,
+                                           int32_t B, int32_t n, int32_t V, int32_t* accept_len,
+                                           int32_t* accept_node, int32_t* out_tokens,
+                                           void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+    return tree_greedy_call(target_logits, dtype, parents, tokens, B, n, V, accept_len,
+                            accept_node, out_tokens, workspace, workspace_bytes, stream, nullptr);
+}
+
+extern "C" int32_t spec_verify_tree_greedy_timed(const void* target_logits, int32_t dtype,
+                                                 const int32_t* parents, const int32_t* tokens,
+                                                 int32_t B, int32_t n, int32_t V,
+                                                 int32_t* accept_len, int32_t* accept_node,
+                                                 int32_t* out_tokens, void* workspace,
+                                                 size_t workspace_bytes, void* stream,
+                                                 void* const* phase_events) {
+    return tree_greedy_call(target_logits, dtype, parents, tokens, B, n, V, accept_len,
+                            accept_node, out_tokens, workspace, workspace_bytes, stream,
+                            phase_events);
 }

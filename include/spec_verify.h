@@ -62,9 +62,16 @@
  *    without any host synchronisation: accept_len[b] = -1 and every output
  *    token of that block = -1, while the other blocks are unaffected.  They
  *    are: a draft token outside [0, V); a NaN or +inf logit in any row of the
- *    block; a row without any finite logit; for chains, a row whose largest
- *    finite logit m has |m| / T > 2^28 (outside the supported domain); for
- *    trees, a malformed parent array or a node token outside [0, V).
+ *    block; a row without any finite logit; a row outside the numeric domain
+ *    (below); for trees, a malformed parent array or a node token outside
+ *    [0, V).
+ *  - Numeric domain (a restriction of this library, not of the method): every
+ *    row whose softmax is taken -- target and draft rows of chains and
+ *    stochastic trees, decoder rows of spec_outcome_topk, draft rows of
+ *    spec_tree_build -- must have |m| / T <= 2^28, m its largest finite
+ *    logit.  The kernels scale logits by 1/T in single precision against an
+ *    integer reference near m/T, which stays exact only within that range.
+ *    A row beyond it makes its block (request) invalid as above.
  *  - -inf logits are legal and mean "masked": that token has probability 0.
  *  - The workspace is scratch owned by the caller: it needs no
  *    initialisation and its contents after a call are unspecified.  Two
@@ -132,18 +139,12 @@ size_t spec_verify_chain_workspace_bytes(int32_t B, int32_t gamma, int32_t V, in
  *                 spec_verify_chain_workspace_bytes(B, gamma, V, dtype)
  *                 bytes, 16-byte aligned (contents irrelevant).
  *  stream         hipStream_t to enqueue on (NULL = null stream).
- *  phase_events   NULLABLE: if not NULL, points to 3 hipEvent_t handles
- *                 (created with timing enabled): [0] and [1] are recorded by
- *                 the launch of the row-statistics kernel (the one pass over
- *                 every logit) at that kernel's start and end, [2] on
- *                 `stream` after the final-draw kernels (instrumentation for
- *                 timing; the optional final_dist pass comes later).
  */
 int32_t spec_verify_chain(const void *target_logits, const void *draft_logits, int32_t dtype,
                           const int32_t *draft_tokens, const float *uniforms, int32_t B,
                           int32_t gamma, int32_t V, double temperature, int32_t *accept_len,
                           int32_t *out_tokens, float *final_dist, void *workspace,
-                          size_t workspace_bytes, void *stream, void *const *phase_events);
+                          size_t workspace_bytes, void *stream);
 
 /* Bytes of workspace spec_verify_chain_pointmass needs for these sizes; 0 if
  * the sizes or dtype are invalid. */
@@ -164,16 +165,15 @@ size_t spec_verify_chain_pointmass_workspace_bytes(int32_t B, int32_t gamma, int
  *
  *  target_logits  [B][gamma+1][V] dtype, as for spec_verify_chain.
  *  draft_tokens   [B][gamma] int32: x_0 .. x_{gamma-1}.
- *  uniforms, temperature, accept_len, out_tokens, final_dist, stream and
- *  phase_events are as for spec_verify_chain; the workspace is sized by
+ *  uniforms, temperature, accept_len, out_tokens, final_dist and stream are
+ *  as for spec_verify_chain; the workspace is sized by
  *  spec_verify_chain_pointmass_workspace_bytes.  Data-dependent errors: a
  *  draft token outside [0, V), or a NaN, +inf or all -inf target row. */
 int32_t spec_verify_chain_pointmass(const void *target_logits, int32_t dtype,
                                     const int32_t *draft_tokens, const float *uniforms,
                                     int32_t B, int32_t gamma, int32_t V, double temperature,
                                     int32_t *accept_len, int32_t *out_tokens, float *final_dist,
-                                    void *workspace, size_t workspace_bytes, void *stream,
-                                    void *const *phase_events);
+                                    void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of workspace spec_verify_tree_greedy needs; 0 if the sizes or dtype
  * are invalid. */
@@ -196,16 +196,12 @@ size_t spec_verify_tree_greedy_workspace_bytes(int32_t B, int32_t n, int32_t V, 
  *                 token id on ties), then -1.
  *  workspace      as for spec_verify_chain, sized by
  *                 spec_verify_tree_greedy_workspace_bytes.
- *  phase_events   NULLABLE: 2 hipEvent_t (timing enabled) recorded by the
- *                 launch of the row-argmax kernel (the one pass over every
- *                 logit) at that kernel's start and end; the path-resolution
- *                 kernel follows.
  */
 int32_t spec_verify_tree_greedy(const void *target_logits, int32_t dtype,
                                 const int32_t *parents, const int32_t *tokens, int32_t B,
                                 int32_t n, int32_t V, int32_t *accept_len, int32_t *accept_node,
                                 int32_t *out_tokens, void *workspace, size_t workspace_bytes,
-                                void *stream, void *const *phase_events);
+                                void *stream);
 
 /* Bytes of workspace spec_verify_tree_stochastic needs; 0 if the sizes or
  * dtype are invalid. */
@@ -227,6 +223,13 @@ size_t spec_verify_tree_stochastic_workspace_bytes(int32_t B, int32_t n, int32_t
  *    in ascending token id: the smallest v whose inclusive prefix sum
  *    exceeds u * (the total).  The pages give no residual rule for branches
  *    rejected below v*, and none is applied.
+ *  THIS RULE DOES NOT PRESERVE THE TARGET DISTRIBUTION.  A child that the
+ *  test rejects leaves its token's mass in p_{v*}, so a token the draft
+ *  proposes more often than the target would emit it is committed too
+ *  often: with one child drawn from q = (0.9, 0.1) under p = (0.5, 0.5),
+ *  token 0 is committed with probability 0.7, not 0.5.  The rule is exact
+ *  when every test is certain (one-hot targets give greedy verification)
+ *  and when q = p.
  *
  *  target_logits, draft_logits  [B][n][V] dtype.
  *  parents, tokens  [B][n] int32, as for spec_verify_tree_greedy.
@@ -238,17 +241,15 @@ size_t spec_verify_tree_stochastic_workspace_bytes(int32_t B, int32_t n, int32_t
  *                request).
  *  An invalid request (a malformed parent array, a token outside [0, V), a
  *  NaN or +inf logit or a row without a finite logit in any target or draft
- *  row, or |max finite logit| / T > 2^28) gets accept_len = accept_node = -1
- *  and all tokens -1.
- *  workspace, stream, phase_events: as for spec_verify_chain (events [0] and
- *  [1] bracket the statistics pass over all 2n rows, [2] follows the draw). */
+ *  row, or a row outside the numeric domain described at the top of this
+ *  file) gets accept_len = accept_node = -1 and all tokens -1.
+ *  workspace, stream: as for spec_verify_chain. */
 int32_t spec_verify_tree_stochastic(const void *target_logits, const void *draft_logits,
                                     int32_t dtype, const int32_t *parents, const int32_t *tokens,
                                     const float *uniforms, int32_t B, int32_t n, int32_t V,
                                     double temperature, int32_t *accept_len, int32_t *accept_node,
                                     int32_t *out_tokens, float *final_dist, void *workspace,
-                                    size_t workspace_bytes, void *stream,
-                                    void *const *phase_events);
+                                    size_t workspace_bytes, void *stream);
 
 /* Cache entries per request of spec_outcome_topk. */
 #define SV_MAX_CACHE 16
@@ -278,15 +279,13 @@ size_t spec_outcome_topk_workspace_bytes(int32_t R, int32_t gamma, int32_t V, in
  *  out_k, out_a  out [R][ncache] int32; out_p out [R][ncache] double.
  *  hit           out [R] double: sum of out_p, or -1 for an invalid request
  *                (a draft token outside [0, V), a NaN or +inf logit, a row
- *                without a finite logit, or |max finite logit| / T > 2^28),
- *                whose slots are then all -1 / 0.
- *  workspace, stream, phase_events: as for spec_verify_tree_greedy (the two
- *  events bracket the one pass over the logits). */
+ *                without a finite logit, or a row outside the numeric
+ *                domain), whose slots are then all -1 / 0.
+ *  workspace, stream: as for spec_verify_tree_greedy. */
 int32_t spec_outcome_topk(const void *logits, int32_t dtype, const int32_t *draft_tokens,
                           int32_t R, int32_t gamma, int32_t V, double temperature, int32_t ncache,
                           int32_t *out_k, int32_t *out_a, double *out_p, double *hit,
-                          void *workspace, size_t workspace_bytes, void *stream,
-                          void *const *phase_events);
+                          void *workspace, size_t workspace_bytes, void *stream);
 
 /* Children per node, and rows times children, of spec_tree_build. */
 #define SV_MAX_TREE_WIDTH 16
@@ -327,16 +326,15 @@ size_t spec_tree_build_workspace_bytes(int32_t R, int32_t M, int32_t V, int32_t 
  *                0; -inf past the last node).
  *  n_nodes       out [R] int32: the number of nodes, or -1 for an invalid
  *                request (a NaN or +inf logit, a row without a finite logit,
- *                or |max finite logit| / T > 2^28 in any of its M rows, or a
- *                child_row entry outside [-1, M)), whose outputs are then all
- *                -1 / -inf.
- *  workspace, stream, phase_events: as for spec_verify_tree_greedy (the two
- *  events bracket the one pass over the logits). */
+ *                or a row outside the numeric domain, in any of its M rows,
+ *                or a child_row entry outside [-1, M)), whose outputs are
+ *                then all -1 / -inf.
+ *  workspace, stream: as for spec_verify_tree_greedy. */
 int32_t spec_tree_build(const void *draft_logits, int32_t dtype, const int32_t *child_row,
                         int32_t R, int32_t M, int32_t V, double temperature, int32_t W,
                         int32_t max_depth, int32_t budget, int32_t *parents, int32_t *tokens,
                         int32_t *node_row, double *score, int32_t *n_nodes, void *workspace,
-                        size_t workspace_bytes, void *stream, void *const *phase_events);
+                        size_t workspace_bytes, void *stream);
 
 /* Speculation-cache lookup ("JetSpec++", Section 4.2: a block drafted in
  * advance for the outcome (k, a) becomes the next block when verification

@@ -1,7 +1,8 @@
 """C-ABI checks that need no GPU: the library loads, exports every function
-declared in include/spec_verify.h, sizes workspaces, and rejects bad
-arguments on the host before anything is enqueued (each case below fails a
-host check, so no kernel is ever launched here)."""
+declared in include/*.h, sizes workspaces, and rejects bad arguments on the
+host before anything is enqueued (each case below fails a host check, so no
+kernel is ever launched here).  The host checks run against the product
+entry points and against their instrumented *_timed twins."""
 import ctypes as ct
 import os
 import re
@@ -11,10 +12,26 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
-@pytest.fixture(scope="module")
-def lib():
+class _TimedTwins:
+    """The library with every entry point that has a *_timed twin replaced
+    by that twin, called with a null event array."""
+
+    def __init__(self, lib):
+        self._lib = lib
+
+    def __getattr__(self, name):
+        f = getattr(self._lib, name)
+        t = getattr(self._lib, name + "_timed", None) if not name.endswith("_timed") else None
+        if t is None:
+            return f
+        return lambda *args: t(*args, None)
+
+
+def _load():
     import exact_draft_verification_amd as sv
 
     if not os.path.exists(sv.library_path()):
@@ -24,10 +41,18 @@ def lib():
     return sv.load_library()
 
 
+@pytest.fixture(scope="module", params=["product", "timed"])
+def lib(request):
+    real = _load()
+    return real if request.param == "product" else _TimedTwins(real)
+
+
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(spec_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(spec_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def header_constants():
@@ -35,14 +60,18 @@ def header_constants():
     return {k: int(v) for k, v in re.findall(r"#define\s+(SV_\w+)\s+(\d+)", text)}
 
 
-def test_exports_every_declared_symbol(lib):
+def test_exports_every_declared_symbol():
+    lib = _load()
     names = declared_functions()
     assert {"spec_verify_chain", "spec_verify_tree_greedy", "spec_verify_chain_workspace_bytes",
             "spec_verify_tree_greedy_workspace_bytes", "spec_verify_status_string",
             "spec_verify_chain_pointmass", "spec_verify_chain_pointmass_workspace_bytes",
             "spec_outcome_topk", "spec_outcome_topk_workspace_bytes",
             "spec_cache_lookup", "spec_tree_build", "spec_tree_build_workspace_bytes",
-            "spec_verify_tree_stochastic", "spec_verify_tree_stochastic_workspace_bytes"} <= set(names)
+            "spec_verify_tree_stochastic", "spec_verify_tree_stochastic_workspace_bytes",
+            "spec_verify_chain_timed", "spec_verify_chain_pointmass_timed",
+            "spec_verify_tree_greedy_timed", "spec_verify_tree_stochastic_timed",
+            "spec_outcome_topk_timed", "spec_tree_build_timed"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
@@ -115,13 +144,12 @@ def p(a):
 def chain_call(lib, h, **over):
     args = dict(target=p(h.t), draft=p(h.d), dtype=0, tok=p(h.tok), u=p(h.u), B=h.B, g=h.g, V=h.V,
                 T=1.0,
-                acc=p(h.acc), out=p(h.out), dist=None, ws=p(h.ws_aligned), wsb=16, stream=None,
-                ev=None)
+                acc=p(h.acc), out=p(h.out), dist=None, ws=p(h.ws_aligned), wsb=16, stream=None)
     args.update(over)
     return lib.spec_verify_chain(args["target"], args["draft"], args["dtype"], args["tok"],
                                  args["u"], args["B"], args["g"], args["V"], args["T"],
                                  args["acc"], args["out"], args["dist"], args["ws"], args["wsb"],
-                                 args["stream"], args["ev"])
+                                 args["stream"])
 
 
 def test_chain_host_errors(lib):
@@ -148,13 +176,12 @@ def test_chain_host_errors(lib):
 
 def pointmass_call(lib, h, **over):
     args = dict(target=p(h.t), dtype=0, tok=p(h.tok), u=p(h.u), B=h.B, g=h.g, V=h.V, T=1.0,
-                acc=p(h.acc), out=p(h.out), dist=None, ws=p(h.ws_aligned), wsb=16, stream=None,
-                ev=None)
+                acc=p(h.acc), out=p(h.out), dist=None, ws=p(h.ws_aligned), wsb=16, stream=None)
     args.update(over)
     return lib.spec_verify_chain_pointmass(args["target"], args["dtype"], args["tok"], args["u"],
                                            args["B"], args["g"], args["V"], args["T"],
                                            args["acc"], args["out"], args["dist"], args["ws"],
-                                           args["wsb"], args["stream"], args["ev"])
+                                           args["wsb"], args["stream"])
 
 
 def test_pointmass_host_errors(lib):
@@ -203,7 +230,7 @@ def test_outcome_host_errors(lib):
         args.update(o)
         return lib.spec_outcome_topk(args["t"], args["dt"], args["tok"], args["R"], args["g"],
                                      args["V"], args["T"], args["nc"], args["k"], args["a"],
-                                     args["pp"], args["hit"], args["ws"], args["wsb"], None, None)
+                                     args["pp"], args["hit"], args["ws"], args["wsb"], None)
 
     assert call(t=None) == c["SV_ERR_NULL"]
     assert call(tok=None) == c["SV_ERR_NULL"]
@@ -269,7 +296,7 @@ def test_tree_build_host_errors(lib):
         return lib.spec_tree_build(args["z"], args["dt"], args["cr"], args["R"], args["M"],
                                    args["V"], args["T"], args["W"], args["N"], args["nb"],
                                    args["par"], args["tok"], args["row"], args["sc"], args["n"],
-                                   args["ws"], args["wsb"], None, None)
+                                   args["ws"], args["wsb"], None)
 
     assert call(z=None) == c["SV_ERR_NULL"]
     assert call(n=None) == c["SV_ERR_NULL"]
@@ -311,8 +338,7 @@ def test_tree_stochastic_host_errors(lib):
         return lib.spec_verify_tree_stochastic(args["t"], args["d"], args["dt"], args["par"],
                                                args["tok"], args["u"], args["B"], args["n"],
                                                args["V"], args["T"], args["acc"], args["node"],
-                                               args["out"], None, args["ws"], args["wsb"], None,
-                                               None)
+                                               args["out"], None, args["ws"], args["wsb"], None)
 
     assert call(d=None) == c["SV_ERR_NULL"]
     assert call(u=None) == c["SV_ERR_NULL"]
@@ -347,7 +373,7 @@ def test_tree_host_errors(lib):
         a.update(o)
         return lib.spec_verify_tree_greedy(a["t"], a["dt"], a["par"], a["tok"], a["B"], a["n"],
                                            a["V"], a["acc"], a["node"], a["out"], a["ws"],
-                                           a["wsb"], None, None)
+                                           a["wsb"], None)
 
     assert call(par=None) == c["SV_ERR_NULL"]
     assert call(node=None) == c["SV_ERR_NULL"]
