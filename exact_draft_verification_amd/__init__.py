@@ -37,7 +37,10 @@ SV_DTYPE_BF16 = 1
 SV_MAX_VOCAB = 1 << 29  # largest vocabulary size V any entry point accepts
 
 _HERE = _os.path.dirname(_os.path.abspath(__file__))
-_LIB_PATH = _os.path.join(_HERE, "libspecverify.so")
+# Another build of the same sources (for instance one whose host code is
+# built with address and undefined-behaviour sanitizers) can be loaded
+# instead by naming it here; there is no other library and no fallback.
+_LIB_PATH = _os.environ.get("SPEC_VERIFY_LIB") or _os.path.join(_HERE, "libspecverify.so")
 _lib = None
 
 
