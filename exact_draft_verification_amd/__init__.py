@@ -30,11 +30,13 @@ __all__ = [
     "spec_tree_build", "spec_tree_build_workspace_bytes", "spec_verify_tree_stochastic",
     "spec_verify_tree_stochastic_workspace_bytes",
     "spec_verify_tree_greedy_workspace_bytes", "spec_verify_status_string",
+    "spec_verify_chain_noalloc", "SV_NOALLOC_SCRATCH_BYTES",
 ]
 
 SV_DTYPE_F32 = 0
 SV_DTYPE_BF16 = 1
 SV_MAX_VOCAB = 1 << 29  # largest vocabulary size V any entry point accepts
+SV_NOALLOC_SCRATCH_BYTES = 1 << 24  # static scratch of spec_verify_chain_noalloc per GPU
 
 _HERE = _os.path.dirname(_os.path.abspath(__file__))
 # Another build of the same sources (for instance one whose host code is
@@ -94,6 +96,8 @@ def load_library():
     lib.spec_tree_build_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
     lib.spec_tree_build_workspace_bytes.restype = SZ
     build_args = [P, I32, P, I32, I32, I32, D, I32, I32, I32, P, P, P, P, P, P, SZ, P]
+    lib.spec_verify_chain_noalloc.argtypes = [P, P, I32, P, P, I32, I32, I32, D, P, P, P, P]
+    lib.spec_verify_chain_noalloc.restype = I32
     # the product entry points, and their instrumented twins (one more
     # argument: the hipEvent_t array the benchmark times kernels with)
     for name, args in (("spec_verify_chain", chain_args),
@@ -268,6 +272,44 @@ def spec_verify_chain(target, draft, draft_tokens, uniforms, temperature, *, acc
                  _ptr(out_tokens), _ptr(final_dist), _ptr(workspace), _nbytes(workspace), _stream_handle(stream, dev))
     if st != 0:
         raise SpecVerifyError(st, "spec_verify_chain")
+    return accept_len, out_tokens, final_dist
+
+
+def spec_verify_chain_noalloc(target, draft, draft_tokens, uniforms, temperature, *,
+                              accept_len=None, out_tokens=None, final_dist=None, want_dist=False,
+                              stream=None):
+    """Chain verification through the allocation-free entry point: the
+    library uses its static per-GPU scratch instead of a workspace.  Same
+    arguments and results as spec_verify_chain (outputs the caller does not
+    pass are allocated here, by torch, not by the library)."""
+    torch = _torch()
+    lib = load_library()
+    if target.dim() != 3:
+        raise ValueError("target must be [B, gamma+1, V]")
+    B, g1, V = target.shape
+    g = g1 - 1
+    dev = target.device
+    code = _dtype_code(target)
+    _check(target, "target", (B, g1, V), device=dev)
+    _check(draft, "draft", (B, g, V), dtype=target.dtype, device=dev)
+    _check(draft_tokens, "draft_tokens", (B, g), dtype=torch.int32, device=dev)
+    _check(uniforms, "uniforms", (B, g1), dtype=torch.float32, device=dev)
+    if accept_len is None:
+        accept_len = _new(B, torch.int32, dev, stream)
+    if out_tokens is None:
+        out_tokens = _new((B, g1), torch.int32, dev, stream)
+    if final_dist is None and want_dist:
+        final_dist = _new((B, V), torch.float32, dev, stream)
+    _check(accept_len, "accept_len", (B,), dtype=torch.int32, device=dev)
+    _check(out_tokens, "out_tokens", (B, g1), dtype=torch.int32, device=dev)
+    if final_dist is not None:
+        _check(final_dist, "final_dist", (B, V), dtype=torch.float32, device=dev)
+    st = lib.spec_verify_chain_noalloc(_ptr(target), _ptr(draft), code, _ptr(draft_tokens),
+                                       _ptr(uniforms), B, g, V, float(temperature),
+                                       _ptr(accept_len), _ptr(out_tokens), _ptr(final_dist),
+                                       _stream_handle(stream, dev))
+    if st != 0:
+        raise SpecVerifyError(st, "spec_verify_chain_noalloc")
     return accept_len, out_tokens, final_dist
 
 

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "spec_verify.h"
 #include "spec_verify_timing.h"
@@ -218,6 +219,8 @@ extern "C" const char* spec_verify_status_string(int32_t status) {
         case SV_ERR_WORKSPACE: return "workspace too small or not 16-byte aligned";
         case SV_ERR_HIP: return "HIP runtime error";
         case SV_ERR_ALIGN: return "a pointer is not aligned to its element size";
+        case SV_ERR_SCRATCH:
+            return "the sizes need more scratch than the allocation-free entry point holds";
         default: return "unknown status";
     }
 }
@@ -243,18 +246,16 @@ extern "C" size_t spec_verify_tree_greedy_workspace_bytes(int32_t B, int32_t n, 
 namespace sv {
 namespace {
 
-// Both chain entry points: validation, workspace layout and the launches.
-// draft_logits is null exactly when `pointmass`.
-int32_t chain_call(const void* target_logits, const void* draft_logits, bool pointmass,
-                   int32_t dtype, const int32_t* draft_tokens, const float* uniforms, int32_t B,
-                   int32_t gamma, int32_t V, double temperature, int32_t* accept_len,
-                   int32_t* out_tokens, float* final_dist, void* workspace,
-                   size_t workspace_bytes, void* stream, void* const* phase_events) {
-    ChainPlan p;
-    int32_t st = chain_plan(B, gamma, V, dtype, pointmass, &p);
+// The host checks of a chain call other than the workspace's: sizes, null
+// pointers, temperature and alignment; fills the plan.
+int32_t chain_check(const void* target_logits, const void* draft_logits, bool pointmass,
+                    int32_t dtype, const int32_t* draft_tokens, const float* uniforms, int32_t B,
+                    int32_t gamma, int32_t V, double temperature, const int32_t* accept_len,
+                    const int32_t* out_tokens, const float* final_dist, ChainPlan* p) {
+    int32_t st = chain_plan(B, gamma, V, dtype, pointmass, p);
     if (st != SV_OK) return st;
     if (!target_logits || (!pointmass && !draft_logits) || !draft_tokens || !uniforms ||
-        !accept_len || !out_tokens || !workspace)
+        !accept_len || !out_tokens)
         return SV_ERR_NULL;
     if (!std::isfinite(temperature) || temperature < 1e-6 || temperature > 1e6)
         return SV_ERR_TEMPERATURE;
@@ -264,6 +265,22 @@ int32_t chain_call(const void* target_logits, const void* draft_logits, bool poi
         !aligned(uniforms, 4) || !aligned(accept_len, 4) || !aligned(out_tokens, 4) ||
         (final_dist && !aligned(final_dist, 4)))
         return SV_ERR_ALIGN;
+    return SV_OK;
+}
+
+// Both chain entry points: validation, workspace layout and the launches.
+// draft_logits is null exactly when `pointmass`.
+int32_t chain_call(const void* target_logits, const void* draft_logits, bool pointmass,
+                   int32_t dtype, const int32_t* draft_tokens, const float* uniforms, int32_t B,
+                   int32_t gamma, int32_t V, double temperature, int32_t* accept_len,
+                   int32_t* out_tokens, float* final_dist, void* workspace,
+                   size_t workspace_bytes, void* stream, void* const* phase_events) {
+    ChainPlan p;
+    const int32_t st = chain_check(target_logits, draft_logits, pointmass, dtype, draft_tokens,
+                                   uniforms, B, gamma, V, temperature, accept_len, out_tokens,
+                                   final_dist, &p);
+    if (st != SV_OK) return st;
+    if (!workspace) return SV_ERR_NULL;
     if (!aligned(workspace, 16) || workspace_bytes < p.bytes) return SV_ERR_WORKSPACE;
 
     ChainArgs a;
@@ -360,6 +377,71 @@ extern "C" int32_t spec_verify_chain_pointmass_timed(
     return chain_call(target_logits, nullptr, true, dtype, draft_tokens, uniforms, B, gamma, V,
                       temperature, accept_len, out_tokens, final_dist, workspace,
                       workspace_bytes, stream, phase_events);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free chain verification.  Its scratch is a file-scope device
+// array, one copy per GPU, held until the process ends.  On the host the name
+// `scratch` is only a stand-in for the device symbol, never an address: each
+// GPU's copy is found once with hipGetSymbolAddress (with that GPU current)
+// and its address kept in scratch_dev, which is what the kernels are given.
+
+namespace sv {
+namespace {
+
+__device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices];  // per device: the address of its copy, or null
+
+// The address of `scratch` on the device that runs `stream` (the current
+// device for the null stream), looked up on the first call there.
+int32_t scratch_for(hipStream_t stream, void** out) {
+    int dev = -1;
+    if (stream) {
+        if (hipStreamGetDevice(stream, &dev) != hipSuccess) return SV_ERR_HIP;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return SV_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return SV_ERR_HIP;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return SV_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return SV_ERR_HIP;
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return SV_ERR_HIP;
+        if (e != hipSuccess || !ptr) return SV_ERR_HIP;
+        scratch_dev[dev] = ptr;
+    }
+    *out = scratch_dev[dev];
+    return SV_OK;
+}
+
+}  // namespace
+}  // namespace sv
+
+extern "C" int32_t spec_verify_chain_noalloc(const void* target_logits, const void* draft_logits,
+                                             int32_t dtype, const int32_t* draft_tokens,
+                                             const float* uniforms, int32_t B, int32_t gamma,
+                                             int32_t V, double temperature, int32_t* accept_len,
+                                             int32_t* out_tokens, float* final_dist,
+                                             void* stream) {
+    ChainPlan p;
+    int32_t st = chain_check(target_logits, draft_logits, false, dtype, draft_tokens, uniforms, B,
+                             gamma, V, temperature, accept_len, out_tokens, final_dist, &p);
+    if (st != SV_OK) return st;
+    if (p.bytes > SV_NOALLOC_SCRATCH_BYTES) return SV_ERR_SCRATCH;
+    void* ws = nullptr;
+    st = scratch_for(static_cast<hipStream_t>(stream), &ws);
+    if (st != SV_OK) return st;
+    // every byte of the workspace is written before it is read within one
+    // call, so the previous call's contents need no clearing
+    return chain_call(target_logits, draft_logits, false, dtype, draft_tokens, uniforms, B, gamma,
+                      V, temperature, accept_len, out_tokens, final_dist, ws,
+                      SV_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 extern "C" size_t spec_outcome_topk_workspace_bytes(int32_t R, int32_t gamma, int32_t V,

@@ -101,6 +101,7 @@ extern "C" {
 #define SV_ERR_WORKSPACE 5   /* workspace too small or not 16-byte aligned         */
 #define SV_ERR_HIP 6         /* the HIP runtime reported an error                  */
 #define SV_ERR_ALIGN 7       /* a pointer is not aligned to its element size       */
+#define SV_ERR_SCRATCH 8     /* sizes need more than SV_NOALLOC_SCRATCH_BYTES      */
 
 /* Limits checked on the host. */
 #define SV_MAX_GAMMA 255   /* draft positions per chain block                     */
@@ -145,6 +146,28 @@ int32_t spec_verify_chain(const void *target_logits, const void *draft_logits, i
                           int32_t gamma, int32_t V, double temperature, int32_t *accept_len,
                           int32_t *out_tokens, float *final_dist, void *workspace,
                           size_t workspace_bytes, void *stream);
+
+/* Scratch held by spec_verify_chain_noalloc on every GPU it runs on. */
+#define SV_NOALLOC_SCRATCH_BYTES 16777216
+
+/* Chain verification that allocates nothing and takes no workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * serving loops that must not call hipMalloc, harnesses that forbid it.
+ * Arguments, results and errors are those of spec_verify_chain without the
+ * workspace (the same kernels run).  Its scratch is a static device array of
+ * SV_NOALLOC_SCRATCH_BYTES (16 MiB) in the library, one per GPU, held from
+ * the first call on that GPU until the process ends; sizes whose workspace
+ * (spec_verify_chain_workspace_bytes) exceeds it return SV_ERR_SCRATCH
+ * before anything is enqueued.  The first call on a GPU looks the array's
+ * address up (no allocation).  Every call on one GPU shares that array: two
+ * calls whose work overlaps on one GPU (different streams, or host threads
+ * racing) corrupt each other's scratch; calls ordered on one stream are
+ * safe. */
+int32_t spec_verify_chain_noalloc(const void *target_logits, const void *draft_logits,
+                                  int32_t dtype, const int32_t *draft_tokens,
+                                  const float *uniforms, int32_t B, int32_t gamma, int32_t V,
+                                  double temperature, int32_t *accept_len, int32_t *out_tokens,
+                                  float *final_dist, void *stream);
 
 /* Bytes of workspace spec_verify_chain_pointmass needs for these sizes; 0 if
  * the sizes or dtype are invalid. */

@@ -414,3 +414,34 @@ def test_product_path_has_no_oracle_or_cpu_fallback():
             sv.load_library()
     finally:
         sv._lib, sv._LIB_PATH = saved
+
+
+def test_noalloc_host_errors():
+    """spec_verify_chain_noalloc checks its arguments, and its scratch limit,
+    before touching any device (so these run without a GPU)."""
+    import exact_draft_verification_amd as sv
+
+    lib = _load()
+    c = header_constants()
+    assert c["SV_NOALLOC_SCRATCH_BYTES"] == sv.SV_NOALLOC_SCRATCH_BYTES
+    h = HostBufs(2, 3, 64)
+
+    def call(**over):
+        args = dict(target=p(h.t), draft=p(h.d), dtype=0, tok=p(h.tok), u=p(h.u), B=h.B, g=h.g,
+                    V=h.V, T=1.0, acc=p(h.acc), out=p(h.out), dist=None, stream=None)
+        args.update(over)
+        return lib.spec_verify_chain_noalloc(args["target"], args["draft"], args["dtype"],
+                                             args["tok"], args["u"], args["B"], args["g"],
+                                             args["V"], args["T"], args["acc"], args["out"],
+                                             args["dist"], args["stream"])
+
+    assert call(target=None) == c["SV_ERR_NULL"]
+    assert call(draft=None) == c["SV_ERR_NULL"]
+    assert call(B=0) == c["SV_ERR_SHAPE"]
+    assert call(dtype=5) == c["SV_ERR_DTYPE"]
+    assert call(T=0.0) == c["SV_ERR_TEMPERATURE"]
+    assert call(target=ct.c_void_p(h.t.ctypes.data + 2)) == c["SV_ERR_ALIGN"]
+    # 8192 blocks of gamma 16 over V = 151936 need about 25 MB of scratch
+    assert sv.spec_verify_chain_workspace_bytes(8192, 16, 151936, 1) > c["SV_NOALLOC_SCRATCH_BYTES"]
+    assert call(B=8192, g=16, V=151936, dtype=1) == c["SV_ERR_SCRATCH"]
+    assert (h.acc == 0).all() and (h.out == 0).all()
