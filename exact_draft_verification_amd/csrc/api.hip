@@ -46,7 +46,7 @@ void plan_segments(int64_t rows_total, int V, int epv, int64_t target, int min_v
 
 struct ChainPlan {
     int rows, nseg, seg_len, nchunk, chunk_tiles, nquart;
-    size_t off_part, off_zx, off_dec, off_qsum, off_fin, bytes;
+    size_t off_part, off_zx, off_dec, off_qsum, off_qpos, off_cdiff, off_fin, bytes;
 };
 
 // Carves `n` objects of `size` bytes out of the workspace at *off (256-byte
@@ -92,6 +92,8 @@ int32_t block_plan(int32_t B, int64_t rows, int32_t V, int32_t dtype, ChainPlan*
     p->off_zx = carve(&off, sizeof(float), nr);
     p->off_dec = carve(&off, sizeof(ChainDecision), nb);
     p->off_qsum = carve(&off, sizeof(double), nb * p->nquart);
+    p->off_qpos = carve(&off, sizeof(double), nb * p->nquart);
+    p->off_cdiff = carve(&off, sizeof(double), nb * p->nchunk);
     p->off_fin = carve(&off, sizeof(FinalState), nb);
     p->bytes = off;
     return SV_OK;
@@ -315,6 +317,8 @@ int32_t chain_call(const void* target_logits, const void* draft_logits, bool poi
     a.zx = reinterpret_cast<float*>(ws + p.off_zx);
     a.dec = reinterpret_cast<ChainDecision*>(ws + p.off_dec);
     a.qsum = reinterpret_cast<double*>(ws + p.off_qsum);
+    a.qpos = reinterpret_cast<double*>(ws + p.off_qpos);
+    a.cdiff = reinterpret_cast<double*>(ws + p.off_cdiff);
     a.fin = reinterpret_cast<FinalState*>(ws + p.off_fin);
     a.accept_len = accept_len;
     a.out_tokens = out_tokens;
@@ -666,6 +670,8 @@ static int32_t tree_stochastic_call(
     a.zx = nullptr;
     a.dec = reinterpret_cast<ChainDecision*>(ws + p.off_dec);
     a.qsum = reinterpret_cast<double*>(ws + p.off_qsum);
+    a.qpos = reinterpret_cast<double*>(ws + p.off_qpos);
+    a.cdiff = reinterpret_cast<double*>(ws + p.off_cdiff);
     a.fin = reinterpret_cast<FinalState*>(ws + p.off_fin);
     a.accept_len = accept_len;
     a.out_tokens = out_tokens;

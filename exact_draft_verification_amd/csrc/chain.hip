@@ -142,6 +142,7 @@ __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
 template <class E>
 __device__ ChainDecision chain_decide(const ChainArgs& a, int b, Stat* s_part) {
     __shared__ double s_L[2 * kMaxGamma + 1];
+    __shared__ double s_S[kMaxGamma + 1];
     __shared__ float s_R[2 * kMaxGamma + 1];
     __shared__ int s_x[kMaxGamma];
     __shared__ int s_bad, s_k;
@@ -195,6 +196,7 @@ __device__ ChainDecision chain_decide(const ChainArgs& a, int b, Stat* s_part) {
         if (!ok) atomicOr(&s_bad, 1);
         s_L[r] = static_cast<double>(t.R) + log2(t.S);
         s_R[r] = t.R;
+        if (r <= g) s_S[r] = t.S;
     }
     __syncthreads();
     if (tid < g) {
@@ -227,10 +229,12 @@ __device__ ChainDecision chain_decide(const ChainArgs& a, int b, Stat* s_part) {
         d.Rp = 0.0f;
         d.dL = 0.0;
         d.excl = -1;
+        d.Sp = 0.0;
     } else {
         const int k = s_k;
         d.k = k;
         d.Rp = s_R[k];
+        d.Sp = s_S[k];
         // ratio test: the residual needs the row pair's log-normaliser gap;
         // point mass: the residual is p_k without the rejected token
         d.dL = (k < g && !a.pointmass) ? s_L[k] - s_L[g + 1 + k] : 0.0;
@@ -254,7 +258,9 @@ __device__ ChainDecision chain_decide(const ChainArgs& a, int b, Stat* s_part) {
 struct DrawRow {
     float Rp, c_hi, c_lo;
     float dL_hi, dL_lo;  // dL as a float pair
+    float A_hi;          // Rp - dL rounded to float (a screen for negligible draft weights)
     double c_d, dL;
+    double A;            // Rp - dL: log2 Q'(v) = z_q(v) c - A
     bool resid;  // residual of p_k and q_k (else p_k itself, unnormalised)
     int excl;    // a token whose weight is 0 (point mass: the rejected one), or -1
 };
@@ -272,14 +278,14 @@ __device__ inline float log_ratio(float zp, float zq, const DrawRow& r, F32) {
     return static_cast<float>(fma(static_cast<double>(zp) - static_cast<double>(zq), r.c_d, -r.dL));
 }
 
-// 1 - 2^-D for D > 0, to within 2e-7 relative.  Below 1: x * g(x) with
+// 1 - 2^-D for 0 <= D < 1, to within 2e-7 relative: x * g(x) with
 // x = D ln 2 and g(x) = (1 - e^-x)/x approximated on [0, ln 2] by a degree-5
 // polynomial (coefficients fitted here to minimise the relative error: at
 // most 1.83e-8 with these fp32 coefficients in exact arithmetic, 1.55e-7
-// once x, each step and x * g are rounded to fp32).  From 1 up: 1 - 2^-D
-// with the hardware exp2, where 2^-D <= 1/2 keeps the subtraction well
-// conditioned.
-__device__ inline float one_minus_exp2_neg(float D) {
+// once x, each step and x * g are rounded to fp32).  From 1 up the callers
+// use 1 - 2^-D with the hardware exp2, where 2^-D <= 1/2 keeps the
+// subtraction well conditioned.
+__device__ inline float one_minus_exp2_neg_small(float D) {
     const float x = D * 0.693147180559945309f;
     float g = -1.033136854e-03f;
     g = fmaf(g, x, 8.067236282e-03f);
@@ -287,37 +293,83 @@ __device__ inline float one_minus_exp2_neg(float D) {
     g = fmaf(g, x, 1.666511893e-01f);
     g = fmaf(g, x, -4.999990761e-01f);
     g = fmaf(g, x, 1.0f);
-    const float small = x * g;
-    const float large = 1.0f - __builtin_amdgcn_exp2f(-D);
-    return D < 1.0f ? small : large;
+    return x * g;
 }
 
-// Unnormalised draw weight of token v.  With P(v) = 2^(z_p c - R_p)
-// (proportional to p_k(v)): residual  w = P(v) * (1 - 2^-max(D(v), 0)), which
-// is 0 for D <= 0; bonus row and fallback: w = P(v).  Branch-free, and
-// masked tokens need no test: a -inf target logit gives P = 0 and D = -inf or
-// NaN (clamped to 0, so w = 0); a -inf draft logit gives D = +inf and
-// w = P(v), as q(v) = 0 requires.
-template <class E, bool RESID>
-__device__ inline float draw_weight(float zp, float zq, const DrawRow& r) {
+// Residual terms of one token of the residual draw (ratio test, k < gamma).
+// With P = 2^(z_p c - R_p) (p's weight) and D = log2 p - log2 q, where q uses
+// the dL in hand, let Q' = P 2^-D (q's weight in P's units):
+//   d  = P - Q' = P (1 - 2^-D), signed,
+//   w  = max(d, 0), the residual weight,
+//   pz = P where D > 0, else 0.
+// If the dL in hand is off by delta (its error from the row statistics, up to
+// about 2e-7), the sum of d over the row is S_p (1 - 2^delta), so the select
+// kernel recovers delta from it, and w + kappa (pz - w) with kappa =
+// delta ln 2 is the weight at the exact dL to first order (dw/d(dL) =
+// -ln 2 (pz - w)).  Without it the residual mass W would carry a relative
+// error of about delta ln 2 q(D > 0) / W, large when p and q nearly agree.
+// So d must be accurate relative to itself, whatever its sign: for |D| < 1
+// it is formed from s = 1 - 2^-|D| (the polynomial) as P s (D > 0) or
+// -P s 2^|D| (D < 0), beyond that from 2^-D.  A token of negligible target
+// weight (as in the draw weights, t <= -60) has d = -Q', taken from its draft
+// logit in double precision when Q' is not negligible as well.
+template <class E>
+__device__ inline void resid_terms(float zp, float zq, const DrawRow& r, float& w, float& d,
+                                   float& pz) {
     float t = fmaf(zp, r.c_hi, -r.Rp);
     t = fmaf(zp, r.c_lo, t);
-    if constexpr (!RESID) {
-        return __builtin_amdgcn_exp2f(t);
-    } else {
-        // R_p is the integer ceiling of the row's largest z*c, so t > -60
-        // keeps every token whose target weight is within 2^-60 of the
-        // largest; the others get weight 0.  Together they could move any
-        // point of the CDF by at most V * 2^-60 relative (1.3e-13 at
-        // V = 151,936), far below the fp32 rounding of the sums, and the
-        // skip saves the residual arithmetic for the bulk of a peaked row.
-        float w = 0.0f;
-        if (t > -60.0f) {
-            const float D = fmaxf(log_ratio(zp, zq, r, E{}), 0.0f);
-            w = __builtin_amdgcn_exp2f(t) * one_minus_exp2_neg(D);
-        }
-        return w;
+    w = 0.0f;
+    d = 0.0f;
+    pz = 0.0f;
+    if (t > -60.0f) {
+        const float D = log_ratio(zp, zq, r, E{});
+        const float aD = fabsf(D);
+        const float sm = one_minus_exp2_neg_small(aD);
+        const float e = __builtin_amdgcn_exp2f(-D);
+        const bool small = aD < 1.0f;
+        const bool pos = D > 0.0f;
+        const float f = pos ? (small ? sm : 1.0f - e) : -(small ? sm * e : e - 1.0f);
+        const float P = __builtin_amdgcn_exp2f(t);
+        d = P * f;
+        w = fmaxf(d, 0.0f);
+        pz = pos ? P : 0.0f;
+    } else if (fmaf(zq, r.c_hi, -r.A_hi) > -62.0f) {
+        // log2 Q' = z_q c - A in double, then 2^(hi + lo) = 2^hi (1 + lo ln 2)
+        const double tq = static_cast<double>(zq) * r.c_d - r.A;
+        const float hi = static_cast<float>(tq);
+        const double lo = tq - static_cast<double>(hi);
+        d = -static_cast<float>(static_cast<double>(__builtin_amdgcn_exp2f(hi)) *
+                                (1.0 + lo * 0.69314718055994530942));
     }
+}
+
+// The lane's kPerVec residual terms in token order: weights w[i] and
+// pz[i], and the fp32 sums of w, d and pz in that order.
+template <class E>
+__device__ inline void lane_resid(const float* zp, const float* zq, const DrawRow& r, float* w,
+                                  float* pz, float& sw, float& sd, float& sp) {
+    sw = 0.0f;
+    sd = 0.0f;
+    sp = 0.0f;
+#pragma unroll
+    for (int i = 0; i < E::kPerVec; ++i) {
+        float d;
+        resid_terms<E>(zp[i], zq[i], r, w[i], d, pz[i]);
+        sw += w[i];
+        sd += d;
+        sp += pz[i];
+    }
+}
+
+// Unnormalised draw weight of token v for a draw from p_k itself (the bonus
+// row, point mass, a stochastic tree, or the fallback of an empty residual):
+// w = P(v) = 2^(z_p c - R_p), 0 for a masked token (-inf logit).  The
+// residual draw uses resid_terms instead.
+template <class E>
+__device__ inline float draw_weight(float zp, float, const DrawRow& r) {
+    float t = fmaf(zp, r.c_hi, -r.Rp);
+    t = fmaf(zp, r.c_lo, t);
+    return __builtin_amdgcn_exp2f(t);
 }
 
 template <class E>
@@ -347,7 +399,9 @@ __device__ inline DrawRow draw_row(const ChainArgs& a, const ChainDecision& d) {
     const float dL_hi = static_cast<float>(d.dL);
     const float dL_lo = static_cast<float>(d.dL - static_cast<double>(dL_hi));
     const bool resid = d.k < a.gamma && !a.pointmass;
-    return DrawRow{d.Rp, a.c_hi, a.c_lo, dL_hi, dL_lo, a.c_d, d.dL, resid, d.excl};
+    const double A = static_cast<double>(d.Rp) - d.dL;
+    return DrawRow{d.Rp,  a.c_hi, a.c_lo, dL_hi, dL_lo, static_cast<float>(A),
+                   a.c_d, d.dL,   A,      resid, d.excl};
 }
 
 // The kPerVec tokens [e, e + kPerVec) of the final row(s) as floats: one
@@ -372,41 +426,31 @@ __device__ inline void load_tokens(const FinalRows<E>& rows, bool resid, int e, 
     }
 }
 
-// A lane's weights and their sum, accumulated in token order in fp32 (the
-// select kernel repeats exactly this order, so its running prefix ends on
-// the very value the quarter sums were built from).  The residual/bonus
-// choice is taken once here, outside the per-token code.
-template <class E, bool RESID>
-__device__ inline float lane_weights_t(const float* zp, const float* zq, const DrawRow& r, int e,
-                                       float* w) {
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < E::kPerVec; ++i) {
-        w[i] = draw_weight<E, RESID>(zp[i], zq[i], r);
-        s += w[i];
-    }
-    if constexpr (!RESID) {
-        // only a point-mass draw excludes a token (the residual never does):
-        // the one lane that holds it zeroes its weight and sums again, in
-        // the same order
-        if (static_cast<unsigned>(r.excl - e) < static_cast<unsigned>(E::kPerVec)) {
-            s = 0.0f;
-#pragma unroll
-            for (int i = 0; i < E::kPerVec; ++i) {
-                w[i] = e + i == r.excl ? 0.0f : w[i];
-                s += w[i];
-            }
-        }
-    }
-    return s;
-}
-
-// Weights of the lane's kPerVec tokens [e, e + kPerVec) and their sum.
+// Weights of the lane's kPerVec tokens [e, e + kPerVec) for a draw from p_k
+// itself (r.resid false) and their sum, accumulated in token order in fp32
+// (the select kernel repeats exactly this order, so its running prefix ends
+// on the very value the quarter sums were built from; lane_resid keeps the
+// same order for the residual draw).
 template <class E>
 __device__ inline float lane_weights(const float* zp, const float* zq, const DrawRow& r, int e,
                                      float* w) {
-    return r.resid ? lane_weights_t<E, true>(zp, zq, r, e, w)
-                   : lane_weights_t<E, false>(zp, zq, r, e, w);
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < E::kPerVec; ++i) {
+        w[i] = draw_weight<E>(zp[i], zq[i], r);
+        s += w[i];
+    }
+    // only a point-mass draw excludes a token: the one lane that holds it
+    // zeroes its weight and sums again, in the same order
+    if (static_cast<unsigned>(r.excl - e) < static_cast<unsigned>(E::kPerVec)) {
+        s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < E::kPerVec; ++i) {
+            w[i] = e + i == r.excl ? 0.0f : w[i];
+            s += w[i];
+        }
+    }
+    return s;
 }
 
 
@@ -468,7 +512,8 @@ __device__ inline void issue_group(const FinalRows<E>& rows, int t, int t1, int 
 // one past it is all -inf (weight 0).
 template <class E, int G, bool RESID>
 __device__ inline void group_sums(const FinalRows<E>& rows, const DrawRow& r, int t, int t1, int V,
-                                  const uint4* p, const uint4* q, double* qs, int nquart) {
+                                  const uint4* p, const uint4* q, double* qs, double* qp,
+                                  int nquart, double& dacc) {
     constexpr int kTile = kThreads * E::kPerVec;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -488,9 +533,22 @@ __device__ inline void group_sums(const FinalRows<E>& rows, const DrawRow& r, in
         } else {
             load_tokens<E>(rows, RESID, e, V, zp, zq);
         }
-        const double sw = wave_sum(static_cast<double>(lane_weights_t<E, RESID>(zp, zq, r, e, w)));
         const int qi = j * kWaves + wave;
-        if (lane == 0 && qi < nquart) qs[qi] = sw;
+        if constexpr (RESID) {
+            float pz[E::kPerVec], lw, ld, lp;
+            lane_resid<E>(zp, zq, r, w, pz, lw, ld, lp);
+            dacc += static_cast<double>(ld);
+            const double sw = wave_sum(static_cast<double>(lw));
+            const double sp = wave_sum(static_cast<double>(lp));
+            if (lane == 0 && qi < nquart) {
+                qs[qi] = sw;
+                qp[qi] = sp;
+            }
+        } else {
+            const double sw =
+                wave_sum(static_cast<double>(lane_weights<E>(zp, zq, r, e, w)));
+            if (lane == 0 && qi < nquart) qs[qi] = sw;
+        }
     }
 }
 
@@ -498,7 +556,7 @@ __device__ inline void group_sums(const FinalRows<E>& rows, const DrawRow& r, in
 // group's loads are in flight while the current group's weights are formed.
 template <class E, int G, bool RESID>
 __device__ inline void stream_tiles(const FinalRows<E>& rows, const DrawRow& r, int t0, int t1,
-                                    int V, double* qs, int nquart) {
+                                    int V, double* qs, double* qp, int nquart, double& dacc) {
     const int vlast = (V / E::kPerVec - 1) * E::kPerVec;  // the row's last whole vector
     const int ngroup = (t1 - t0 + G - 1) / G;
     uint4 cp[G], cq[G];
@@ -506,14 +564,14 @@ __device__ inline void stream_tiles(const FinalRows<E>& rows, const DrawRow& r, 
     for (int gi = 0; gi + 1 < ngroup; ++gi) {
         uint4 np[G], nq[G];
         issue_group<E, G, RESID>(rows, t0 + (gi + 1) * G, t1, vlast, np, nq);
-        group_sums<E, G, RESID>(rows, r, t0 + gi * G, t1, V, cp, cq, qs, nquart);
+        group_sums<E, G, RESID>(rows, r, t0 + gi * G, t1, V, cp, cq, qs, qp, nquart, dacc);
 #pragma unroll
         for (int m = 0; m < G; ++m) {
             cp[m] = np[m];
             if constexpr (RESID) cq[m] = nq[m];
         }
     }
-    group_sums<E, G, RESID>(rows, r, t0 + (ngroup - 1) * G, t1, V, cp, cq, qs, nquart);
+    group_sums<E, G, RESID>(rows, r, t0 + (ngroup - 1) * G, t1, V, cp, cq, qs, qp, nquart, dacc);
 }
 
 // Chunk workgroup: the block's decision, then the chunk's tiles of the final
@@ -537,22 +595,49 @@ __global__ __launch_bounds__(kThreads) void chain_chunks_kernel(ChainArgs a) {
     const int ntile = (a.V + kTile - 1) / kTile;
     const int t0 = c * a.chunk_tiles, t1 = min(ntile, t0 + a.chunk_tiles);
     double* qs = a.qsum + static_cast<int64_t>(b) * a.nquart;
+    double* qp = a.qpos + static_cast<int64_t>(b) * a.nquart;
+    double dacc = 0.0;  // residual draw: this thread's share of sum (P - Q') over the chunk
     if (rows.vec_ok && a.V >= E::kPerVec) {
         if (r.resid)
-            stream_tiles<E, G, true>(rows, r, t0, t1, a.V, qs, a.nquart);
+            stream_tiles<E, G, true>(rows, r, t0, t1, a.V, qs, qp, a.nquart, dacc);
         else
-            stream_tiles<E, G, false>(rows, r, t0, t1, a.V, qs, a.nquart);
-        return;
+            stream_tiles<E, G, false>(rows, r, t0, t1, a.V, qs, qp, a.nquart, dacc);
+    } else {
+        // rows not 16-byte aligned (or shorter than a vector): token by token
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        for (int j = t0; j < t1; ++j) {
+            float zp[E::kPerVec], zq[E::kPerVec], w[E::kPerVec];
+            const int e = j * kTile + static_cast<int>(threadIdx.x) * E::kPerVec;
+            load_tokens<E>(rows, r.resid, e, a.V, zp, zq);
+            const int qi = j * kWaves + wave;
+            if (r.resid) {
+                float pz[E::kPerVec], lw, ld, lp;
+                lane_resid<E>(zp, zq, r, w, pz, lw, ld, lp);
+                dacc += static_cast<double>(ld);
+                const double sw = wave_sum(static_cast<double>(lw));
+                const double sp = wave_sum(static_cast<double>(lp));
+                if (lane == 0 && qi < a.nquart) {
+                    qs[qi] = sw;
+                    qp[qi] = sp;
+                }
+            } else {
+                const double sw = wave_sum(static_cast<double>(lane_weights<E>(zp, zq, r, e, w)));
+                if (lane == 0 && qi < a.nquart) qs[qi] = sw;
+            }
+        }
     }
-    // rows not 16-byte aligned (or shorter than a vector): token by token
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int j = t0; j < t1; ++j) {
-        float zp[E::kPerVec], zq[E::kPerVec], w[E::kPerVec];
-        const int e = j * kTile + static_cast<int>(threadIdx.x) * E::kPerVec;
-        load_tokens<E>(rows, r.resid, e, a.V, zp, zq);
-        const double sw = wave_sum(static_cast<double>(lane_weights<E>(zp, zq, r, e, w)));
-        const int qi = j * kWaves + wave;
-        if (lane == 0 && qi < a.nquart) qs[qi] = sw;
+    if (r.resid) {
+        // the chunk's sum of P - Q'
+        __shared__ double s_d[kWaves];
+        const double wd = wave_sum(dacc);
+        if ((threadIdx.x & 63) == 0) s_d[threadIdx.x >> 6] = wd;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            double t = 0.0;
+#pragma unroll
+            for (int i = 0; i < kWaves; ++i) t += s_d[i];
+            a.cdiff[static_cast<int64_t>(b) * a.nchunk + c] = t;
+        }
     }
 }
 
@@ -578,10 +663,20 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
     // this lane's run of quarter sums, requested together with the decision
     // and the uniform (runs of up to kRun in registers, longer ones looped)
     constexpr int kRun = 16;
-    double run_v[kRun];
+    double run_v[kRun], run_p[kRun];
+    const double* qp = a.qpos + static_cast<int64_t>(b) * a.nquart;
 #pragma unroll
     for (int j = 0; j < kRun; ++j) run_v[j] = q0 + j < q1 ? qs[q0 + j] : 0.0;
     const ChainDecision d = load_decision(a, b);
+    // residual draw: the quarters' sums of P where D > 0, and the chunks'
+    // sums of P - Q' (written only for a residual draw; read only then)
+    const bool resid_draw = d.k >= 0 && d.k < g && !a.pointmass;
+    double dpart = 0.0;
+    if (resid_draw) {
+#pragma unroll
+        for (int j = 0; j < kRun; ++j) run_p[j] = q0 + j < q1 ? qp[q0 + j] : 0.0;
+        for (int c = lane; c < a.nchunk; c += 64) dpart += a.cdiff[static_cast<int64_t>(b) * a.nchunk + c];
+    }
     const double u =
         static_cast<double>(a.uniforms[static_cast<int64_t>(b) * (g + 1) + (a.given ? 0 : g)]);
     // the block's draft tokens for its output row, requested now (one per
@@ -599,11 +694,16 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
     for (int q = q0 + kRun; q < q1; ++q) mine += qs[q];
     int fallback = 0;
     DrawRow r = draw_row(a, d);
+    // residual draw: kappa = delta ln 2 from the row's sum of P - Q' (see
+    // resid_terms); every weight below is taken as w + kappa (pz - w)
+    double kappa = 0.0;
+    if (resid_draw) kappa = log1p(-wave_sum(dpart) / d.Sp);
     if ((r.resid || r.excl >= 0) && !(wave_sum(mine) > 0.0)) {
         fallback = 1;
         r.resid = false;
         r.excl = -1;
         // quarter sums of p_k, each by one lane, in the chunk kernel's order
+        kappa = 0.0;
         mine = 0.0;
         for (int q = q0; q < q1; ++q) {
             double sq = 0.0;
@@ -616,6 +716,14 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
             qs[q] = sq;
             mine += sq;
         }
+    }
+    const bool corr = r.resid;  // (after a fallback the draw is from p_k itself)
+    if (corr) {
+        double mp = 0.0;
+#pragma unroll
+        for (int j = 0; j < kRun; ++j) mp += run_p[j];
+        for (int q = q0 + kRun; q < q1; ++q) mp += qp[q];
+        mine += kappa * (mp - mine);
     }
     double W;
     const double excl = wave_exclusive_scan(mine, &W);
@@ -648,13 +756,20 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
             // rewrote the sums in memory only): lane j takes its j-th entry
             // by shuffle
             x = 0.0;
+            double xp = 0.0;
 #pragma unroll
             for (int j = 0; j < kRun; ++j) {
                 const double v = readlane_f64(run_v[j], src);
                 if (lane == j) x = v;
+                if (corr) {
+                    const double vp = readlane_f64(run_p[j], src);
+                    if (lane == j) xp = vp;
+                }
             }
+            if (corr) x += kappa * (xp - x);
         } else {
             x = q < sq1 ? qs[q] : 0.0;
+            if (corr && q < sq1) x += kappa * (qp[q] - x);
         }
         double xt;
         const double xe = wave_exclusive_scan(x, &xt);
@@ -677,7 +792,7 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
             int lastq = -1;
             qfound = -1;
             for (int q = q0; q < q1; ++q) {
-                const double sqv = qs[q];
+                const double sqv = corr ? qs[q] + kappa * (qp[q] - qs[q]) : qs[q];
                 if (sqv > 0.0) {
                     lastq = q;
                     run_last = run;
@@ -699,20 +814,31 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
     }
     // tokens of the chosen quarter, kPerVec per lane in token order
     const int e0 = qstar * kQuart + lane * E::kPerVec;
-    float zp[E::kPerVec], zq[E::kPerVec], w[E::kPerVec];
+    float zp[E::kPerVec], zq[E::kPerVec], w[E::kPerVec], pz[E::kPerVec];
     load_tokens<E>(rows, r.resid, e0, a.V, zp, zq);
-    const float lsum = lane_weights<E>(zp, zq, r, e0, w);
+    double lval;
+    if (corr) {
+        float lw, ld, lp;
+        lane_resid<E>(zp, zq, r, w, pz, lw, ld, lp);
+        lval = static_cast<double>(lw) + kappa * (static_cast<double>(lp) - static_cast<double>(lw));
+    } else {
+        lval = static_cast<double>(lane_weights<E>(zp, zq, r, e0, w));
+#pragma unroll
+        for (int i = 0; i < E::kPerVec; ++i) pz[i] = 0.0f;
+    }
     double qtot;
-    const double lbase = base + wave_exclusive_scan(static_cast<double>(lsum), &qtot);
+    const double lbase = base + wave_exclusive_scan(lval, &qtot);
     int found = INT32_MAX, lastpos = -1;
-    float pre = 0.0f;
+    float pre = 0.0f, prep = 0.0f;
 #pragma unroll
     for (int i = 0; i < E::kPerVec; ++i) {
         pre += w[i];
+        prep += pz[i];
         if (w[i] > 0.0f) {
             lastpos = e0 + i;
-            if (!last_positive && found == INT32_MAX && lbase + static_cast<double>(pre) > target)
-                found = e0 + i;
+            const double at = static_cast<double>(pre) +
+                              kappa * (static_cast<double>(prep) - static_cast<double>(pre));
+            if (!last_positive && found == INT32_MAX && lbase + at > target) found = e0 + i;
         }
     }
     const unsigned long long fl = __ballot(found != INT32_MAX);
@@ -735,7 +861,7 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
     } else {
         write_outputs<E>(a, b, d.k, token);
     }
-    if (lane == 0 && a.final_dist) a.fin[b] = FinalState{W, fallback, 0};
+    if (lane == 0 && a.final_dist) a.fin[b] = FinalState{W, kappa, fallback, 0};
 }
 
 template <class E>
@@ -757,10 +883,16 @@ __global__ __launch_bounds__(kThreads) void chain_dist_kernel(ChainArgs a) {
     const double inv = 1.0 / f.W;
     for (int e = threadIdx.x; e < a.V; e += kThreads) {
         const float zp = E::one(rows.p + e);
-        float w = r.resid ? draw_weight<E, true>(zp, E::one(rows.q + e), r)
-                          : draw_weight<E, false>(zp, 0.0f, r);
-        if (e == r.excl) w = 0.0f;
-        out[e] = static_cast<float>(static_cast<double>(w) * inv);
+        double w;
+        if (r.resid) {
+            float wf, df, pzf;
+            resid_terms<E>(zp, E::one(rows.q + e), r, wf, df, pzf);
+            w = static_cast<double>(wf) +
+                f.kappa * (static_cast<double>(pzf) - static_cast<double>(wf));
+        } else {
+            w = e == r.excl ? 0.0 : static_cast<double>(draw_weight<E>(zp, 0.0f, r));
+        }
+        out[e] = static_cast<float>(w * inv);
     }
 }
 

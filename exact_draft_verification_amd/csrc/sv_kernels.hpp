@@ -35,11 +35,14 @@ struct ChainDecision {
     double dL;     // (R_p + log2 S_p) - (R_q + log2 S_q) at row k (ratio test, k < gamma), else 0
     int32_t excl;  // point mass, k < gamma: the rejected draft token (weight 0 in the draw); else -1
     int32_t pad;   // tree verification: accept length (where the drawn token goes); else 0
+    double Sp;     // S of target row k (sum of 2^(z c - Rp) over the row)
 };
 
 // Normaliser of the final draw of one block, kept for the final_dist pass.
 struct FinalState {
-    double W;          // sum of the (unnormalised) draw weights over the row
+    double W;          // sum of the (corrected, unnormalised) draw weights over the row
+    double kappa;      // residual draw: first-order correction of the weights for the error
+                       // of dL (w + kappa * (P[D > 0] - w)); 0 otherwise
     int32_t fallback;  // 1 if an empty residual fell back to p_k
     int32_t pad;
 };
@@ -70,6 +73,9 @@ struct ChainArgs {
                             // (target) and gamma+1+i (draft); other entries unused
     ChainDecision* dec;     // [B]
     double* qsum;           // [B][nquart]: draw-weight sum per quarter
+    double* qpos;           // [B][nquart]: residual draw: sum of P over the quarter's tokens
+                            // with D > 0 (the weights' derivative in dL, see chain.hip)
+    double* cdiff;          // [B][nchunk]: residual draw: sum of P - Q' (signed) per chunk
     FinalState* fin;        // [B]
     int32_t* accept_len;
     int32_t* out_tokens;

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void tree_stoch_decide_kernel(TreeStochAr
         if (tid == 0) {
             a.accept_len[b] = -1;
             t.accept_node[b] = -1;
-            a.dec[b] = ChainDecision{-1, 0.0f, 0.0, -1, 0};
+            a.dec[b] = ChainDecision{-1, 0.0f, 0.0, -1, 0, 0.0};
         }
         return;
     }
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void tree_stoch_decide_kernel(TreeStochAr
         a.accept_len[b] = depth;
         t.accept_node[b] = vstar;
         // the draw: p at v* (the chain kernels' bonus draw), token at `depth`
-        a.dec[b] = ChainDecision{vstar, s_Rp[vstar], 0.0, -1, depth};
+        a.dec[b] = ChainDecision{vstar, s_Rp[vstar], 0.0, -1, depth, 0.0};
     }
 }
 

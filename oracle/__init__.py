@@ -52,7 +52,7 @@ def _declare(lib):
     P, I, D = _ct.c_void_p, _ct.c_int, _ct.c_double
     lib.oracle_chain.argtypes = [P, P, I, P, P, I, I, I, D, P, P, P, P, P, P, I]
     lib.oracle_chain_du.argtypes = [P, P, I, P, P, I, I, I, D, P, P, P, P, P, P, I]
-    lib.oracle_chain_alpha.argtypes = [P, P, I, I, I, I, D, P]
+    lib.oracle_chain_alpha.argtypes = [P, P, I, I, I, I, D, P, I]
     lib.oracle_tree_greedy.argtypes = [P, I, P, P, I, I, I, P, P, P, P, I]
     lib.oracle_chain_pointmass.argtypes = [P, I, P, P, I, I, I, D, P, P, P, P, P, P, I]
     lib.oracle_chain_pointmass_du.argtypes = [P, I, P, P, I, I, I, D, P, P, P, P, P, P, I]
@@ -183,7 +183,7 @@ def outcome_topk(logits, draft_tokens, T, ncache, dtype="f32", want_all=False) -
     return dict(k=k, a=a, p=p, hit=hit, all_scores=allp)
 
 
-def chain_alpha(target, draft, T, dtype="f32") -> np.ndarray:
+def chain_alpha(target, draft, T, dtype="f32", threads=None) -> np.ndarray:
     """alpha[b, i] = sum_v min(p_i(v), q_i(v)), the acceptance probability at
     draft position i when the draft token is drawn from q_i."""
     lib = _load()
@@ -191,8 +191,9 @@ def chain_alpha(target, draft, T, dtype="f32") -> np.ndarray:
     draft = _logits(draft, dtype)
     B, g1, V = target.shape
     out = np.empty((B, g1 - 1), np.float64)
+    nt = default_threads() if threads is None else threads
     rc = lib.oracle_chain_alpha(_ptr(target), _ptr(draft), _DT[dtype], B, g1 - 1, V, float(T),
-                                _ptr(out))
+                                _ptr(out), nt)
     if rc != 0:
         raise ValueError("oracle_chain_alpha rejected its arguments")
     return out

@@ -636,27 +636,54 @@ int oracle_outcome_topk(const void *logits, int dtype, const int32_t *draft_toke
 /* Per-position acceptance probability alpha_i = sum_v min(p_i(v), q_i(v)),
  * the probability that the test at position i passes when x ~ q_i
  * ([SD] "Rejection uses a residual distribution": accepted and residual
- * parts recombine to p).  Invalid rows give NaN. */
-int oracle_chain_alpha(const void *target, const void *draft, int dtype, int B, int gamma, int V,
-                       double T, double *alpha)
+ * parts recombine to p).  Invalid rows give NaN.  Blocks are shared out over
+ * up to nthreads threads. */
+typedef struct {
+    const void *target, *draft;
+    int dtype, B, gamma, V, nthreads, tid;
+    double T;
+    double *alpha;
+} alpha_arg;
+
+static void *alpha_worker(void *p)
 {
-    if (!target || !draft || !alpha || B < 1 || gamma < 1 || V < 1 || !(T > 0.0))
-        return -1;
-    for (int b = 0; b < B; ++b)
+    const alpha_arg *A = (const alpha_arg *)p;
+    const int gamma = A->gamma, V = A->V, dtype = A->dtype;
+    for (int b = A->tid; b < A->B; b += A->nthreads)
         for (int i = 0; i < gamma; ++i) {
             int64_t pr = (int64_t)b * (gamma + 1) * V + (int64_t)i * V;
             int64_t qr = (int64_t)b * gamma * V + (int64_t)i * V;
             double mp, Sp, mq, Sq, a = 0.0;
-            if (row_softmax_stats(target, dtype, pr, V, T, &mp, &Sp) ||
-                row_softmax_stats(draft, dtype, qr, V, T, &mq, &Sq)) {
-                alpha[(int64_t)b * gamma + i] = NAN;
+            if (row_softmax_stats(A->target, dtype, pr, V, A->T, &mp, &Sp) ||
+                row_softmax_stats(A->draft, dtype, qr, V, A->T, &mq, &Sq)) {
+                A->alpha[(int64_t)b * gamma + i] = NAN;
                 continue;
             }
             for (int v = 0; v < V; ++v)
-                a += fmin(prob_at(target, dtype, pr, v, T, mp, Sp),
-                          prob_at(draft, dtype, qr, v, T, mq, Sq));
-            alpha[(int64_t)b * gamma + i] = a;
+                a += fmin(prob_at(A->target, dtype, pr, v, A->T, mp, Sp),
+                          prob_at(A->draft, dtype, qr, v, A->T, mq, Sq));
+            A->alpha[(int64_t)b * gamma + i] = a;
         }
+    return NULL;
+}
+
+int oracle_chain_alpha(const void *target, const void *draft, int dtype, int B, int gamma, int V,
+                       double T, double *alpha, int nthreads)
+{
+    if (!target || !draft || !alpha || B < 1 || gamma < 1 || V < 1 || !(T > 0.0))
+        return -1;
+    if (dtype != ORC_F32 && dtype != ORC_BF16)
+        return -1;
+    int nt = nthreads < 1 ? 1 : (nthreads > B ? B : nthreads);
+    alpha_arg *args = malloc(sizeof(alpha_arg) * (size_t)nt);
+    if (!args)
+        return -2;
+    for (int t = 0; t < nt; ++t) {
+        alpha_arg a = {target, draft, dtype, B, gamma, V, nt, t, T, alpha};
+        args[t] = a;
+    }
+    run_parallel(alpha_worker, args, sizeof(alpha_arg), nt);
+    free(args);
     return 0;
 }
 

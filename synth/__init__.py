@@ -51,6 +51,7 @@ __all__ = [
     "tree_inputs",
     "config_inputs",
     "config_bytes",
+    "redraw_chain_tokens",
 ]
 
 # The five workloads: sizes, distributions and temperatures.  V = 151936 is a
@@ -521,6 +522,21 @@ def stree_config_bytes(**overrides) -> int:
     c.update(overrides)
     e = 4 if c["dtype"] == "f32" else 2
     return 2 * c["B"] * c["n"] * c["V"] * e
+
+
+def redraw_chain_tokens(d: dict, seed: int) -> tuple[np.ndarray, np.ndarray]:
+    """Fresh draft tokens and uniforms for the logits of chain inputs d:
+    d_i ~ softmax(draft_i / T) by the Gumbel-max trick over the stored draft
+    logits, as chain_inputs draws them, and U[0, 1) float32 uniforms.
+    Returns (draft_tokens [B, gamma] int32, uniforms [B, gamma+1] float32)."""
+    rng = np.random.default_rng(seed)
+    B, g = d["draft_tokens"].shape
+    dv = _as_f32(d["draft"], d["dtype"])
+    tok = np.empty((B, g), np.int32)
+    for b in range(B):
+        gum = _gumbel(rng, dv.shape[1:])
+        tok[b] = np.argmax(dv[b] / np.float32(d["T"]) + gum, axis=1)
+    return tok, rng.random((B, g + 1), dtype=np.float32)
 
 
 def config_inputs(cfg: int, seed: int = 0, threads: int | None = None, **overrides) -> dict:

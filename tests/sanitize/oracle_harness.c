@@ -17,7 +17,7 @@ int oracle_chain(const void *, const void *, int, const int32_t *, const float *
 int oracle_chain_pointmass(const void *, int, const int32_t *, const float *, int, int, int,
                            double, int32_t *, int32_t *, double *, double *, double *, int32_t *,
                            int);
-int oracle_chain_alpha(const void *, const void *, int, int, int, int, double, double *);
+int oracle_chain_alpha(const void *, const void *, int, int, int, int, double, double *, int);
 int oracle_outcome_topk(const void *, int, const int32_t *, int, int, int, double, int,
                         int32_t *, int32_t *, double *, double *, double *);
 int oracle_tree_greedy(const void *, int, const int32_t *, const int32_t *, int, int, int,
@@ -86,7 +86,7 @@ int main(void)
                0);
         EXPECT(oracle_tree_greedy(tt, 0, par, ntok, B, N, V, acc, node, outt, amax, nt), 0);
     }
-    EXPECT(oracle_chain_alpha(tgt, drf, 0, B, G, V, 1.0, alpha), 0);
+    EXPECT(oracle_chain_alpha(tgt, drf, 0, B, G, V, 1.0, alpha, 2), 0);
     EXPECT(oracle_outcome_topk(tgt, 0, tok, B, G, V, 0.9, 4, ck, ca, cp, hit, allp), 0);
     EXPECT(oracle_tree_build(zb, 0, B, M, V, 1.0, W, 3, BUD, NULL, bpar, btok, brow, bsc, bn, gap),
            0);
@@ -99,7 +99,7 @@ int main(void)
     EXPECT(oracle_chain(tgt, drf, 0, tok, u, B, G, V, -1.0, acc, out, NULL, NULL, NULL, NULL, 1), -1);
     EXPECT(oracle_chain_pointmass(tgt, 7, tok, u, B, G, V, 1.0, acc, out, NULL, NULL, NULL, NULL, 1),
            -1);
-    EXPECT(oracle_chain_alpha(tgt, drf, 0, 0, G, V, 1.0, alpha), -1);
+    EXPECT(oracle_chain_alpha(tgt, drf, 0, 0, G, V, 1.0, alpha, 1), -1);
     EXPECT(oracle_outcome_topk(tgt, 0, tok, B, G, V, 1.0, 0, ck, ca, cp, hit, NULL), -1);
     EXPECT(oracle_tree_greedy(tt, 0, par, ntok, B, 0, V, acc, node, outt, NULL, 1), -1);
     EXPECT(oracle_tree_build(zb, 0, B, M, V, 1.0, 0, 3, BUD, NULL, bpar, btok, brow, bsc, bn, gap),

@@ -56,8 +56,9 @@ def test_long_chunk_runs(shape):
 
 @pytest.mark.parametrize("cfg", [3, 5])
 def test_config_shapes_full_size(cfg):
-    d = synth.pointmass_config_inputs(cfg, seed=7000 + cfg)
-    run_case(d, f"pm-config{cfg}", want_dist=(cfg == 3))
+    for s in range(5):
+        d = synth.pointmass_config_inputs(cfg, seed=7000 + 10 * s + cfg)
+        run_case(d, f"pm-config{cfg}-s{s}", want_dist=True)
 
 
 def test_more_uniforms_config3():

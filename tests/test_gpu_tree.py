@@ -29,8 +29,11 @@ def run_case(d, label, dtype="bf16"):
     return g, o
 
 
-def test_config4_full_size():
-    for s in range(2):
+@pytest.mark.parametrize("seeds", [range(i, i + 5) for i in range(0, 20, 5)],
+                         ids=[f"s{i}-{i + 4}" for i in range(0, 20, 5)])
+def test_config4_full_size(seeds):
+    """20 seeded rounds of the 64 x 64-node workload, bit-exact."""
+    for s in seeds:
         d = synth.config_inputs(4, seed=4000 + s)
         g, _ = run_case(d, f"config4-s{s}")
         assert (g["accept_len"] >= 0).all()

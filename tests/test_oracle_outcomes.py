@@ -65,9 +65,10 @@ def test_worked_example_024():
 
 @pytest.mark.parametrize("seed", range(20))
 def test_cache_maximises_hit_probability(seed):
-    """Outcomes are disjoint, so the hit probability of a cache is the sum of
-    its entries' probabilities and the best cache of size B is the B most
-    probable outcomes: brute force over every B-subset of a tiny block."""
+    """A block ends in exactly one outcome, so a cache's chance of holding the
+    realised one adds up over its entries, and no B-subset beats the B
+    largest scores: checked by brute force over every B-subset of a tiny
+    block ("JetSpec++", Section 4.2 "Outcome Selection")."""
     rng = np.random.default_rng(400 + seed)
     V, g, B = 3, 2, 3
     z = f32(rng.normal(0, 1.0, (g + 1, V)))

@@ -22,7 +22,7 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
 
 def coefficients():
     text = open(SRC).read()
-    body = re.search(r"one_minus_exp2_neg\(float D\) \{(.*?)\n\}", text, re.S).group(1)
+    body = re.search(r"one_minus_exp2_neg_small\(float D\) \{(.*?)\n\}", text, re.S).group(1)
     lead = re.search(r"float g = ([-0-9.e+]+)f;", body).group(1)
     rest = re.findall(r"g = fmaf\(g, x, ([-0-9.e+]+)f\);", body)
     ln2 = re.search(r"const float x = D \* ([0-9.]+)f;", body).group(1)
