@@ -66,7 +66,7 @@ struct ChainArgs {
     int nseg, seg_len;      // statistics: segments per row, elements per segment
     int nchunk;             // final draw: chunk workgroups per row
     int chunk_tiles;        // final draw: tiles (one 16-byte vector per thread) per chunk
-                            // workgroup: 1, 2 or 4
+                            // workgroup, streamed in groups of 1, 2 or 4
     int nquart;             // final draw: quarters (64 16-byte vectors) per row
     Stat* part;             // [B][rows][nseg]
     float* zx;              // [B][rows]: logit of the draft token in rows i < gamma

@@ -269,8 +269,8 @@ def test_uniform_extremes():
     V = d["V"]
     top = np.nextafter(np.float32(1), np.float32(0))
     # The draw's uniform at 0 or just below 1 lies within the band of the
-    # CDF's end points, so the oracle comparison excludes these blocks; the
-    # assertions pin them instead.
+    # CDF's end points, so the comparison checks these blocks against the
+    # outcomes admissible there; the assertions pin the exact tokens as well.
     # u = 0 everywhere: every test passes (each p_i(x_i) > 0 here), and the
     # bonus draw takes the first token of positive probability under
     # p_gamma, token 0 (every logit is finite and moderate).
