@@ -13,7 +13,8 @@ same JSON line under "per_config", each with its own roofline block.
 Timing: the K timed steps are captured once in a HIP graph (rotating through
 enough input copies that the working set is at least 512 MiB, twice the
 Infinity Cache) and replayed between two events, with a device synchronise on
-both sides.  The dominant kernel's average duration comes from HIP events the
+both sides; a spin kernel queued ahead of the start event covers the host's
+submission of the graph, so the events bracket the K steps themselves.  The dominant kernel's average duration comes from HIP events the
 library records around it on the same stream, over K eager steps.  The CPU
 baseline is the fp64 oracle on a bounded sample of the same workload.
 
@@ -355,12 +356,24 @@ def measure(w, steps, warmup, torch, hip):
 
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    g.replay()
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end)
+
+    def timed_replay(graph):
+        """ms between events around one replay of the K captured steps.  The
+        host needs about 15 us per step to submit the graph's kernels; a spin
+        kernel ahead of the start event (at least about 5 ms) keeps the GPU
+        busy meanwhile and at its working clock after the host-side checks,
+        so the events bracket the K steps running back to back rather than
+        the submission (which would add about 300 us to 20 config-5 steps)."""
+        torch.cuda.synchronize()
+        torch.cuda._sleep(min(max(steps * 120_000, 12_000_000), 400_000_000))
+        start.record()
+        graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end)
+
+    g.replay()  # a second untimed replay, just ahead of the timed one
+    ms = timed_replay(g)
     for a, b in zip(eager, w.outputs()):
         for x, y in zip(a, b):
             if not torch.equal(x, y):
@@ -394,12 +407,7 @@ def measure(w, steps, warmup, torch, hip):
             w.step(i, hc)
     reps = []
     for _ in range(5):
-        torch.cuda.synchronize()
-        start.record()
-        g.replay()
-        end.record()
-        torch.cuda.synchronize()
-        reps.append(start.elapsed_time(end) * 1e3 / steps)
+        reps.append(timed_replay(g) * 1e3 / steps)
     del g
     reps.sort()
     res = dict(ms_per_step=ms / steps, gbps=w.bytes * steps / (ms * 1e-3) / 1e9,
