@@ -496,6 +496,31 @@ def copy_calibration(nbytes, reps, torch):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def stream_reference(nbytes, reps, torch):
+    """Reference rates for reading nbytes of bf16 logits once, with torch's own
+    reduction kernels (a max and an fp32 sum over the whole tensor): the
+    bandwidth a general-purpose streaming kernel reaches on the same box, to
+    set beside the statistics kernels.  Prints one JSON line."""
+    x = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    x.normal_()
+    ops = {"amax": lambda: torch.amax(x), "sum_fp32": lambda: torch.sum(x, dtype=torch.float32)}
+    out = {"stream_reference_bytes": x.numel() * 2, "reps": reps}
+    for name, fn in ops.items():
+        for _ in range(3):
+            fn()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(reps):
+            fn()
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / reps
+        out[name] = {"us": round(ms * 1e3, 2), "gbps": round(x.numel() * 2 / (ms * 1e-3) / 1e9, 1)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -512,6 +537,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--stream-reference", type=int, default=0, metavar="BYTES",
+                    help="time torch's own reductions over BYTES of bf16 (a bandwidth reference)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -523,6 +550,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, 5, torch)
+        return
+    if args.stream_reference:
+        stream_reference(args.stream_reference, 20, torch)
         return
     import exact_draft_verification_amd as sv
 
