@@ -47,18 +47,18 @@ def test_outcome_workload_full_size():
     run_case(d, 8, "oc-workload-R4")
 
 
-def test_outcome_workload_bench_launch_sampled():
+@pytest.mark.parametrize("seed", [8002, 8003])
+def test_outcome_workload_bench_launch(seed):
     """The whole workload as bench.py times it (all 32 requests, so the same
-    segments and grid), checked against the oracle on a sample of requests."""
-    d = synth.outcome_config_inputs(seed=8002)
-    pick = [0, 13, 31]
-    print(f"[case] oc-bench-launch R={d['target'].shape[0]} sample {pick}", flush=True)
+    segments and grid), every request checked against the oracle."""
+    d = synth.outcome_config_inputs(seed=seed)
+    R = d["target"].shape[0]
+    print(f"[case] oc-bench-launch seed {seed} R={R}", flush=True)
     g = gpu_outcome(d, d["ncache"])
-    o = oracle.outcome_topk(d["target"][pick], d["draft_tokens"][pick], d["T"], d["ncache"],
+    o = oracle.outcome_topk(d["target"], d["draft_tokens"], d["T"], d["ncache"],
                             dtype=d["dtype"], want_all=True)
-    swaps = compare_outcomes({k: v[pick] for k, v in g.items()}, o["all_scores"], o,
-                             "oc-bench-launch")
-    print(f"[case] oc-bench-launch: near-tie swaps {swaps}", flush=True)
+    swaps = compare_outcomes(g, o["all_scores"], o, f"oc-bench-launch-s{seed}")
+    print(f"[case] oc-bench-launch seed {seed}: near-tie swaps {swaps}", flush=True)
 
 
 def test_peaked_and_tied_rows():

@@ -65,20 +65,17 @@ def test_workload_full_size_sample():
     run_case(d, "st-workload-B4")
 
 
-def test_workload_bench_launch_sampled():
+@pytest.mark.parametrize("seed", [9101, 9102, 9103])
+def test_workload_bench_launch(seed):
     """The whole workload as bench.py times it (64 requests: the same chunk
-    runs and grids, no final_dist), checked against the oracle on a sample of
-    requests."""
-    d = synth.stree_config_inputs(seed=9101)
-    pick = [0, 21, 63]
-    print(f"[case] st-bench-launch B={d['target'].shape[0]} sample {pick}", flush=True)
+    runs and grids, no final_dist), every request checked against the
+    oracle."""
+    d = synth.stree_config_inputs(seed=seed)
+    print(f"[case] st-bench-launch seed {seed} B={d['target'].shape[0]}", flush=True)
     g = gpu_stree(d, want_dist=False)
-    o = oracle.tree_stochastic(d["target"][pick], d["draft"][pick], d["parents"][pick],
-                               d["tokens"][pick], d["uniforms"][pick], d["T"], dtype=d["dtype"])
-    sub = {k: d[k][pick] for k in ("target", "draft", "parents", "tokens", "uniforms")}
-    sub.update(T=d["T"], dtype=d["dtype"])
-    compare_stree({k: (None if v is None else v[pick]) for k, v in g.items()}, o,
-                  "st-bench-launch", False, sub)
+    o = oracle.tree_stochastic(d["target"], d["draft"], d["parents"], d["tokens"],
+                               d["uniforms"], d["T"], dtype=d["dtype"])
+    compare_stree(g, o, f"st-bench-launch-s{seed}", False, d)
 
 
 def test_one_hot_targets_equal_greedy_verification():
