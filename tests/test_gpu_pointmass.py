@@ -54,9 +54,17 @@ def test_long_chunk_runs(shape):
     run_case(d, f"pm-long{shape}")
 
 
-@pytest.mark.parametrize("cfg", [3, 5])
-def test_config_shapes_full_size(cfg):
-    for s in range(5):
+# 20 seeded rounds each of the point-mass workloads with the shapes of
+# configs 3 and 5 (final_dist compared on every one), in chunks that keep each
+# test well under a minute.
+PM_FULL = ([(3, range(i, i + 5)) for i in range(0, 20, 5)] +
+           [(5, range(i, i + 4)) for i in range(0, 20, 4)])
+
+
+@pytest.mark.parametrize("cfg,seeds", PM_FULL,
+                         ids=[f"pm{c}-s{r.start}-{r.stop - 1}" for c, r in PM_FULL])
+def test_config_shapes_full_size(cfg, seeds):
+    for s in seeds:
         d = synth.pointmass_config_inputs(cfg, seed=7000 + 10 * s + cfg)
         run_case(d, f"pm-config{cfg}-s{s}", want_dist=True)
 
