@@ -48,7 +48,8 @@
  * Conventions shared by every entry point:
  *  - Pointers to logits, tokens, uniforms, parents, outputs and workspace are
  *    DEVICE pointers owned by the caller; the library allocates no device
- *    memory, keeps no global state and never synchronises the stream.  All
+ *    memory and never synchronises the stream, and its only global state is
+ *    the per-GPU address of spec_verify_chain_noalloc's static scratch.  All
  *    work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *    results are valid once that stream reaches this point.
  *  - Arrays are dense, row-major, with the shapes given below.  Logits are
