@@ -296,6 +296,43 @@ __device__ inline float one_minus_exp2_neg_small(float D) {
     return x * g;
 }
 
+// t = z_p c - R_p of a token (its target weight is 2^t).
+__device__ inline float target_t(float zp, const DrawRow& r) {
+    const float t = fmaf(zp, r.c_hi, -r.Rp);
+    return fmaf(zp, r.c_lo, t);
+}
+
+// The terms of a token whose target weight is not negligible (t > -60).
+template <class E>
+__device__ inline void resid_main(float zp, float zq, float t, const DrawRow& r, float& w,
+                                  float& d, float& pz) {
+    const float D = log_ratio(zp, zq, r, E{});
+    const float aD = fabsf(D);
+    const float sm = one_minus_exp2_neg_small(aD);
+    const float e = __builtin_amdgcn_exp2f(-D);
+    const bool small = aD < 1.0f;
+    const bool pos = D > 0.0f;
+    const float f = pos ? (small ? sm : 1.0f - e) : -(small ? sm * e : e - 1.0f);
+    const float P = __builtin_amdgcn_exp2f(t);
+    d = P * f;
+    w = fmaxf(d, 0.0f);
+    pz = pos ? P : 0.0f;
+}
+
+// A token of negligible target weight: whether its draft weight Q' is not
+// negligible as well, and then d = -Q' (log2 Q' = z_q c - A in double, then
+// 2^(hi + lo) = 2^hi (1 + lo ln 2)).
+__device__ inline bool draft_weight_counts(float zq, const DrawRow& r) {
+    return fmaf(zq, r.c_hi, -r.A_hi) > -62.0f;
+}
+__device__ inline float minus_draft_weight(float zq, const DrawRow& r) {
+    const double tq = static_cast<double>(zq) * r.c_d - r.A;
+    const float hi = static_cast<float>(tq);
+    const double lo = tq - static_cast<double>(hi);
+    return -static_cast<float>(static_cast<double>(__builtin_amdgcn_exp2f(hi)) *
+                               (1.0 + lo * 0.69314718055994530942));
+}
+
 // Residual terms of one token of the residual draw (ratio test, k < gamma).
 // With P = 2^(z_p c - R_p) (p's weight) and D = log2 p - log2 q, where q uses
 // the dL in hand, let Q' = P 2^-D (q's weight in P's units):
@@ -316,35 +353,19 @@ __device__ inline float one_minus_exp2_neg_small(float D) {
 template <class E>
 __device__ inline void resid_terms(float zp, float zq, const DrawRow& r, float& w, float& d,
                                    float& pz) {
-    float t = fmaf(zp, r.c_hi, -r.Rp);
-    t = fmaf(zp, r.c_lo, t);
+    const float t = target_t(zp, r);
     w = 0.0f;
     d = 0.0f;
     pz = 0.0f;
-    if (t > -60.0f) {
-        const float D = log_ratio(zp, zq, r, E{});
-        const float aD = fabsf(D);
-        const float sm = one_minus_exp2_neg_small(aD);
-        const float e = __builtin_amdgcn_exp2f(-D);
-        const bool small = aD < 1.0f;
-        const bool pos = D > 0.0f;
-        const float f = pos ? (small ? sm : 1.0f - e) : -(small ? sm * e : e - 1.0f);
-        const float P = __builtin_amdgcn_exp2f(t);
-        d = P * f;
-        w = fmaxf(d, 0.0f);
-        pz = pos ? P : 0.0f;
-    } else if (fmaf(zq, r.c_hi, -r.A_hi) > -62.0f) {
-        // log2 Q' = z_q c - A in double, then 2^(hi + lo) = 2^hi (1 + lo ln 2)
-        const double tq = static_cast<double>(zq) * r.c_d - r.A;
-        const float hi = static_cast<float>(tq);
-        const double lo = tq - static_cast<double>(hi);
-        d = -static_cast<float>(static_cast<double>(__builtin_amdgcn_exp2f(hi)) *
-                                (1.0 + lo * 0.69314718055994530942));
-    }
+    if (t > -60.0f)
+        resid_main<E>(zp, zq, t, r, w, d, pz);
+    else if (draft_weight_counts(zq, r))
+        d = minus_draft_weight(zq, r);
 }
 
 // The lane's kPerVec residual terms in token order: weights w[i] and
-// pz[i], and the fp32 sums of w, d and pz in that order.
+// pz[i], and the fp32 sums of w, d and pz in that order (the select kernel's
+// view of one quarter).
 template <class E>
 __device__ inline void lane_resid(const float* zp, const float* zq, const DrawRow& r, float* w,
                                   float* pz, float& sw, float& sd, float& sp) {
@@ -358,6 +379,32 @@ __device__ inline void lane_resid(const float* zp, const float* zq, const DrawRo
         sw += w[i];
         sd += d;
         sp += pz[i];
+    }
+}
+
+// The same three fp32 sums without the terms themselves (the chunk kernel's
+// view).  A token adds only its nonzero terms: adding +0 or -0 to these sums
+// is exact (a running sum of them is never -0), so the sums are bit for bit
+// those of lane_resid, and a token whose terms are all zero (most tokens of a
+// peaked row) costs only its tests.
+template <class E>
+__device__ inline void lane_resid_sums(const float* zp, const float* zq, const DrawRow& r,
+                                       float& sw, float& sd, float& sp) {
+    sw = 0.0f;
+    sd = 0.0f;
+    sp = 0.0f;
+#pragma unroll
+    for (int i = 0; i < E::kPerVec; ++i) {
+        const float t = target_t(zp[i], r);
+        if (t > -60.0f) {
+            float w, d, pz;
+            resid_main<E>(zp[i], zq[i], t, r, w, d, pz);
+            sw += w;
+            sd += d;
+            sp += pz;
+        } else if (draft_weight_counts(zq[i], r)) {
+            sd += minus_draft_weight(zq[i], r);
+        }
     }
 }
 
@@ -535,8 +582,8 @@ __device__ inline void group_sums(const FinalRows<E>& rows, const DrawRow& r, in
         }
         const int qi = j * kWaves + wave;
         if constexpr (RESID) {
-            float pz[E::kPerVec], lw, ld, lp;
-            lane_resid<E>(zp, zq, r, w, pz, lw, ld, lp);
+            float lw, ld, lp;
+            lane_resid_sums<E>(zp, zq, r, lw, ld, lp);
             dacc += static_cast<double>(ld);
             const double sw = wave_sum(static_cast<double>(lw));
             const double sp = wave_sum(static_cast<double>(lp));
@@ -611,8 +658,8 @@ __global__ __launch_bounds__(kThreads) void chain_chunks_kernel(ChainArgs a) {
             load_tokens<E>(rows, r.resid, e, a.V, zp, zq);
             const int qi = j * kWaves + wave;
             if (r.resid) {
-                float pz[E::kPerVec], lw, ld, lp;
-                lane_resid<E>(zp, zq, r, w, pz, lw, ld, lp);
+                float lw, ld, lp;
+                lane_resid_sums<E>(zp, zq, r, lw, ld, lp);
                 dacc += static_cast<double>(ld);
                 const double sw = wave_sum(static_cast<double>(lw));
                 const double sp = wave_sum(static_cast<double>(lp));
