@@ -972,8 +972,8 @@ hipError_t launch_chain_chunks(const ChainArgs& a, int dtype, hipStream_t s) {
     }
     // bf16 runs of more than two tiles stream in groups of two: at 8 tokens
     // per 16-byte vector the residual arithmetic per group is large enough,
-    // and the smaller register footprint (about 80 VGPRs against 112 with
-    // groups of four) keeps six waves per SIMD instead of four
+    // and the smaller register footprint (under 80 VGPRs against over 100
+    // with groups of four) keeps more waves per SIMD
     if (a.chunk_tiles == 1) return go(chain_chunks_kernel<BF16, 1>);
     return go(chain_chunks_kernel<BF16, 2>);
 }
