@@ -142,6 +142,28 @@ struct TopVectorFolder {
         lst = lane < pos ? lst : (lane == pos ? ck : up);
         publish();
     }
+    // The vectors of a batch after the first: a vector is offered when its
+    // maximum is not below the threshold's value (a float test that passes
+    // every vector whose key is above th, equal values and NaN included);
+    // its key is then formed from the lane's value and index and tested
+    // exactly.  Lanes are taken in increasing order and each is tested
+    // against th as it stands, as offer() does.
+    template <int N, bool FULL>
+    __device__ inline void offer_maxima(const float* vm, int v0, int nvec) {
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            const int vi = v0 + u * kThreads;
+            uint64_t m = __ballot((FULL || vi < nvec) && !(vm[u] < th_val));
+            while (m) {
+                const int l = __builtin_ctzll(m);
+                m &= m - 1;
+                const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vm[u]), l));
+                const uint32_t i = static_cast<uint32_t>(__builtin_amdgcn_readlane(vi, l));
+                const uint64_t ck = make_key(v, i);
+                if (ck > th) insert(ck);
+            }
+        }
+    }
     template <int N>
     __device__ inline void offer(const uint64_t* key) {
 #pragma unroll
@@ -191,26 +213,26 @@ struct TopVectorFolder {
             refresh();
             // cheap test first: can any lane's batch reach the threshold?
             if (!__ballot(!(bm < th_val))) return;
+            offer_maxima<N, FULL>(vm, v0, nvec);
+            return;
         }
+        // the first batch: the list starts as the sorted best vectors of
+        // each lane's batch; the lanes' other vectors are offered as usual
         uint64_t key[N];
 #pragma unroll
         for (int u = 0; u < N; ++u) {
             const int vi = v0 + u * kThreads;
             key[u] = (FULL || vi < nvec) ? make_key(vm[u], static_cast<uint32_t>(vi)) : 0;
         }
-        if (!seeded) {
-            // the list starts as the sorted best vectors of each lane's first
-            // batch; the lanes' other vectors are offered as usual
-            uint64_t best = key[0];
+        uint64_t best = key[0];
 #pragma unroll
-            for (int u = 1; u < N; ++u) best = key[u] > best ? key[u] : best;
-            lst = wave_sort_desc(best);
+        for (int u = 1; u < N; ++u) best = key[u] > best ? key[u] : best;
+        lst = wave_sort_desc(best);
 #pragma unroll
-            for (int u = 0; u < N; ++u) key[u] = key[u] == best ? 0 : key[u];
-            seeded = true;
-            publish();
-            refresh();
-        }
+        for (int u = 0; u < N; ++u) key[u] = key[u] == best ? 0 : key[u];
+        seeded = true;
+        publish();
+        refresh();
         offer<N>(key);
     }
 };
@@ -334,15 +356,16 @@ __global__ __launch_bounds__(kThreads) void outcome_stats_kernel(OutcomeArgs a) 
         }
     }
     __syncthreads();
-    // exact ranks (equal keys, i.e. empty ones, by position)
+    // exact ranks: nonzero keys are distinct, so a key's rank is the number
+    // of keys above it; empty keys (0) follow them in position order
     OutcomeCand* out = a.cand + static_cast<int64_t>(unit) * KB;
     if (tid < nc) {
         const uint64_t ck = s_ck[tid];
         int rank = 0;
-        for (int j = 0; j < nc; ++j) {
-            const uint64_t o = s_ck[j];
-            rank += (o > ck) || (o == ck && j < tid);
-        }
+#pragma unroll 4
+        for (int j = 0; j < nc; ++j) rank += s_ck[j] > ck;
+        if (ck == 0)
+            for (int j = 0; j < tid; ++j) rank += s_ck[j] == 0;
         if (rank < KB)
             out[rank] = ck != 0 ? OutcomeCand{key_value(ck), static_cast<int32_t>(key_index(ck))}
                                 : OutcomeCand{kNegInf, INT32_MAX};

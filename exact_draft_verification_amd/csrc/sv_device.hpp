@@ -172,14 +172,17 @@ __device__ inline Stat stat_merge(const Stat& a, const Stat& b) {
     return r;
 }
 
-// Pairwise sum of N floats (N a power of two) to keep the fp32 rounding of
-// one batch at log2(N) steps.
+// Pairwise sum of N floats, to keep the fp32 rounding of one batch at
+// ceil(log2 N) steps: each step adds element i + ceil(n/2) to element i of
+// the n still to be summed (for N a power of two, element i + n/2; an odd
+// count carries its middle element to the next step).
 template <int N>
 __device__ inline float pairwise_sum(float* v) {
 #pragma unroll
-    for (int w = N / 2; w >= 1; w /= 2) {
+    for (int n = N; n > 1; n = (n + 1) / 2) {
+        const int off = (n + 1) / 2;
 #pragma unroll
-        for (int i = 0; i < w; ++i) v[i] = v[i] + v[i + w];
+        for (int i = 0; i < n / 2; ++i) v[i] = v[i] + v[i + off];
     }
     return v[0];
 }
