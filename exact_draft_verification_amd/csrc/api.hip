@@ -20,6 +20,7 @@ constexpr int64_t kChainUnits = 4096;   // chain statistics workgroups to aim fo
 constexpr int64_t kTreeUnits = 8192;    // tree argmax workgroups to aim for
 constexpr int64_t kOutcomeUnits = 1024; // outcome-scoring workgroups to aim for
 constexpr int64_t kChunkUnits = 1024;   // final-draw chunk workgroups to aim for
+constexpr int kResidualChunkTiles = 4;   // tiles per chunk at most where the draw can be residual
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -61,7 +62,7 @@ size_t carve(size_t* off, size_t size, size_t n) {
 // logits) for the ratio test, gamma+1 (target only) for a point-mass draft.
 // Statistics segments, final-draw chunks and workspace for B blocks of `rows`
 // logit rows each (chains; stochastic trees, whose blocks are requests).
-int32_t block_plan(int32_t B, int64_t rows, int32_t V, int32_t dtype, ChainPlan* p) {
+int32_t block_plan(int32_t B, int64_t rows, int32_t V, int32_t dtype, int max_tiles, ChainPlan* p) {
     const int E = elem_bytes(dtype), epv = 16 / E;
     const int64_t rows_total = static_cast<int64_t>(B) * rows;
     // every element index and byte offset must fit comfortably in int64, and
@@ -77,10 +78,13 @@ int32_t block_plan(int32_t B, int64_t rows, int32_t V, int32_t dtype, ChainPlan*
     // quarter tile (64 vectors); a chunk workgroup takes the block's decision
     // once and then streams a run of tiles, so a large batch gets a few long
     // chunks per block (about kChunkUnits workgroups in all) and a small one
-    // many single-tile chunks
+    // many single-tile chunks.  A residual draw reads two rows and takes more
+    // arithmetic per token, which overlaps its loads better with more waves:
+    // its runs are capped at max_tiles tiles.
     const int64_t tile = static_cast<int64_t>(kThreadsHost) * epv;
     const int64_t ntile = ceil_div(V, tile);
     int64_t nchunk = ceil_div(kChunkUnits, B);
+    if (max_tiles > 0 && nchunk < ceil_div(ntile, max_tiles)) nchunk = ceil_div(ntile, max_tiles);
     if (nchunk > ntile) nchunk = ntile;
     p->chunk_tiles = static_cast<int>(ceil_div(ntile, nchunk));
     p->nchunk = static_cast<int>(ceil_div(ntile, p->chunk_tiles));
@@ -103,14 +107,15 @@ int32_t chain_plan(int32_t B, int32_t gamma, int32_t V, int32_t dtype, bool poin
                    ChainPlan* p) {
     if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
     if (B < 1 || gamma < 1 || V < 1 || V > kMaxVocab || gamma > kMaxGamma) return SV_ERR_SHAPE;
-    return block_plan(B, (pointmass ? 1 : 2) * static_cast<int64_t>(gamma) + 1, V, dtype, p);
+    return block_plan(B, (pointmass ? 1 : 2) * static_cast<int64_t>(gamma) + 1, V, dtype,
+                      pointmass ? 0 : kResidualChunkTiles, p);
 }
 
 // Stochastic tree verification: n target rows and n draft rows per request.
 int32_t tree_stoch_plan(int32_t B, int32_t n, int32_t V, int32_t dtype, ChainPlan* p) {
     if (!dtype_ok(dtype)) return SV_ERR_DTYPE;
     if (B < 1 || n < 1 || V < 1 || V > kMaxVocab || n > kMaxTreeNodes) return SV_ERR_SHAPE;
-    return block_plan(B, 2 * static_cast<int64_t>(n), V, dtype, p);
+    return block_plan(B, 2 * static_cast<int64_t>(n), V, dtype, 0, p);
 }
 
 struct TreePlan {
