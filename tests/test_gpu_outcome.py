@@ -72,6 +72,28 @@ def test_peaked_and_tied_rows():
     run_case(d, 16, "oc-ties")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tied_rows_full_width(dtype):
+    """Integer logits over rows of 151,936 tokens: about a ninth of every row
+    shares the top value, so the streaming pass's threshold soon sits on a
+    value that later vectors equal, and only token ids decide between them.
+    Equal logits of one row have bit-equal scores on both sides, so the cache
+    must follow the oracle slot by slot with no swap at all (lowest token
+    first among equal probabilities)."""
+    rng = np.random.default_rng(8)
+    R, g, V = 2, 3, 151936
+    z = rng.integers(-6, 3, (R, g + 1, V)).astype(np.float32)
+    tgt = synth.bf16_bits(z) if dtype == "bf16" else z
+    d = dict(target=tgt, draft_tokens=rng.integers(0, V, (R, g)).astype(np.int32), gamma=g, V=V,
+             dtype=dtype, T=1.0)
+    label = f"oc-ties-full-{dtype}"
+    print(f"[case] {label} R={R} gamma={g} V={V} {dtype} ncache=16", flush=True)
+    gpu = gpu_outcome(d, 16)
+    o = oracle.outcome_topk(d["target"], d["draft_tokens"], d["T"], 16, dtype=dtype, want_all=True)
+    assert compare_outcomes(gpu, o["all_scores"], o, label) == 0
+    assert (gpu["k"] == o["k"]).all() and (gpu["a"] == o["a"]).all()
+
+
 def test_masked_rows_and_invalid_requests():
     rng = np.random.default_rng(6)
     R, g, V = 5, 3, 500
