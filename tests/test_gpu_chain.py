@@ -45,9 +45,10 @@ def test_shapes_and_ragged_tails(shape, dtype):
 
 
 # Batches large enough that each final-draw workgroup streams a run of
-# several tiles (about 1024 chunk workgroups in all): runs of 2 to 17 tiles,
-# a ragged last tile, and vocabularies whose rows are not 16-byte aligned
-# (mixed aligned and unaligned rows in one launch).
+# several tiles: a ratio-test chain's runs are capped at four tiles, so these
+# give runs of 3 and 4 (the point-mass tests cover runs of up to 33), a
+# ragged last run and tile, and vocabularies whose rows are not 16-byte
+# aligned (mixed aligned and unaligned rows in one launch).
 LONG_SHAPES = [(256, 2, 40000, "bf16"), (512, 1, 65541, "bf16"), (300, 2, 20000, "f32"),
                (300, 2, 20003, "f32"), (200, 3, 30000, "bf16")]
 
