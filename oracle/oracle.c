@@ -35,9 +35,10 @@
  *    convention r = 0 when p(x) = 0 and r = 1 when q(x) = 0 < p(x);
  *  - the final draw maps u to a token by inverse CDF in ascending token id:
  *    the smallest v with sum_{t<=v} w(t) > u * W; if rounding leaves no such
- *    v, the last v with w(v) > 0.  This map is a convention: the pages fix
- *    the law of the draw (pinned by the tests) but not the order in which
- *    the CDF is walked, so the map itself is "parity unpinned";
+ *    v, the last v with w(v) > 0.  The pages fix the law of the draw but not
+ *    the order in which the CDF is walked; this order is the textbook
+ *    inverse-transform sampler's, and the tests pin the map against NumPy's
+ *    Generator.choice, which samples the same way;
  *  - a residual with W = 0 (impossible in exact arithmetic after a
  *    rejection) falls back to sampling from p at that position; the block is
  *    flagged and its final margin is 0;
