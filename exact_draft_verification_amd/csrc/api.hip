@@ -333,8 +333,7 @@ int32_t chain_call(const void* target_logits, const void* draft_logits, bool poi
     if (launch_chain_stats(a, dtype, s, event_at(phase_events, 0), event_at(phase_events, 1)) !=
         hipSuccess)
         return SV_ERR_HIP;
-    if (launch_chain_chunks(a, dtype, s) != hipSuccess) return SV_ERR_HIP;
-    if (launch_chain_select(a, dtype, s) != hipSuccess) return SV_ERR_HIP;
+    if (launch_chain_draw(a, dtype, s) != hipSuccess) return SV_ERR_HIP;
     if (record(phase_events, 2, s) != SV_OK) return SV_ERR_HIP;
     if (final_dist && launch_chain_dist(a, dtype, s) != hipSuccess) return SV_ERR_HIP;
     return SV_OK;

@@ -139,17 +139,17 @@ __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainArgs a) {
 // requested in one round of loads; the partials are merged per row in LDS;
 // then for each draft position i, r_i = min(1, p_i(x_i)/q_i(x_i)) is
 // evaluated in the log2 domain in fp64 and the first i with u_i >= r_i kept.
-template <class E>
+template <class E, int NT = kThreads>
 __device__ ChainDecision chain_decide(const ChainArgs& a, int b, Stat* s_part) {
     __shared__ double s_L[2 * kMaxGamma + 1];
     __shared__ double s_S[kMaxGamma + 1];
     __shared__ float s_R[2 * kMaxGamma + 1];
     __shared__ int s_x[kMaxGamma];
     __shared__ int s_bad, s_k;
-    constexpr int kPer = kMaxBlockParts / kThreads;
+    constexpr int kPer = kMaxBlockParts / NT;
     const int g = a.gamma, rows = a.rows, tid = threadIdx.x;
     const int np = rows * a.nseg;
-    // per-position inputs (gamma <= 255 < kThreads: one position per thread)
+    // per-position inputs (gamma <= 255 < NT: one position per thread)
     int x = 0;
     float zp = 0.0f, zq = 0.0f, u = 0.0f;
     if (tid < g) {
@@ -168,17 +168,17 @@ __device__ ChainDecision chain_decide(const ChainArgs& a, int b, Stat* s_part) {
         uint4 t[kPer];
 #pragma unroll
         for (int m = 0; m < kPer; ++m)
-            t[m] = m * kThreads < np ? src[min(tid + m * kThreads, np - 1)] : make_uint4(0u, 0u, 0u, 0u);
+            t[m] = m * NT < np ? src[min(tid + m * NT, np - 1)] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
         for (int m = 0; m < kPer; ++m)
-            if (tid + m * kThreads < np) dst[tid + m * kThreads] = t[m];
+            if (tid + m * NT < np) dst[tid + m * NT] = t[m];
     }
     if (tid == 0) {
         s_bad = 0;
         s_k = g;
     }
     __syncthreads();
-    for (int r = tid; r < rows; r += kThreads) {
+    for (int r = tid; r < rows; r += NT) {
         // four independent merge chains (the merge is a short dependent
         // sequence, so one chain over many segments is latency-bound)
         const Stat* p = s_part + r * a.nseg;
@@ -511,10 +511,10 @@ __device__ inline double wave_exclusive_scan(double v, double* total) {
 // Outputs of block b: accept length k, then x_0 .. x_{k-1}, the drawn token
 // and -1 padding (all -1 for an invalid block).  Any block size.
 template <class E>
-__device__ void write_outputs(const ChainArgs& a, int b, int k, int token) {
+__device__ void write_outputs(const ChainArgs& a, int b, int k, int token, int first, int stride) {
     const int g = a.gamma;
     int32_t* out = a.out_tokens + static_cast<int64_t>(b) * (g + 1);
-    for (int i = threadIdx.x; i <= g; i += blockDim.x) {
+    for (int i = first; i <= g; i += stride) {
         int32_t v = -1;
         if (k >= 0) {
             if (i < k)
@@ -524,7 +524,7 @@ __device__ void write_outputs(const ChainArgs& a, int b, int k, int token) {
         }
         out[i] = v;
     }
-    if (threadIdx.x == 0) a.accept_len[b] = k;
+    if (first == 0) a.accept_len[b] = k;
 }
 
 // The decision of block b as written by the chunk kernel.  k is clamped to
@@ -542,10 +542,10 @@ __device__ inline ChainDecision load_decision(const ChainArgs& a, int b) {
 // at or past t1 re-reads tile t1 - 1, and a vector not wholly inside the row
 // re-reads the row's last whole vector; group_sums discards both.  Needs
 // 16-byte aligned rows of at least one whole vector.
-template <class E, int G, bool RESID>
+template <class E, int G, bool RESID, int NT = kThreads>
 __device__ inline void issue_group(const FinalRows<E>& rows, int t, int t1, int vlast, uint4* p,
                                    uint4* q) {
-    constexpr int kTile = kThreads * E::kPerVec;
+    constexpr int kTile = NT * E::kPerVec;
 #pragma unroll
     for (int m = 0; m < G; ++m) {
         const int e = min(min(t + m, t1 - 1) * kTile + static_cast<int>(threadIdx.x) * E::kPerVec, vlast);
@@ -557,11 +557,11 @@ __device__ inline void issue_group(const FinalRows<E>& rows, int t, int t1, int 
 // Quarter sums of the group of tiles [t, min(t + G, t1)) from its raw
 // vectors; a vector that straddles the row's end is read token by token,
 // one past it is all -inf (weight 0).
-template <class E, int G, bool RESID>
+template <class E, int G, bool RESID, int NT = kThreads>
 __device__ inline void group_sums(const FinalRows<E>& rows, const DrawRow& r, int t, int t1, int V,
                                   const uint4* p, const uint4* q, double* qs, double* qp,
                                   int nquart, double& dacc) {
-    constexpr int kTile = kThreads * E::kPerVec;
+    constexpr int kTile = NT * E::kPerVec;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int m = 0; m < G; ++m) {
@@ -580,7 +580,7 @@ __device__ inline void group_sums(const FinalRows<E>& rows, const DrawRow& r, in
         } else {
             load_tokens<E>(rows, RESID, e, V, zp, zq);
         }
-        const int qi = j * kWaves + wave;
+        const int qi = j * (NT / 64) + wave;
         if constexpr (RESID) {
             float lw, ld, lp;
             lane_resid_sums<E>(zp, zq, r, lw, ld, lp);
@@ -601,24 +601,24 @@ __device__ inline void group_sums(const FinalRows<E>& rows, const DrawRow& r, in
 
 // The chunk's tiles [t0, t1) in groups of G, software-pipelined: the next
 // group's loads are in flight while the current group's weights are formed.
-template <class E, int G, bool RESID>
+template <class E, int G, bool RESID, int NT = kThreads>
 __device__ inline void stream_tiles(const FinalRows<E>& rows, const DrawRow& r, int t0, int t1,
                                     int V, double* qs, double* qp, int nquart, double& dacc) {
     const int vlast = (V / E::kPerVec - 1) * E::kPerVec;  // the row's last whole vector
     const int ngroup = (t1 - t0 + G - 1) / G;
     uint4 cp[G], cq[G];
-    issue_group<E, G, RESID>(rows, t0, t1, vlast, cp, cq);
+    issue_group<E, G, RESID, NT>(rows, t0, t1, vlast, cp, cq);
     for (int gi = 0; gi + 1 < ngroup; ++gi) {
         uint4 np[G], nq[G];
-        issue_group<E, G, RESID>(rows, t0 + (gi + 1) * G, t1, vlast, np, nq);
-        group_sums<E, G, RESID>(rows, r, t0 + gi * G, t1, V, cp, cq, qs, qp, nquart, dacc);
+        issue_group<E, G, RESID, NT>(rows, t0 + (gi + 1) * G, t1, vlast, np, nq);
+        group_sums<E, G, RESID, NT>(rows, r, t0 + gi * G, t1, V, cp, cq, qs, qp, nquart, dacc);
 #pragma unroll
         for (int m = 0; m < G; ++m) {
             cp[m] = np[m];
             if constexpr (RESID) cq[m] = nq[m];
         }
     }
-    group_sums<E, G, RESID>(rows, r, t0 + (ngroup - 1) * G, t1, V, cp, cq, qs, qp, nquart, dacc);
+    group_sums<E, G, RESID, NT>(rows, r, t0 + (ngroup - 1) * G, t1, V, cp, cq, qs, qp, nquart, dacc);
 }
 
 // Chunk workgroup: the block's decision, then the chunk's tiles of the final
@@ -699,22 +699,27 @@ __global__ __launch_bounds__(kThreads) void chain_chunks_kernel(ChainArgs a) {
 // is taken.  A residual that sums to zero (possible only through rounding
 // after a rejection) falls back to p_k: the wave then recomputes the quarter
 // sums from p_k itself (slow, but never on a normal path).
+//
+// select_block is that selection for one wave (all 64 of its lanes, lane =
+// this lane's index): qs and qp are the block's quarter sums (global memory,
+// or LDS when the whole draw runs in one workgroup).  The residual draw's sum
+// of P - Q' over the row comes from the chunks' partial sums cd[0 .. nchunk)
+// when cd is given, else it is rowd.  dk: the block's decision if the caller
+// holds it, else it is loaded here.
 template <class E>
-__global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
+__device__ void select_block(const ChainArgs& a, int b, int lane, double* qs, const double* qp,
+                             const double* cd, double rowd, const ChainDecision* dk) {
     constexpr int kQuart = 64 * E::kPerVec;
-    const int b = blockIdx.x, lane = threadIdx.x;
     const int g = a.gamma;
-    double* qs = a.qsum + static_cast<int64_t>(b) * a.nquart;
     const int per = (a.nquart + 63) / 64;
     const int q0 = min(a.nquart, lane * per), q1 = min(a.nquart, q0 + per);
     // this lane's run of quarter sums, requested together with the decision
     // and the uniform (runs of up to kRun in registers, longer ones looped)
     constexpr int kRun = 16;
     double run_v[kRun], run_p[kRun];
-    const double* qp = a.qpos + static_cast<int64_t>(b) * a.nquart;
 #pragma unroll
     for (int j = 0; j < kRun; ++j) run_v[j] = q0 + j < q1 ? qs[q0 + j] : 0.0;
-    const ChainDecision d = load_decision(a, b);
+    const ChainDecision d = dk ? *dk : load_decision(a, b);
     // residual draw: the quarters' sums of P where D > 0, and the chunks'
     // sums of P - Q' (written only for a residual draw; read only then)
     const bool resid_draw = d.k >= 0 && d.k < g && !a.pointmass;
@@ -722,7 +727,11 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
     if (resid_draw) {
 #pragma unroll
         for (int j = 0; j < kRun; ++j) run_p[j] = q0 + j < q1 ? qp[q0 + j] : 0.0;
-        for (int c = lane; c < a.nchunk; c += 64) dpart += a.cdiff[static_cast<int64_t>(b) * a.nchunk + c];
+        if (cd) {
+            for (int c = lane; c < a.nchunk; c += 64) dpart += cd[c];
+        } else if (lane == 0) {
+            dpart = rowd;
+        }
     }
     const double u =
         static_cast<double>(a.uniforms[static_cast<int64_t>(b) * (g + 1) + (a.given ? 0 : g)]);
@@ -731,7 +740,7 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
     const bool lane_out = !a.given && g < 64;
     const int xtok = lane_out && lane < g ? a.tokens[static_cast<int64_t>(b) * g + lane] : -1;
     if (d.k < 0) {
-        if (!a.given) write_outputs<E>(a, b, -1, -1);  // (a given decision wrote its own)
+        if (!a.given) write_outputs<E>(a, b, -1, -1, lane, 64);  // (a given decision wrote its own)
         return;
     }
     const FinalRows<E> rows = final_rows<E>(a, b, d.k);
@@ -906,9 +915,93 @@ __global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
                 lane < d.k ? xtok : (lane == d.k ? token : -1);
         if (lane == 0) a.accept_len[b] = d.k;
     } else {
-        write_outputs<E>(a, b, d.k, token);
+        write_outputs<E>(a, b, d.k, token, lane, 64);
     }
     if (lane == 0 && a.final_dist) a.fin[b] = FinalState{W, kappa, fallback, 0};
+}
+
+template <class E>
+__global__ __launch_bounds__(64) void chain_select_kernel(ChainArgs a) {
+    const int b = blockIdx.x;
+    select_block<E>(a, b, threadIdx.x, a.qsum + static_cast<int64_t>(b) * a.nquart,
+                    a.qpos + static_cast<int64_t>(b) * a.nquart,
+                    a.cdiff + static_cast<int64_t>(b) * a.nchunk, 0.0, nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// The whole final draw of a block in one workgroup of kBlockThreads threads,
+// for batches with at least one block per compute unit (the launcher uses it
+// for point-mass drafts): the decision once instead of once per chunk, the
+// final row (and q_k for a residual) streamed with the quarter sums kept in
+// LDS, then the selection on the first wave, reading the sums from LDS, with
+// no selection launch and no quarter sums in HBM.  A
+// quarter is the same 64 vectors as in the chunk kernel (wave w of tile j
+// owns quarter 16j + w), its sum the same fp64 wave sum of the same lanes'
+// fp32 sums, so the selection is the select kernel's; only the row's sum of
+// P - Q' (the residual correction's input) is added in another order.
+constexpr int kBlockThreads = 1024;
+constexpr size_t kBlockDrawLds = 48 * 1024;  // its dynamic LDS at most
+
+template <class E, int G>
+__global__ __launch_bounds__(kBlockThreads) void chain_block_draw_kernel(ChainArgs a) {
+    constexpr int NT = kBlockThreads, NW = NT / 64;
+    constexpr int kTile = NT * E::kPerVec;
+    extern __shared__ double s_dyn[];
+    double* s_qs = s_dyn;                                      // [nquart] weight sums
+    double* s_qp = s_qs + a.nquart;                            // [nquart] sums of P, D > 0
+    Stat* s_part = reinterpret_cast<Stat*>(s_qp + a.nquart);  // [rows][nseg]
+    __shared__ double s_d[NW];
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const ChainDecision d = chain_decide<E, NT>(a, b, s_part);
+    if (tid == 0) a.dec[b] = d;  // (the final_dist kernel reads it)
+    const DrawRow r = draw_row(a, d);
+    const bool resid = d.k >= 0 && r.resid;
+    double dacc = 0.0;  // residual draw: this thread's share of sum (P - Q') over the row
+    if (d.k >= 0) {
+        const FinalRows<E> rows = final_rows<E>(a, b, d.k);
+        const int ntile = (a.V + kTile - 1) / kTile;
+        if (rows.vec_ok && a.V >= E::kPerVec) {
+            if (r.resid)
+                stream_tiles<E, G, true, NT>(rows, r, 0, ntile, a.V, s_qs, s_qp, a.nquart, dacc);
+            else
+                stream_tiles<E, G, false, NT>(rows, r, 0, ntile, a.V, s_qs, s_qp, a.nquart, dacc);
+        } else {
+            // rows not 16-byte aligned (or shorter than a vector): token by token
+            for (int j = 0; j < ntile; ++j) {
+                float zp[E::kPerVec], zq[E::kPerVec], w[E::kPerVec];
+                const int e = j * kTile + tid * E::kPerVec;
+                load_tokens<E>(rows, r.resid, e, a.V, zp, zq);
+                const int qi = j * NW + wave;
+                if (r.resid) {
+                    float lw, ld, lp;
+                    lane_resid_sums<E>(zp, zq, r, lw, ld, lp);
+                    dacc += static_cast<double>(ld);
+                    const double sw = wave_sum(static_cast<double>(lw));
+                    const double sp = wave_sum(static_cast<double>(lp));
+                    if (lane == 0 && qi < a.nquart) {
+                        s_qs[qi] = sw;
+                        s_qp[qi] = sp;
+                    }
+                } else {
+                    const double sw =
+                        wave_sum(static_cast<double>(lane_weights<E>(zp, zq, r, e, w)));
+                    if (lane == 0 && qi < a.nquart) s_qs[qi] = sw;
+                }
+            }
+        }
+    }
+    if (resid) {
+        const double wd = wave_sum(dacc);
+        if (lane == 0) s_d[wave] = wd;
+    }
+    __syncthreads();  // the quarter sums and the waves' sums are in LDS
+    if (wave != 0) return;
+    double rowd = 0.0;
+    if (resid) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) rowd += s_d[i];
+    }
+    select_block<E>(a, b, lane, s_qs, s_qp, nullptr, rowd, &d);
 }
 
 template <class E>
@@ -976,6 +1069,52 @@ hipError_t launch_chain_chunks(const ChainArgs& a, int dtype, hipStream_t s) {
     // with groups of four) keeps more waves per SIMD
     if (a.chunk_tiles == 1) return go(chain_chunks_kernel<BF16, 1>);
     return go(chain_chunks_kernel<BF16, 2>);
+}
+
+// LDS of chain_block_draw_kernel beyond its static arrays: the quarter sums
+// and their sums of P, and the block's partials for the decision.
+static size_t block_draw_lds(const ChainArgs& a) {
+    return 2 * sizeof(double) * static_cast<size_t>(a.nquart) +
+           sizeof(Stat) * static_cast<size_t>(a.rows) * a.nseg;
+}
+
+// Compute units of the current device, found once (every device this
+// library runs on is the same part); 0 if the runtime cannot say.
+static int device_cus() {
+    static const int cus = [] {
+        int dev = 0, n = 0;
+        return (hipGetDevice(&dev) == hipSuccess &&
+                hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+                   ? n
+                   : 0;
+    }();
+    return cus;
+}
+
+hipError_t launch_chain_draw(const ChainArgs& a, int dtype, hipStream_t s) {
+    // A point-mass draft's draw (one row, little arithmetic per token) runs
+    // in one workgroup per block when the blocks cover the compute units,
+    // the logits' rows are 16-byte aligned and the quarter sums fit in LDS.
+    // A residual draw reads two rows and does more arithmetic per token; it
+    // needs the chunk kernel's greater number of waves per compute unit to
+    // hide its latencies (at B = 256 the single workgroup per block was
+    // slower than chunks and selection), so ratio-test chains keep those.
+    const size_t eb = dtype == 0 ? 4 : 2;
+    const bool aligned = (reinterpret_cast<uintptr_t>(a.target) & 15u) == 0 &&
+                         (static_cast<size_t>(a.V) * eb) % 16 == 0;
+    const int cus = device_cus();
+    if (a.pointmass && !a.given && aligned && cus > 0 && a.B >= cus &&
+        block_draw_lds(a) <= kBlockDrawLds) {
+        const size_t lds = block_draw_lds(a);
+        if (dtype == 0)
+            hipLaunchKernelGGL((chain_block_draw_kernel<F32, 2>), dim3(a.B), dim3(kBlockThreads), lds, s, a);
+        else
+            hipLaunchKernelGGL((chain_block_draw_kernel<BF16, 2>), dim3(a.B), dim3(kBlockThreads), lds, s, a);
+        return hipGetLastError();
+    }
+    const hipError_t e = launch_chain_chunks(a, dtype, s);
+    if (e != hipSuccess) return e;
+    return launch_chain_select(a, dtype, s);
 }
 
 hipError_t launch_chain_select(const ChainArgs& a, int dtype, hipStream_t s) {

@@ -166,6 +166,9 @@ hipError_t launch_chain_stats(const ChainArgs& a, int dtype, hipStream_t s, hipE
 hipError_t launch_chain_chunks(const ChainArgs& a, int dtype, hipStream_t s);
 hipError_t launch_chain_select(const ChainArgs& a, int dtype, hipStream_t s);
 hipError_t launch_chain_dist(const ChainArgs& a, int dtype, hipStream_t s);
+// The final draw of a chain (chunk and select kernels, or one workgroup per
+// block for a large batch of point-mass blocks).
+hipError_t launch_chain_draw(const ChainArgs& a, int dtype, hipStream_t s);
 hipError_t launch_tree_argmax(const TreeArgs& a, int dtype, hipStream_t s, hipEvent_t ev_start,
                               hipEvent_t ev_stop);
 hipError_t launch_tree_resolve(const TreeArgs& a, hipStream_t s);
