@@ -171,3 +171,31 @@ def test_uniform_extremes():
         d["uniforms"][:, 3] = u_draw
         g, _ = run_case(d, f"pm-reject-draw{u_draw:.0f}")
         assert (g["accept_len"] == 0).all() and (g["out_tokens"][:, 0] == want).all()
+
+
+def test_block_draw_matches_chunk_draw():
+    """A point-mass batch of at least one block per compute unit draws each
+    block in one workgroup (quarter sums kept in LDS), a smaller batch in
+    chunk workgroups and a selection kernel.  Both form the same quarter sums
+    and select the same way, so the same blocks must give bit-identical accept
+    lengths, tokens and final_dist through either path: a batch of exactly
+    one block per compute unit against the same batch without its last
+    block."""
+    torch, _ = require_gpu()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    B, g, V = cus, 4, 151936
+    d = synth.pointmass_inputs(B, g, V, "bf16", T=0.8, target=("gumbel", 4.0), p_match=0.8,
+                               seed=4300)
+    print(f"[case] pm block-vs-chunk B={B} gamma={g} V={V} bf16", flush=True)
+    big = gpu_pointmass(d, want_dist=True)
+    sub = {k: (v[: B - 1] if isinstance(v, np.ndarray) and v.shape[:1] == (B,) else v)
+           for k, v in d.items()}
+    sub["B"] = B - 1
+    small = gpu_pointmass(sub, want_dist=True)
+    assert np.array_equal(big["accept_len"][: B - 1], small["accept_len"])
+    assert np.array_equal(big["out_tokens"][: B - 1], small["out_tokens"])
+    assert np.array_equal(big["final_dist"][: B - 1], small["final_dist"])
+    # the batch is not degenerate: rejections (residual of p without the
+    # rejected token) and full acceptances (bonus draws) both occur
+    acc = big["accept_len"]
+    assert (acc < g).sum() > 10 and (acc == g).sum() > 0
