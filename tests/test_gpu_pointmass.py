@@ -173,20 +173,21 @@ def test_uniform_extremes():
         assert (g["accept_len"] == 0).all() and (g["out_tokens"][:, 0] == want).all()
 
 
-def test_block_draw_matches_chunk_draw():
+@pytest.mark.parametrize("dtype,g,V", [("bf16", 4, 151936), ("f32", 4, 151936), ("bf16", 255, 4096)])
+def test_block_draw_matches_chunk_draw(dtype, g, V):
     """A point-mass batch of at least one block per compute unit draws each
     block in one workgroup (quarter sums kept in LDS), a smaller batch in
     chunk workgroups and a selection kernel.  Both form the same quarter sums
     and select the same way, so the same blocks must give bit-identical accept
     lengths, tokens and final_dist through either path: a batch of exactly
     one block per compute unit against the same batch without its last
-    block."""
+    block.  gamma = 255 also takes the outputs' writes past the first wave's
+    64 lanes."""
     torch, _ = require_gpu()
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    B, g, V = cus, 4, 151936
-    d = synth.pointmass_inputs(B, g, V, "bf16", T=0.8, target=("gumbel", 4.0), p_match=0.8,
-                               seed=4300)
-    print(f"[case] pm block-vs-chunk B={B} gamma={g} V={V} bf16", flush=True)
+    B = torch.cuda.get_device_properties(0).multi_processor_count
+    d = synth.pointmass_inputs(B, g, V, dtype, T=0.8, target=("gumbel", 4.0), p_match=0.8,
+                               seed=4300 + g)
+    print(f"[case] pm block-vs-chunk B={B} gamma={g} V={V} {dtype}", flush=True)
     big = gpu_pointmass(d, want_dist=True)
     sub = {k: (v[: B - 1] if isinstance(v, np.ndarray) and v.shape[:1] == (B,) else v)
            for k, v in d.items()}
@@ -198,4 +199,6 @@ def test_block_draw_matches_chunk_draw():
     # the batch is not degenerate: rejections (residual of p without the
     # rejected token) and full acceptances (bonus draws) both occur
     acc = big["accept_len"]
-    assert (acc < g).sum() > 10 and (acc == g).sum() > 0
+    assert (acc < g).sum() > 10
+    if g < 16:
+        assert (acc == g).sum() > 0
